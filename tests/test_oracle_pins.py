@@ -1,0 +1,317 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Each test ties one part of the oracle to a fact the pages or the mathematics
+fix: a pure-Python brute force, a library attention routine on the original
+contiguous slab, the tiled online-softmax algorithm, invariants (weights sum
+to one, block-id permutation, shared prefixes) and closed-form special
+cases.  ``test_planted_mistakes_are_caught`` plants plausible mistakes in a
+patched copy of the oracle and checks that some pin fails for each.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import paged_attention as pa
+from paged_kv_cache_23_amd.workloads import build_workload, tiny_fp32, storage_numpy
+from tests.oracle_inputs import oracle_args
+
+BS = 16
+
+
+# ---------------------------------------------------------------------------
+# Independent references used by the pins
+# ---------------------------------------------------------------------------
+def brute_force_decode(q, k_pool, v_pool, tables, lens, scale, G):
+    """Pure-Python loops over (b, h, t, d), math.fsum / math.exp, reading the
+    pool through the block table directly (no slab)."""
+    B, Hq, D = q.shape
+    out = np.zeros((B, Hq, D))
+    for b in range(B):
+        n = int(lens[b])
+        for h in range(Hq):
+            g = h // G
+            scores = []
+            for t in range(n):
+                phys = int(tables[b][t // BS])
+                off = t % BS
+                scores.append(float(scale) * math.fsum(float(q[b, h, d]) * float(k_pool[phys, g, off, d])
+                                                       for d in range(D)))
+            if n == 0:
+                continue
+            m = max(scores)
+            e = [math.exp(s - m) for s in scores]
+            z = math.fsum(e)
+            for d in range(D):
+                out[b, h, d] = math.fsum(e[t] / z * float(v_pool[int(tables[b][t // BS]), g, d, t % BS])
+                                         for t in range(n))
+    return out
+
+
+def scatter_slabs(k_slabs, v_slabs, rng, spare=3):
+    """Build a pool + tables from per-sequence contiguous slabs (test-local scatter)."""
+    Hkv, D = k_slabs[0].shape[1], k_slabs[0].shape[2]
+    nblks = [-(-s.shape[0] // BS) for s in k_slabs]
+    NB = sum(nblks) + spare
+    perm = rng.permutation(NB)
+    k_pool = rng.standard_normal((NB, Hkv, BS, D))
+    v_pool = rng.standard_normal((NB, Hkv, D, BS))
+    tables = np.full((len(k_slabs), max(nblks)), -1, dtype=np.int32)
+    nxt = 0
+    for b, (ks, vs) in enumerate(zip(k_slabs, v_slabs)):
+        for j in range(nblks[b]):
+            phys = int(perm[nxt])
+            nxt += 1
+            tables[b, j] = phys
+            for off in range(BS):
+                t = j * BS + off
+                if t < ks.shape[0]:
+                    k_pool[phys, :, off, :] = ks[t]
+                    v_pool[phys, :, :, off] = vs[t]
+    return k_pool.astype(np.float32), v_pool.astype(np.float32), tables
+
+
+def tiled_online_decode(qrow, K, V, scale, tile=BS):
+    """fp64 transcription of the tiled online-softmax loop for one query row
+    (Habr article §3, pseudocode of the FlashAttention forward pass, with
+    one query row and key/value tiles of ``tile`` tokens)."""
+    m, l = -math.inf, 0.0
+    O = np.zeros(V.shape[1])
+    for j in range(0, K.shape[0], tile):
+        S = scale * (K[j:j + tile] @ qrow)
+        m_new = max(m, S.max())
+        P = np.exp(S - m_new)
+        l_new = l * math.exp(m - m_new) + P.sum()
+        O = O * (l * math.exp(m - m_new) / l_new) + (P / l_new) @ V[j:j + tile]
+        m, l = m_new, l_new
+    return O
+
+
+def split_merge_decode(qrow, K, V, scale, part):
+    """Partitions of ``part`` tokens each keep (max, sum, unnormalised acc);
+    the merge rescales them to the global max (same algebra as the running
+    rescale by exp(m_old - m_new) in the tiled loop)."""
+    parts = []
+    for lo in range(0, K.shape[0], part):
+        S = scale * (K[lo:lo + part] @ qrow)
+        m = S.max()
+        P = np.exp(S - m)
+        parts.append((m, P.sum(), P @ V[lo:lo + part]))
+    M = max(p[0] for p in parts)
+    L = sum(p[1] * math.exp(p[0] - M) for p in parts)
+    acc = sum(p[2] * math.exp(p[0] - M) for p in parts)
+    return acc / L
+
+
+# ---------------------------------------------------------------------------
+# Pins
+# ---------------------------------------------------------------------------
+def _tiny():
+    return tiny_fp32()
+
+
+def test_brute_force_tiny():
+    """Oracle == pure-Python brute force on the tiny fp32 workload (both steps)."""
+    wl = _tiny()
+    for after in (False, True):
+        args = oracle_args(wl, after_append=after)
+        if after:  # decode after the append: pools carry the appended token
+            from oracle import oracle_append
+            from tests.oracle_inputs import oracle_append_args
+            kp, vp = oracle_append(**oracle_append_args(wl))
+            args = oracle_args(wl, after_append=True, k_pool=kp, v_pool=vp)
+        got = oracle.oracle_decode(**args)
+        ref = brute_force_decode(args["q"], args["k_pool"], args["v_pool"], args["block_tables"],
+                                 args["context_lens"], np.float32(wl.scale), 2)
+        assert np.max(np.abs(got - ref)) <= 1e-12
+
+
+@pytest.mark.parametrize("G", [1, 2, 4])
+def test_paged_equals_slab_sdpa(G):
+    """Gather-then-attend on the pool == torch SDPA (fp64) on the original slabs."""
+    rng = np.random.default_rng(11 + G)
+    Hkv, D = 2, 32
+    Hq = Hkv * G
+    lens = [1, 15, 16, 17, 40, 64]
+    k_slabs = [rng.standard_normal((n, Hkv, D)).astype(np.float32) for n in lens]
+    v_slabs = [rng.standard_normal((n, Hkv, D)).astype(np.float32) for n in lens]
+    k_pool, v_pool, tables = scatter_slabs(k_slabs, v_slabs, rng)
+    q = rng.standard_normal((len(lens), Hq, D)).astype(np.float32)
+    scale = float(np.float32(1 / math.sqrt(D)))
+    got = oracle.oracle_decode(q, "f32", k_pool, v_pool, "f32", tables, np.array(lens), scale)
+    for b, n in enumerate(lens):
+        qt = torch.from_numpy(q[b].astype(np.float64))[None, :, None, :]          # [1, Hq, 1, D]
+        kt = torch.from_numpy(k_slabs[b].astype(np.float64)).permute(1, 0, 2)[None]  # [1, Hkv, n, D]
+        vt = torch.from_numpy(v_slabs[b].astype(np.float64)).permute(1, 0, 2)[None]
+        ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, scale=scale, enable_gqa=True)
+        assert np.max(np.abs(got[b] - ref[0, :, 0, :].numpy())) <= 1e-12
+
+
+@pytest.mark.parametrize("n", [1, 16, 17, 100, 257])
+def test_online_and_split_equal_two_pass(n):
+    """The tiled online form and the partition merge reach the oracle's result."""
+    rng = np.random.default_rng(n)
+    D = 16
+    K = rng.standard_normal((n, D)) * 2.0
+    V = rng.standard_normal((n, D))
+    qrow = rng.standard_normal(D)
+    scale = 0.25
+    ref = oracle.softmax_weights(scale * (K @ qrow)) @ V
+    assert np.max(np.abs(tiled_online_decode(qrow, K, V, scale) - ref)) <= 1e-12
+    for part in (16, 32, 48, 1000):
+        assert np.max(np.abs(split_merge_decode(qrow, K, V, scale, part) - ref)) <= 1e-12
+
+
+def test_softmax_weights_sum_to_one():
+    rng = np.random.default_rng(5)
+    for n in (1, 2, 17, 4096):
+        w = oracle.softmax_weights(rng.standard_normal(n) * 10)
+        assert abs(w.sum() - 1.0) <= 1e-14
+        assert np.all(w >= 0)
+
+
+@pytest.mark.parametrize("kv_dtype", ["f32", "bf16", "fp8"])
+def test_block_permutation_invariance(kv_dtype):
+    """Permuting physical block ids (pool and tables together) leaves the output bit-identical."""
+    rng = np.random.default_rng(7)
+    wl = build_workload("perm", [5, 16, 33, 70], 4, 2, 32, kv_dtype, seed=7)
+    args = oracle_args(wl)
+    base = oracle.oracle_decode(**args)
+    NB = wl.num_blocks
+    pi = rng.permutation(NB)
+    kp = np.empty_like(args["k_pool"])
+    vp = np.empty_like(args["v_pool"])
+    kp[pi] = args["k_pool"]
+    vp[pi] = args["v_pool"]
+    t = args["block_tables"]
+    t2 = np.where(t >= 0, pi[np.clip(t, 0, None)], -1).astype(np.int32)
+    got = oracle.oracle_decode(**dict(args, k_pool=kp, v_pool=vp, block_tables=t2))
+    assert np.array_equal(got, base)
+
+
+def test_shared_prefix_equals_private_copies():
+    """Tables pointing at one refcounted prefix give the same bits as private copies."""
+    wl = build_workload("share", [35, 48, 50, 63], 4, 2, 32, "bf16", seed=9, shared_prefix=32)
+    args = oracle_args(wl)
+    shared = oracle.oracle_decode(**args)
+    kp, vp, t = args["k_pool"], args["v_pool"], args["block_tables"].copy()
+    extra_k, extra_v = [], []
+    nxt = kp.shape[0]
+    for b in range(1, t.shape[0]):     # every sequence but the first gets private copies
+        for j in range(2):
+            extra_k.append(kp[t[b, j]])
+            extra_v.append(vp[t[b, j]])
+            t[b, j] = nxt
+            nxt += 1
+    kp2 = np.concatenate([kp, np.stack(extra_k)])
+    vp2 = np.concatenate([vp, np.stack(extra_v)])
+    private = oracle.oracle_decode(**dict(args, k_pool=kp2, v_pool=vp2, block_tables=t))
+    assert np.array_equal(shared, private)
+
+
+def test_special_cases():
+    rng = np.random.default_rng(3)
+    Hkv, D, G = 1, 8, 2
+    # n = 1: the single value row comes back exactly
+    kp = rng.standard_normal((2, Hkv, BS, D)).astype(np.float32)
+    vp = rng.standard_normal((2, Hkv, D, BS)).astype(np.float32)
+    q = rng.standard_normal((1, G, D)).astype(np.float32)
+    tbl = np.array([[1]], dtype=np.int32)
+    out = oracle.oracle_decode(q, "f32", kp, vp, "f32", tbl, np.array([1]), 0.5)
+    assert np.array_equal(out[0, 0], vp[1, 0, :, 0].astype(np.float64))
+    # all keys equal, or q = 0: the mean of the values
+    n = 40
+    kp = np.repeat(rng.standard_normal((1, Hkv, 1, D)), BS, axis=2).repeat(3, axis=0).astype(np.float32)
+    vp = rng.standard_normal((3, Hkv, D, BS)).astype(np.float32)
+    tbl = np.array([[2, 0, 1]], dtype=np.int32)
+    out = oracle.oracle_decode(q, "f32", kp, vp, "f32", tbl, np.array([n]), 0.5)
+    V = np.concatenate([vp[p, 0].T for p in tbl[0]])[:n].astype(np.float64)
+    assert np.max(np.abs(out[0, 0] - V.mean(axis=0))) <= 1e-14
+    kp_r = rng.standard_normal((3, Hkv, BS, D)).astype(np.float32)
+    out0 = oracle.oracle_decode(np.zeros_like(q), "f32", kp_r, vp, "f32", tbl, np.array([n]), 0.5)
+    assert np.max(np.abs(out0[0, 1] - V.mean(axis=0))) <= 1e-14
+    # one key far above the rest: its value row dominates
+    kp_d = (rng.standard_normal((3, Hkv, BS, D)) * 0.01).astype(np.float32)
+    kp_d[0, 0, 5, :] = q[0, 0] * 50
+    out_d = oracle.oracle_decode(q, "f32", kp_d, vp, "f32", tbl, np.array([n]), 1.0)
+    assert np.max(np.abs(out_d[0, 0] - vp[0, 0, :, 5])) <= 1e-6
+
+
+def test_zero_length_sequence_gives_zero():
+    wl = build_workload("zero", [0, 20], 2, 1, 16, "f32", seed=2)
+    out = oracle.oracle_decode(**oracle_args(wl))
+    assert np.all(out[0] == 0.0)
+    assert np.any(out[1] != 0.0)
+
+
+# ---------------------------------------------------------------------------
+# Planted mistakes: each must make at least one pin fail
+# ---------------------------------------------------------------------------
+def _gather_v_token_major(pool, table_row, n, which, head):
+    """Mistake: read the V tile as if it were token-major like K."""
+    if which == "k":
+        return _ORIG_GATHER(pool, table_row, n, which, head)
+    D = pool.shape[2]
+    flat = pool[:, head].reshape(pool.shape[0], BS, D)  # wrong view of [D, 16]
+    rows = [flat[int(table_row[j])] for j in range(-(-n // BS))]
+    return np.concatenate(rows)[:n]
+
+
+def _gather_full_last_block(pool, table_row, n, which, head):
+    """Mistake: read every slot of the last block (masking dropped)."""
+    return _ORIG_GATHER(pool, table_row, -(-n // BS) * BS, which, head)
+
+
+_ORIG_GATHER = pa.gather_slab
+_ORIG_ATTEND = pa._attend_pair
+
+
+def _attend_no_scale(qf_rows, K, V, scale64):
+    return _ORIG_ATTEND(qf_rows, K, V, 1.0)
+
+
+def _decode_pairs_wrong_group(q, q_dtype, k_pool, v_pool, kv_dtype, block_tables, context_lens,
+                              scale, pairs, k_scale=None, v_scale=None):
+    """Mistake: query head h reads kv head h % Hkv instead of h // G."""
+    Hq, D = q.shape[1], q.shape[2]
+    Hkv = k_pool.shape[1]
+    G = Hq // Hkv
+    out = np.zeros((len(pairs), G, D))
+    for idx, (b, g) in enumerate(pairs):
+        n = int(context_lens[b])
+        for r in range(G):
+            h = g * G + r
+            gg = h % Hkv
+            K = pa._widen(_ORIG_GATHER(k_pool, block_tables[b], n, "k", gg), kv_dtype)
+            V = pa._widen(_ORIG_GATHER(v_pool, block_tables[b], n, "v", gg), kv_dtype)
+            out[idx, r] = pa._attend_pair(pa._widen(q[b, h:h + 1], q_dtype), K, V, float(np.float32(scale)))[0]
+    return out
+
+
+def _pins_pass() -> bool:
+    try:
+        test_brute_force_tiny()
+        for G in (1, 2, 4):
+            test_paged_equals_slab_sdpa(G)
+    except AssertionError:
+        return False
+    return True
+
+
+@pytest.mark.parametrize("mistake", ["v_token_major", "mask_dropped", "scale_dropped", "wrong_group"])
+def test_planted_mistakes_are_caught(monkeypatch, mistake):
+    assert _pins_pass()
+    if mistake == "v_token_major":
+        monkeypatch.setattr(pa, "gather_slab", _gather_v_token_major)
+    elif mistake == "mask_dropped":
+        monkeypatch.setattr(pa, "gather_slab", _gather_full_last_block)
+    elif mistake == "scale_dropped":
+        monkeypatch.setattr(pa, "_attend_pair", _attend_no_scale)
+    elif mistake == "wrong_group":
+        monkeypatch.setattr(pa, "oracle_decode_pairs", _decode_pairs_wrong_group)
+    assert not _pins_pass()
