@@ -1,0 +1,359 @@
+#!/usr/bin/env python3
+"""Paged decode benchmark on one MI355X.
+
+A step is one decode pass of one layer over the whole batch: the partition
+kernel plus the merge kernel (and, for workloads that append, the kv_append
+of one token per sequence first).  Inputs are seeded synthetic data already
+resident in HBM; successive steps rotate over ``--layers`` distinct copies of
+the pool so that the bytes touched between reuses of one copy exceed the
+256 MB Infinity Cache.
+
+Prints ONE JSON line on stdout: KV GB/s read (the algorithmic bytes
+sum_b n_b * 2 * Hkv * D * bytes/element), its share of the 8 TB/s HBM peak,
+decode tokens/s (sequences / step time), the dominant kernel's roofline, and
+the CPU oracle timed on this host over the same workload.
+
+Extra modes used by the profiling commands:
+  --profile-one   warm up, then launch the decode a few times (for rocprofv3)
+  --copy-probe    run a plain device-to-device copy of known size (calibrates
+                  the FETCH_SIZE / WRITE_SIZE counters)
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "paged decode KV GB/s read (% of HBM peak) + decode tokens/s, 8B-shape b64"
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = ["paged_kv_cache_23_amd/csrc/decode.hip", "paged_kv_cache_23_amd/csrc/pkv_internal.h"]
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(workload: str):
+    """HBM bytes per decode-kernel launch from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source; else None."""
+    path = os.path.join(PROFILE_DIR, f"decode_partitions_{workload}_pmc.txt")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_hash = re.search(r"^source_hash:\s*(\w+)", text, re.M)
+    m_bytes = re.search(r"^hbm_bytes_per_launch:\s*([0-9.eE+]+)", text, re.M)
+    if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash():
+        return None
+    return float(m_bytes.group(1))
+
+
+class Runner:
+    """Pre-marshalled C-ABI calls for one workload on the current stream."""
+
+    def __init__(self, wl, layers: int):
+        import torch
+        from paged_kv_cache_23_amd import ops
+
+        self.torch, self.ops, self.wl = torch, ops, wl
+        dev = torch.device("cuda:0")
+        self.q = wl.q.to(dev)
+        k0, v0 = wl.k_pool.to(dev), wl.v_pool.to(dev)
+        # distinct copies of the pool: one per "layer" of the rotation
+        self.k_pools = [k0] + [k0.clone() for _ in range(layers - 1)]
+        self.v_pools = [v0] + [v0.clone() for _ in range(layers - 1)]
+        self.k_scale = None if wl.k_scale is None else wl.k_scale.to(dev)
+        self.v_scale = None if wl.v_scale is None else wl.v_scale.to(dev)
+        self.append = wl.k_new is not None
+        if self.append:
+            self.k_new, self.v_new = wl.k_new.to(dev), wl.v_new.to(dev)
+            self.slots = wl.slot_mapping.to(dev)
+            tables, lens = wl.block_tables_after, wl.context_lens_after
+        else:
+            tables, lens = wl.block_tables, wl.context_lens
+        self.tables, self.lens = tables.to(dev), lens.to(dev)
+        self.B = wl.batch
+        self.max_ctx = int(lens.max())
+        self.out = torch.empty_like(self.q)
+        self.desc = ops.cache_desc(k0, v0, wl.num_q_heads, self.k_scale, self.v_scale)
+        lib = ops.library()
+        self.lib = lib
+        self.part = lib.pkv_partition_tokens(ctypes.byref(self.desc), self.B, self.max_ctx)
+        nbytes = lib.pkv_decode_workspace_bytes(ctypes.byref(self.desc), self.B, self.max_ctx, self.part)
+        self.ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+        self.ws_bytes = self.ws.numel()
+        self.kv_bytes = wl.kv_bytes(after_append=self.append)
+        self.append_bytes = 0
+        if self.append:   # bf16 K/V read + one code per element written
+            T, Hkv, D = wl.k_new.shape
+            elt = 1 if wl.kv_dtype == "fp8" else wl.k_pool.element_size()
+            self.append_bytes = 2 * T * Hkv * D * (wl.k_new.element_size() + elt)
+
+    def stream(self):
+        return ctypes.c_void_p(self.torch.cuda.current_stream().cuda_stream)
+
+    def append_step(self, layer: int, stream):
+        st = self.lib.pkv_kv_append(ctypes.byref(self.desc), self.k_new.data_ptr(), self.v_new.data_ptr(),
+                                    self.slots.data_ptr(), self.slots.shape[0], self.k_pools[layer].data_ptr(),
+                                    self.v_pools[layer].data_ptr(), stream)
+        if st:
+            raise RuntimeError(f"pkv_kv_append failed: {st}")
+
+    def partitions(self, layer: int, stream):
+        st = self.lib.pkv_paged_decode_partitions(
+            ctypes.byref(self.desc), self.q.data_ptr(), self.k_pools[layer].data_ptr(),
+            self.v_pools[layer].data_ptr(), self.tables.data_ptr(), self.tables.shape[1], self.lens.data_ptr(),
+            self.B, self.max_ctx, self.wl.scale, self.part, self.out.data_ptr(), self.ws.data_ptr(),
+            self.ws_bytes, stream)
+        if st:
+            raise RuntimeError(f"pkv_paged_decode_partitions failed: {st}")
+
+    def reduce(self, stream):
+        st = self.lib.pkv_paged_decode_reduce(ctypes.byref(self.desc), self.tables.shape[1], self.lens.data_ptr(),
+                                              self.B, self.max_ctx, self.part, self.out.data_ptr(),
+                                              self.ws.data_ptr(), self.ws_bytes, stream)
+        if st:
+            raise RuntimeError(f"pkv_paged_decode_reduce failed: {st}")
+
+    def step(self, layer: int, stream):
+        if self.append:
+            self.append_step(layer, stream)
+        self.partitions(layer, stream)
+        self.reduce(stream)
+
+
+def check_against_oracle(runner, sample_seqs: int = 4) -> float:
+    """Max |error| of layer 0's output over a few sequences (oracle on the host copy)."""
+    import numpy as np
+
+    import oracle
+    from paged_kv_cache_23_amd.workloads import storage_numpy
+
+    wl = runner.wl
+    runner.torch.cuda.synchronize()
+    got = runner.out.float().cpu().numpy().astype(np.float64)
+    tables = wl.block_tables_after if runner.append else wl.block_tables
+    lens = wl.context_lens_after if runner.append else wl.context_lens
+    k_pool, v_pool = storage_numpy(runner.k_pools[0].cpu()), storage_numpy(runner.v_pools[0].cpu())
+    pairs = [(b, g) for b in range(min(sample_seqs, wl.batch)) for g in range(wl.num_kv_heads)]
+    ref = oracle.oracle_decode_pairs(storage_numpy(wl.q), wl.q_dtype, k_pool, v_pool, wl.kv_dtype,
+                                     tables.numpy(), lens.numpy(), wl.scale, pairs,
+                                     None if wl.k_scale is None else wl.k_scale.numpy(),
+                                     None if wl.v_scale is None else wl.v_scale.numpy())
+    G = wl.num_q_heads // wl.num_kv_heads
+    rows = np.stack([got[b, g * G:(g + 1) * G] for b, g in pairs])
+    return float(np.max(np.abs(rows - ref)))
+
+
+def cpu_baseline(wl, min_seconds: float = 10.0, max_reps: int = 20):
+    """The oracle, as it stands, on this host: the whole decode step of the
+    workload (every sequence and kv head), repeated until min_seconds."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    from paged_kv_cache_23_amd.workloads import storage_numpy
+
+    q, kp, vp = storage_numpy(wl.q), storage_numpy(wl.k_pool), storage_numpy(wl.v_pool)
+    ks = None if wl.k_scale is None else wl.k_scale.numpy()
+    vs = None if wl.v_scale is None else wl.v_scale.numpy()
+    tables, lens = wl.block_tables.numpy(), wl.context_lens.numpy()
+    reps, t0 = 0, time.perf_counter()
+    with threadpool_limits(1):
+        while reps < max_reps:
+            oracle.oracle_decode(q, wl.q_dtype, kp, vp, wl.kv_dtype, tables, lens, wl.scale, ks, vs)
+            reps += 1
+            if time.perf_counter() - t0 >= min_seconds:
+                break
+    sec = (time.perf_counter() - t0) / reps
+    return {
+        "value": round(wl.kv_bytes() / sec / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"whole {wl.name} decode step (all {wl.batch} sequences x {wl.num_kv_heads} kv heads, "
+                  f"{wl.kv_bytes() / 1e6:.0f} MB of KV) in fp64 NumPy on one host thread, "
+                  f"{reps} repetitions, {sec:.2f} s each",
+        "seconds_per_step": round(sec, 3),
+        "decode_tokens_per_s": round(wl.batch / sec, 2),
+    }
+
+
+def run_bench(args) -> dict:
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_23_amd import workloads as W
+
+    wl = W.WORKLOADS[args.workload]()
+    log(f"workload {wl.name}: B={wl.batch} Hq={wl.num_q_heads} Hkv={wl.num_kv_heads} D={wl.head_dim} "
+        f"kv={wl.kv_dtype} blocks={wl.num_blocks} KV={wl.kv_bytes() / 1e6:.1f} MB")
+    runner = Runner(wl, args.layers)
+    log(f"partition={runner.part} tokens, workspace={runner.ws_bytes} B, layers={args.layers}")
+    torch.cuda.synchronize()
+
+    # one checked step on layer 0 (the output is compared with the oracle below)
+    s = runner.stream()
+    runner.step(0, s)
+    torch.cuda.synchronize()
+    err = check_against_oracle(runner)
+    log(f"parity on sampled sequences: max|err| = {err:.3g}")
+
+    L = args.layers
+    for i in range(args.warmup):
+        runner.step(i % L, s)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    t_wall0 = time.perf_counter()
+    start_ev = torch.cuda.Event(enable_timing=True)
+    end_ev = torch.cuda.Event(enable_timing=True)
+    start_ev.record()
+    for i in range(K):
+        layer = i % L
+        if runner.append:
+            runner.append_step(layer, s)
+        ev[i][0].record()
+        runner.partitions(layer, s)
+        ev[i][1].record()
+        runner.reduce(s)
+        ev[i][2].record()
+    end_ev.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall0
+    total_ms = start_ev.elapsed_time(end_ev)
+    part_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
+    red_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
+    ms_per_step = total_ms / K
+    log(f"{K} steps: {total_ms:.3f} ms on the stream, {wall * 1e3:.3f} ms wall; partition kernel "
+        f"mean {part_ms.mean() * 1e3:.1f} us (p10 {np.percentile(part_ms, 10) * 1e3:.1f}, "
+        f"p90 {np.percentile(part_ms, 90) * 1e3:.1f}), merge kernel mean {red_ms.mean() * 1e3:.1f} us")
+
+    step_bytes = runner.kv_bytes + runner.append_bytes
+    gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
+    kern_gbs = runner.kv_bytes / (part_ms.mean() * 1e-3) / 1e9
+    traffic = committed_traffic(wl.name)
+    result = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"f32": "f32", "bf16": "bf16", "fp8": "fp8-e4m3 kv / bf16 q"}[wl.kv_dtype],
+        "data": "synthetic",
+        "config": {
+            "workload": f"{wl.name}: single-layer paged decode, batch {wl.batch}, {wl.num_q_heads} q / "
+                        f"{wl.num_kv_heads} kv heads, head_dim {wl.head_dim}, 16-token blocks, "
+                        f"shuffled pool, {args.layers}-layer pool rotation",
+            "batch": wl.batch,
+            "context_tokens": int((wl.context_lens_after if runner.append else wl.context_lens).sum()),
+            "kv_bytes_per_step": step_bytes,
+            "partition_tokens": runner.part,
+        },
+        "hbm_peak_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "decode_tokens_per_s": round(wl.batch / (ms_per_step * 1e-3), 1),
+        "max_abs_err_sampled": err,
+        "roofline": {
+            "kernel": "decode_partitions_kernel",
+            "bound": "hbm",
+            "achieved": round(kern_gbs, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(kern_gbs / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": runner.kv_bytes,
+            "mean_launch_us": round(float(part_ms.mean()) * 1e3, 2),
+            "merge_kernel_mean_us": round(float(red_ms.mean()) * 1e3, 2),
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on the host ...")
+        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    else:
+        result["cpu_baseline"] = None
+    return result
+
+
+def profile_one(args) -> None:
+    import torch
+
+    from paged_kv_cache_23_amd import workloads as W
+
+    wl = W.WORKLOADS[args.workload]()
+    runner = Runner(wl, args.layers)
+    s = runner.stream()
+    for i in range(args.warmup):
+        runner.step(i % args.layers, s)
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        runner.step(i % args.layers, s)
+    torch.cuda.synchronize()
+    log(f"profiled {args.steps} steps of {wl.name} (partition {runner.part}, {runner.kv_bytes} KV bytes/step)")
+
+
+def copy_probe(args) -> None:
+    import torch
+
+    n = 1 << 30   # 1 GiB read + 1 GiB written per copy
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"copied {n} bytes {args.steps} times")
+
+
+def main() -> int:
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default="llama3-8b-b64")
+    p.add_argument("--layers", type=int, default=4)
+    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--profile-one", action="store_true")
+    p.add_argument("--copy-probe", action="store_true")
+    args = p.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr, flush=True)
+        return 2
+    if args.copy_probe:
+        copy_probe(args)
+        return 0
+    if args.profile_one:
+        profile_one(args)
+        return 0
+    result = run_bench(args)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

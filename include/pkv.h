@@ -1,0 +1,161 @@
+/*
+ * pkv.h - paged KV-cache decode attention on AMD MI355X (gfx950).
+ *
+ * Plain C ABI: device pointers, sizes and a HIP stream handle, nothing else.
+ * The library allocates no memory, keeps no pointer after a call returns and
+ * holds no mutable global state; every call is asynchronous on `stream`
+ * (a hipStream_t passed as void*, NULL for the default stream).
+ *
+ * The operation follows the source pages:
+ *  - Habr KV-Cache article (habr.com/ru/articles/1021832), section 4
+ *    "Recalling PagedAttention": the cache is a pool of fixed 16-token
+ *    blocks that need not be contiguous; a per-sequence block table maps
+ *    logical block j to a physical block id.
+ *  - Same article, section 5 "How vLLM combines FlashAttention and
+ *    PagedAttention": one decode call takes one query per sequence and head,
+ *    the K and V caches, an int32 block table [batch, max_num_blocks] of
+ *    physical ids, and the true length of each sequence; the kernel gathers
+ *    the scattered blocks itself.
+ *  - Same article, section 3 "Recalling FlashAttention": the result is exact
+ *    attention softmax(q K^T * scale) V, reached with an online softmax.
+ *  - Same article, section 1 "Prefill and Decode": each decode step appends
+ *    the new token's K and V to the cache.
+ *
+ * Layout (this library's choice; one (block, kv head) tile is contiguous):
+ *   q       [num_seqs][num_q_heads][head_dim]                 q_dtype
+ *   out     [num_seqs][num_q_heads][head_dim]                 q_dtype
+ *   k_pool  [num_blocks][num_kv_heads][16][head_dim]          kv_dtype (token-major tile)
+ *   v_pool  [num_blocks][num_kv_heads][head_dim][16]          kv_dtype (dim-major tile)
+ *   block_tables [num_seqs][max_blocks_per_seq] int32 physical block ids
+ *   context_lens [num_seqs] int32, tokens held by each sequence
+ *   slot_mapping [num_tokens] int64, slot = block * 16 + offset
+ * Query head h reads kv head h / (num_q_heads / num_kv_heads): contiguous
+ * query groups share a kv head (grouped-query attention, Habr article
+ * section 2, "GQA: 8x reduction").
+ *
+ * Status: every function returns PKV_OK (0) or a negative PKV_E* code.
+ * Argument checks run on the host before any HIP call.  Data-dependent
+ * conditions are not checked on the host; the kernels keep every access in
+ * bounds regardless (see each function).
+ */
+#ifndef PKV_H_
+#define PKV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PKV_OK 0
+#define PKV_EINVAL (-1)       /* null pointer, bad size or shape */
+#define PKV_EUNSUPPORTED (-2) /* dtype / head_dim / group size not built */
+#define PKV_EWORKSPACE (-3)   /* workspace missing or too small */
+#define PKV_ELAUNCH (-4)      /* the HIP runtime reported an error */
+
+#define PKV_BLOCK_SIZE 16
+
+typedef enum pkv_dtype {
+  PKV_F32 = 0,      /* IEEE binary32 */
+  PKV_BF16 = 1,     /* bfloat16 */
+  PKV_FP8_E4M3 = 2  /* OCP E4M3FN, one float32 scale per kv head */
+} pkv_dtype;
+
+/* Shape and format of one layer's cache.
+ * Supported: head_dim 64 or 128; block_size 16; num_q_heads a multiple of
+ * num_kv_heads with at most 16 query heads per kv head; (kv, q) dtypes
+ * (F32, F32), (BF16, BF16) or (FP8_E4M3, BF16).  For FP8 caches, k_scale and
+ * v_scale are device arrays [num_kv_heads] of float32: a stored code c of
+ * head h means decode(c) * scale[h].  They must be NULL for other dtypes. */
+typedef struct pkv_cache_desc {
+  int32_t num_blocks;
+  int32_t block_size;
+  int32_t num_kv_heads;
+  int32_t num_q_heads;
+  int32_t head_dim;
+  int32_t kv_dtype;
+  int32_t q_dtype;
+  const float* k_scale;
+  const float* v_scale;
+} pkv_cache_desc;
+
+/* Write the K and V of num_tokens new tokens into their slots.
+ * (Habr article, section 1: one new token per sequence is appended each
+ * decode step; section 4, step-by-step example: it goes to the next slot of
+ * the sequence's last block, the caller opening a fresh block when full.)
+ *   k_new, v_new  device [num_tokens][num_kv_heads][head_dim]; q_dtype for an
+ *                 FP8 cache (quantised here), else kv_dtype (bit copy)
+ *   slot_mapping  device [num_tokens]; a slot outside [0, num_blocks * 16) is
+ *                 padding and writes nothing
+ *   k_pool, v_pool device pools, updated in place
+ * FP8: code = E4M3 round-to-nearest-even, saturating to +-448, of the IEEE
+ * float32 quotient x / scale[h].  Slots must be distinct and must not lie in
+ * blocks shared with other sequences; two tokens with the same slot leave
+ * one of them.  num_tokens == 0 is a no-op. */
+int pkv_kv_append(const pkv_cache_desc* desc, const void* k_new, const void* v_new,
+                  const int64_t* slot_mapping, int32_t num_tokens, void* k_pool,
+                  void* v_pool, void* stream);
+
+/* Partition size (tokens, a multiple of 32) that pkv_paged_decode uses for
+ * this batch shape: long contexts are split into partitions whose partial
+ * softmax states are merged by a second kernel.  Returns a negative status
+ * on bad arguments. */
+int32_t pkv_partition_tokens(const pkv_cache_desc* desc, int32_t num_seqs,
+                             int32_t max_context_len);
+
+/* Device workspace bytes that a decode with this shape needs; 0 when no
+ * sequence can span more than one partition.  partition_tokens == 0 means
+ * pkv_partition_tokens(...).  Returns 0 on bad arguments. */
+size_t pkv_decode_workspace_bytes(const pkv_cache_desc* desc, int32_t num_seqs,
+                                  int32_t max_context_len, int32_t partition_tokens);
+
+/* Decode attention for one query token per sequence over its paged cache:
+ *   out[b][h] = softmax_t(scale * q[b][h] . K_b[t]) V_b[t],  t < context_lens[b]
+ * where K_b / V_b are sequence b's tokens gathered through its block table,
+ * and h reads kv head h / group.  Only table entries j < ceil(n / 16) are
+ * read; token slots at or past n in the last block are ignored (they may
+ * hold anything, NaN included).  A sequence of length 0 gets a zero output.
+ * Lengths are taken as min(context_lens[b], max_context_len,
+ * 16 * max_blocks_per_seq); block ids are clamped into [0, num_blocks).
+ * Accumulation is float32; out is rounded once to q_dtype (nearest even).
+ *   workspace  device buffer of pkv_decode_workspace_bytes(..., 0) bytes
+ *              (may be NULL when that is 0); its contents are scratch. */
+int pkv_paged_decode(const pkv_cache_desc* desc, const void* q, const void* k_pool,
+                     const void* v_pool, const int32_t* block_tables,
+                     int32_t max_blocks_per_seq, const int32_t* context_lens,
+                     int32_t num_seqs, int32_t max_context_len, float scale, void* out,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* The two kernels of pkv_paged_decode as separate calls, with an explicit
+ * partition size (a positive multiple of 32 up to 2048, or 0 for the default).
+ * pkv_paged_decode_partitions writes the output of every sequence that fits
+ * in one partition and a float32 partial state (running max, sum, unnormalised
+ * accumulator) per partition of the others into the workspace;
+ * pkv_paged_decode_reduce merges those partials into out (section 3's
+ * rescale by exp(m_old - m_new), applied across partitions).  Calling them
+ * in order on one stream equals pkv_paged_decode with that partition size. */
+int pkv_paged_decode_partitions(const pkv_cache_desc* desc, const void* q,
+                                const void* k_pool, const void* v_pool,
+                                const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                const int32_t* context_lens, int32_t num_seqs,
+                                int32_t max_context_len, float scale,
+                                int32_t partition_tokens, void* out, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
+int pkv_paged_decode_reduce(const pkv_cache_desc* desc, int32_t max_blocks_per_seq,
+                            const int32_t* context_lens, int32_t num_seqs,
+                            int32_t max_context_len, int32_t partition_tokens, void* out,
+                            const void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static description of a status code. */
+const char* pkv_strerror(int status);
+
+/* Library version string. */
+const char* pkv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H_ */

@@ -1,0 +1,62 @@
+"""Compile the HIP sources into ``libpkv.so`` (in-tree) with hipcc for gfx950.
+
+Run ``python -m paged_kv_cache_23_amd.build`` or call ``build()``.  The
+library is written next to this file; the Python binding loads it from
+there.
+"""
+
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+LIB_PATH = os.path.join(HERE, "libpkv.so")
+SOURCES = ["api.hip", "append.hip", "decode.hip"]
+
+HIP_FLAGS = [
+    "--offload-arch=gfx950",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-shared",
+    # keep hipcc from forming packed-fp32 instructions (v_pk_fma_f32 & co.)
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall",
+    "-Wno-unused-command-line-argument",
+]
+
+
+def hipcc() -> str:
+    exe = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(exe):
+        raise RuntimeError("hipcc not found: install ROCm or put hipcc on PATH")
+    return exe
+
+
+def build(verbose: bool = False, extra_flags=None) -> str:
+    """Compile every source and return the library path."""
+    tmp = LIB_PATH + ".tmp"
+    cmd = [hipcc(), *HIP_FLAGS, *(extra_flags or []),
+           "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+           *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    # hipcc's host pass does not know the packed-fp32 feature; that note is harmless
+    noise = "'-packed-fp32-ops' is not a recognized feature"
+    msgs = "\n".join(l for l in (res.stdout + res.stderr).splitlines() if noise not in l)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{msgs}")
+    if verbose and msgs.strip():
+        print(msgs, flush=True)
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,222 @@
+// C ABI of libpkv: host-side argument checks, partition choice, workspace
+// layout and kernel dispatch.  Declarations and contracts: include/pkv.h.
+
+#include "pkv.h"
+#include "pkv_internal.h"
+
+#include <stdint.h>
+
+namespace {
+
+using pkv::DecodeArgs;
+
+constexpr size_t kWsAlign = 256;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_desc(const pkv_cache_desc* d) {
+  if (!d) return PKV_EINVAL;
+  if (d->num_blocks <= 0 || d->num_kv_heads <= 0 || d->num_q_heads <= 0 || d->head_dim <= 0)
+    return PKV_EINVAL;
+  if (d->block_size != PKV_BLOCK_SIZE) return PKV_EINVAL;
+  if (d->num_q_heads % d->num_kv_heads != 0) return PKV_EINVAL;
+  if (d->num_q_heads / d->num_kv_heads > pkv::kMaxGroup) return PKV_EUNSUPPORTED;
+  if (d->head_dim != 64 && d->head_dim != 128) return PKV_EUNSUPPORTED;
+  const int kv = d->kv_dtype, qd = d->q_dtype;
+  if (kv < PKV_F32 || kv > PKV_FP8_E4M3 || qd < PKV_F32 || qd > PKV_FP8_E4M3) return PKV_EINVAL;
+  const bool ok = (kv == PKV_F32 && qd == PKV_F32) || (kv == PKV_BF16 && qd == PKV_BF16) ||
+                  (kv == PKV_FP8_E4M3 && qd == PKV_BF16);
+  if (!ok) return PKV_EUNSUPPORTED;
+  if (kv == PKV_FP8_E4M3) {
+    if (!d->k_scale || !d->v_scale) return PKV_EINVAL;
+  } else if (d->k_scale || d->v_scale) {
+    return PKV_EINVAL;
+  }
+  return PKV_OK;
+}
+
+// Default partition size.  A workgroup streams one partition of one
+// (sequence, kv head); partitions must be long enough that each of its
+// four waves streams several 32-token chunks, and numerous enough that the
+// grid covers the 256 compute units several times over.
+int32_t default_partition(const pkv_cache_desc* d, int32_t num_seqs, int32_t max_ctx) {
+  const int64_t pairs = (int64_t)num_seqs * d->num_kv_heads;
+  int32_t part = 512;
+  // grow the partition while the grid would still hold >= 2048 workgroups
+  while (part < pkv::kMaxPartitionTokens && pairs * ((max_ctx + 2 * part - 1) / (2 * part)) >= 2048) part *= 2;
+  return part;
+}
+
+int32_t resolve_partition(const pkv_cache_desc* d, int32_t num_seqs, int32_t max_ctx, int32_t part) {
+  if (part == 0) return default_partition(d, num_seqs, max_ctx);
+  if (part < 0 || part % pkv::kChunkTokens != 0 || part > pkv::kMaxPartitionTokens) return -1;
+  return part;
+}
+
+int32_t num_partitions(int32_t max_ctx, int32_t part) {
+  if (max_ctx <= 0) return 1;
+  return (int32_t)(((int64_t)max_ctx + part - 1) / part);
+}
+
+size_t workspace_bytes(const pkv_cache_desc* d, int32_t num_seqs, int32_t max_ctx, int32_t part) {
+  const int32_t P = num_partitions(max_ctx, part);
+  if (P <= 1) return 0;
+  const size_t rows = (size_t)num_seqs * d->num_q_heads * P;
+  const size_t acc = (rows * d->head_dim * sizeof(float) + kWsAlign - 1) / kWsAlign * kWsAlign;
+  return acc + rows * 2 * sizeof(float);
+}
+
+int check_decode_args(const pkv_cache_desc* d, const void* q, const void* k_pool, const void* v_pool,
+                      const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens,
+                      int32_t num_seqs, int32_t max_ctx, const void* out) {
+  int st = check_desc(d);
+  if (st != PKV_OK) return st;
+  if (!q || !k_pool || !v_pool || !block_tables || !context_lens || !out) return PKV_EINVAL;
+  if (num_seqs < 0 || max_blocks <= 0 || max_ctx < 0) return PKV_EINVAL;
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out)) return PKV_EINVAL;
+  return PKV_OK;
+}
+
+DecodeArgs make_args(const pkv_cache_desc* d, const void* q, const void* k_pool, const void* v_pool,
+                     const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens,
+                     int32_t num_seqs, int32_t max_ctx, float scale, int32_t part, void* out,
+                     void* workspace) {
+  DecodeArgs a{};
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.k_scale = d->k_scale;
+  a.v_scale = d->v_scale;
+  a.out = out;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = d->num_q_heads;
+  a.num_kv_heads = d->num_kv_heads;
+  a.group = d->num_q_heads / d->num_kv_heads;
+  a.head_dim = d->head_dim;
+  a.max_blocks = max_blocks;
+  a.num_blocks = d->num_blocks;
+  a.max_context_len = max_ctx;
+  a.part_tokens = part;
+  a.num_parts = num_partitions(max_ctx, part);
+  a.kv_dtype = d->kv_dtype;
+  a.scale = scale;
+  if (a.num_parts > 1) {
+    const size_t rows = (size_t)num_seqs * d->num_q_heads * a.num_parts;
+    const size_t acc = (rows * d->head_dim * sizeof(float) + kWsAlign - 1) / kWsAlign * kWsAlign;
+    a.ws_acc = static_cast<float*>(workspace);
+    a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + acc);
+  }
+  return a;
+}
+
+int launch_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ELAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+int pkv_kv_append(const pkv_cache_desc* desc, const void* k_new, const void* v_new,
+                  const int64_t* slot_mapping, int32_t num_tokens, void* k_pool, void* v_pool,
+                  void* stream) {
+  int st = check_desc(desc);
+  if (st != PKV_OK) return st;
+  if (num_tokens < 0) return PKV_EINVAL;
+  if (num_tokens == 0) return PKV_OK;
+  if (!k_new || !v_new || !slot_mapping || !k_pool || !v_pool) return PKV_EINVAL;
+  pkv::AppendArgs a{};
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.slot_mapping = slot_mapping;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.k_scale = desc->k_scale;
+  a.v_scale = desc->v_scale;
+  a.num_tokens = num_tokens;
+  a.num_kv_heads = desc->num_kv_heads;
+  a.head_dim = desc->head_dim;
+  a.num_blocks = desc->num_blocks;
+  a.kv_dtype = desc->kv_dtype;
+  return launch_status(pkv::launch_append(a, static_cast<hipStream_t>(stream)));
+}
+
+int32_t pkv_partition_tokens(const pkv_cache_desc* desc, int32_t num_seqs, int32_t max_context_len) {
+  int st = check_desc(desc);
+  if (st != PKV_OK) return st;
+  if (num_seqs < 0 || max_context_len < 0) return PKV_EINVAL;
+  return default_partition(desc, num_seqs, max_context_len);
+}
+
+size_t pkv_decode_workspace_bytes(const pkv_cache_desc* desc, int32_t num_seqs, int32_t max_context_len,
+                                  int32_t partition_tokens) {
+  if (check_desc(desc) != PKV_OK || num_seqs < 0 || max_context_len < 0) return 0;
+  const int32_t part = resolve_partition(desc, num_seqs, max_context_len, partition_tokens);
+  if (part <= 0) return 0;
+  return workspace_bytes(desc, num_seqs, max_context_len, part);
+}
+
+int pkv_paged_decode_partitions(const pkv_cache_desc* desc, const void* q, const void* k_pool,
+                                const void* v_pool, const int32_t* block_tables,
+                                int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+                                int32_t max_context_len, float scale, int32_t partition_tokens, void* out,
+                                void* workspace, size_t ws_bytes, void* stream) {
+  int st = check_decode_args(desc, q, k_pool, v_pool, block_tables, max_blocks_per_seq, context_lens,
+                             num_seqs, max_context_len, out);
+  if (st != PKV_OK) return st;
+  const int32_t part = resolve_partition(desc, num_seqs, max_context_len, partition_tokens);
+  if (part <= 0) return PKV_EINVAL;
+  const size_t need = workspace_bytes(desc, num_seqs, max_context_len, part);
+  if (need && (!workspace || ws_bytes < need)) return PKV_EWORKSPACE;
+  if (need && !aligned16(workspace)) return PKV_EINVAL;
+  if (num_seqs == 0) return PKV_OK;
+  DecodeArgs a = make_args(desc, q, k_pool, v_pool, block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                           max_context_len, scale, part, out, workspace);
+  return launch_status(pkv::launch_decode_partitions(a, static_cast<hipStream_t>(stream)));
+}
+
+int pkv_paged_decode_reduce(const pkv_cache_desc* desc, int32_t max_blocks_per_seq,
+                            const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
+                            int32_t partition_tokens, void* out, const void* workspace, size_t ws_bytes,
+                            void* stream) {
+  int st = check_desc(desc);
+  if (st != PKV_OK) return st;
+  if (!context_lens || !out || num_seqs < 0 || max_context_len < 0 || max_blocks_per_seq <= 0)
+    return PKV_EINVAL;
+  if (!aligned16(out)) return PKV_EINVAL;
+  const int32_t part = resolve_partition(desc, num_seqs, max_context_len, partition_tokens);
+  if (part <= 0) return PKV_EINVAL;
+  const size_t need = workspace_bytes(desc, num_seqs, max_context_len, part);
+  if (need == 0 || num_seqs == 0) return PKV_OK;   // nothing spans two partitions
+  if (!workspace || ws_bytes < need) return PKV_EWORKSPACE;
+  // the merge reads lengths and partials only; q, pools and tables are unused
+  DecodeArgs a = make_args(desc, out, out, out, context_lens, max_blocks_per_seq, context_lens, num_seqs,
+                           max_context_len, 1.f, part, out, const_cast<void*>(workspace));
+  return launch_status(pkv::launch_decode_reduce(a, static_cast<hipStream_t>(stream)));
+}
+
+int pkv_paged_decode(const pkv_cache_desc* desc, const void* q, const void* k_pool, const void* v_pool,
+                     const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                     int32_t num_seqs, int32_t max_context_len, float scale, void* out, void* workspace,
+                     size_t ws_bytes, void* stream) {
+  int st = pkv_paged_decode_partitions(desc, q, k_pool, v_pool, block_tables, max_blocks_per_seq, context_lens,
+                                       num_seqs, max_context_len, scale, 0, out, workspace, ws_bytes, stream);
+  if (st != PKV_OK) return st;
+  return pkv_paged_decode_reduce(desc, max_blocks_per_seq, context_lens, num_seqs, max_context_len, 0, out,
+                                 workspace, ws_bytes, stream);
+}
+
+const char* pkv_strerror(int status) {
+  switch (status) {
+    case PKV_OK: return "ok";
+    case PKV_EINVAL: return "invalid argument";
+    case PKV_EUNSUPPORTED: return "unsupported dtype, head_dim or group size";
+    case PKV_EWORKSPACE: return "workspace missing or too small";
+    case PKV_ELAUNCH: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+const char* pkv_version(void) { return "pkv 0.1.0 gfx950"; }
+
+}  // extern "C"

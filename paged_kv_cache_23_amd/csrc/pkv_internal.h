@@ -1,0 +1,62 @@
+// Internal launch interface between the C ABI layer and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pkv {
+
+constexpr int kBlockTokens = 16;    // tokens per cache block
+constexpr int kChunkTokens = 32;    // tokens one wave consumes per step: two blocks
+constexpr int kDecodeWaves = 4;     // waves per decode workgroup
+constexpr int kMaxGroup = 16;       // query heads per kv head that one MFMA column tile holds
+constexpr int kMaxPartitionTokens = 2048;   // block ids of a partition fit two VGPRs of a wave
+
+enum KvType : int32_t { kF32 = 0, kBF16 = 1, kFP8 = 2 };
+
+struct DecodeArgs {
+  const void* q;
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  const float* k_scale;
+  const float* v_scale;
+  void* out;
+  float* ws_acc;   // [num_seqs][num_q_heads][num_parts][head_dim]
+  float* ws_ml;    // [num_seqs][num_q_heads][num_parts][2]  (max in log2 units, sum)
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t group;
+  int32_t head_dim;
+  int32_t max_blocks;
+  int32_t num_blocks;
+  int32_t max_context_len;
+  int32_t part_tokens;
+  int32_t num_parts;
+  int32_t kv_dtype;
+  float scale;
+};
+
+struct AppendArgs {
+  const void* k_new;
+  const void* v_new;
+  const int64_t* slot_mapping;
+  void* k_pool;
+  void* v_pool;
+  const float* k_scale;
+  const float* v_scale;
+  int32_t num_tokens;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t num_blocks;
+  int32_t kv_dtype;
+};
+
+hipError_t launch_decode_partitions(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_reduce(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
+
+}  // namespace pkv

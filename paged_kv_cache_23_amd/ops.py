@@ -1,0 +1,238 @@
+"""ctypes binding of ``libpkv.so``: argument marshalling only.
+
+Each function checks that the torch tensors match the C ABI's layout
+(device, dtype, shape, contiguity), passes their device pointers and the
+current HIP stream, and raises on a non-zero status.  Every step of the
+computation runs in the library's HIP kernels; there is no fallback path.
+Shapes and the cache layout are documented in ``include/pkv.h``:
+
+* q, out   ``[B, Hq, D]``            float32 or bfloat16
+* k_pool   ``[NB, Hkv, 16, D]``      float32, bfloat16 or uint8 (E4M3 codes)
+* v_pool   ``[NB, Hkv, D, 16]``
+* block_tables ``[B, max_blocks]`` int32, context_lens ``[B]`` int32
+* slot_mapping ``[T]`` int64; k_new / v_new ``[T, Hkv, D]``
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+from .build import LIB_PATH
+
+F32, BF16, FP8_E4M3 = 0, 1, 2
+BLOCK_SIZE = 16
+
+_lib = None
+
+
+class CacheDesc(ctypes.Structure):
+    _fields_ = [
+        ("num_blocks", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("kv_dtype", ctypes.c_int32),
+        ("q_dtype", ctypes.c_int32),
+        ("k_scale", ctypes.c_void_p),
+        ("v_scale", ctypes.c_void_p),
+    ]
+
+
+def library() -> ctypes.CDLL:
+    """Load ``libpkv.so`` once; a missing library is an error, never a fallback."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -c 'import __graft_entry__ as g; g.build()'`")
+        lib = ctypes.CDLL(LIB_PATH)
+        P, I32, SZ, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
+        D = ctypes.POINTER(CacheDesc)
+        sigs = {
+            "pkv_kv_append": (ctypes.c_int, [D, P, P, P, I32, P, P, P]),
+            "pkv_partition_tokens": (I32, [D, I32, I32]),
+            "pkv_decode_workspace_bytes": (SZ, [D, I32, I32, I32]),
+            "pkv_paged_decode": (ctypes.c_int, [D, P, P, P, P, I32, P, I32, I32, F, P, P, SZ, P]),
+            "pkv_paged_decode_partitions": (ctypes.c_int, [D, P, P, P, P, I32, P, I32, I32, F, I32, P, P, SZ, P]),
+            "pkv_paged_decode_reduce": (ctypes.c_int, [D, I32, P, I32, I32, I32, P, P, SZ, P]),
+            "pkv_strerror": (ctypes.c_char_p, [ctypes.c_int]),
+            "pkv_version": (ctypes.c_char_p, []),
+        }
+        for name, (res, args) in sigs.items():
+            fn = getattr(lib, name)
+            fn.restype, fn.argtypes = res, args
+        _lib = lib
+    return _lib
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        raise RuntimeError(f"{what}: {library().pkv_strerror(status).decode()} (status {status})")
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _require(t: torch.Tensor, name: str, dtypes, ndim: int) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor, got {t.device}")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _kv_code(pool: torch.Tensor) -> int:
+    if pool.dtype == torch.float32:
+        return F32
+    if pool.dtype == torch.bfloat16:
+        return BF16
+    if pool.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return FP8_E4M3
+    raise ValueError(f"unsupported cache dtype {pool.dtype}")
+
+
+def cache_desc(k_pool: torch.Tensor, v_pool: torch.Tensor, num_q_heads: int,
+               k_scale: Optional[torch.Tensor] = None,
+               v_scale: Optional[torch.Tensor] = None) -> CacheDesc:
+    """Descriptor for pools ``k_pool [NB, Hkv, 16, D]`` / ``v_pool [NB, Hkv, D, 16]``."""
+    kv = _kv_code(k_pool)
+    _require(k_pool, "k_pool", (k_pool.dtype,), 4)
+    _require(v_pool, "v_pool", (k_pool.dtype,), 4)
+    NB, Hkv, bs, D = k_pool.shape
+    if bs != BLOCK_SIZE or tuple(v_pool.shape) != (NB, Hkv, D, BLOCK_SIZE):
+        raise ValueError(f"pool shapes {tuple(k_pool.shape)} / {tuple(v_pool.shape)} do not match "
+                         "[NB, Hkv, 16, D] / [NB, Hkv, D, 16]")
+    if kv == FP8_E4M3:
+        if k_scale is None or v_scale is None:
+            raise ValueError("an fp8 cache needs k_scale and v_scale")
+        for name, sc in (("k_scale", k_scale), ("v_scale", v_scale)):
+            _require(sc, name, (torch.float32,), 1)
+            if sc.shape[0] != Hkv:
+                raise ValueError(f"{name} must have {Hkv} entries")
+    elif k_scale is not None or v_scale is not None:
+        raise ValueError("scales are only used with an fp8 cache")
+    return CacheDesc(NB, BLOCK_SIZE, Hkv, int(num_q_heads), D, kv,
+                     F32 if kv == F32 else BF16, _ptr(k_scale), _ptr(v_scale))
+
+
+def kv_append(k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: torch.Tensor,
+              k_pool: torch.Tensor, v_pool: torch.Tensor, k_scale: Optional[torch.Tensor] = None,
+              v_scale: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Write each token's K/V ``[T, Hkv, D]`` into slot ``slot_mapping[t]`` of the pools (in place)."""
+    Hkv = k_pool.shape[1]
+    desc = cache_desc(k_pool, v_pool, Hkv, k_scale, v_scale)
+    new_dtype = torch.bfloat16 if desc.kv_dtype == FP8_E4M3 else k_pool.dtype
+    _require(k_new, "k_new", (new_dtype,), 3)
+    _require(v_new, "v_new", (new_dtype,), 3)
+    _require(slot_mapping, "slot_mapping", (torch.int64,), 1)
+    T = slot_mapping.shape[0]
+    if tuple(k_new.shape) != (T, Hkv, desc.head_dim) or k_new.shape != v_new.shape:
+        raise ValueError(f"k_new/v_new must be [{T}, {Hkv}, {desc.head_dim}]")
+    _check(library().pkv_kv_append(ctypes.byref(desc), _ptr(k_new), _ptr(v_new), _ptr(slot_mapping),
+                                   T, _ptr(k_pool), _ptr(v_pool), _stream(stream)), "pkv_kv_append")
+
+
+def _decode_checks(q, k_pool, v_pool, block_tables, context_lens, k_scale, v_scale, out):
+    desc = cache_desc(k_pool, v_pool, q.shape[1] if q.dim() == 3 else 0, k_scale, v_scale)
+    q_dtype = torch.float32 if desc.q_dtype == F32 else torch.bfloat16
+    _require(q, "q", (q_dtype,), 3)
+    B = q.shape[0]
+    if q.shape[2] != desc.head_dim:
+        raise ValueError(f"q head_dim {q.shape[2]} != cache head_dim {desc.head_dim}")
+    _require(block_tables, "block_tables", (torch.int32,), 2)
+    _require(context_lens, "context_lens", (torch.int32,), 1)
+    if block_tables.shape[0] != B or context_lens.shape[0] != B:
+        raise ValueError("block_tables / context_lens must have one row per sequence")
+    if out is None:
+        out = torch.empty_like(q)
+    _require(out, "out", (q_dtype,), 3)
+    if out.shape != q.shape:
+        raise ValueError("out must have the shape of q")
+    return desc, out
+
+
+def _max_ctx(block_tables: torch.Tensor, max_context_len: Optional[int]) -> int:
+    # without a host-side value, the table width bounds every length (no device sync)
+    return int(max_context_len) if max_context_len is not None else BLOCK_SIZE * block_tables.shape[1]
+
+
+def partition_tokens(k_pool, v_pool, num_q_heads: int, num_seqs: int, max_context_len: int,
+                     k_scale=None, v_scale=None) -> int:
+    desc = cache_desc(k_pool, v_pool, num_q_heads, k_scale, v_scale)
+    res = library().pkv_partition_tokens(ctypes.byref(desc), num_seqs, max_context_len)
+    _check(min(res, 0), "pkv_partition_tokens")
+    return res
+
+
+def decode_workspace_bytes(k_pool, v_pool, num_q_heads: int, num_seqs: int, max_context_len: int,
+                           partition: int = 0, k_scale=None, v_scale=None) -> int:
+    desc = cache_desc(k_pool, v_pool, num_q_heads, k_scale, v_scale)
+    return int(library().pkv_decode_workspace_bytes(ctypes.byref(desc), num_seqs, max_context_len, partition))
+
+
+def _workspace(nbytes: int, like: torch.Tensor, workspace: Optional[torch.Tensor]):
+    if nbytes == 0:
+        return workspace, 0
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=like.device)
+    if workspace.device.type != "cuda" or workspace.numel() * workspace.element_size() < nbytes:
+        raise ValueError(f"workspace must be a device buffer of at least {nbytes} bytes")
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def paged_decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                 block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
+                 out: Optional[torch.Tensor] = None, k_scale: Optional[torch.Tensor] = None,
+                 v_scale: Optional[torch.Tensor] = None, max_context_len: Optional[int] = None,
+                 workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Decode attention of one query per sequence over its paged K/V; returns ``out``."""
+    desc, out = _decode_checks(q, k_pool, v_pool, block_tables, context_lens, k_scale, v_scale, out)
+    mctx = _max_ctx(block_tables, max_context_len)
+    lib = library()
+    need = lib.pkv_decode_workspace_bytes(ctypes.byref(desc), q.shape[0], mctx, 0)
+    workspace, wbytes = _workspace(need, q, workspace)
+    _check(lib.pkv_paged_decode(ctypes.byref(desc), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
+                                block_tables.shape[1], _ptr(context_lens), q.shape[0], mctx, float(scale),
+                                _ptr(out), _ptr(workspace), wbytes, _stream(stream)), "pkv_paged_decode")
+    return out
+
+
+def paged_decode_partitions(q, k_pool, v_pool, block_tables, context_lens, scale, partition: int,
+                            out, workspace, k_scale=None, v_scale=None, max_context_len=None,
+                            stream=None) -> None:
+    """First kernel of ``paged_decode`` with an explicit partition size."""
+    desc, out = _decode_checks(q, k_pool, v_pool, block_tables, context_lens, k_scale, v_scale, out)
+    mctx = _max_ctx(block_tables, max_context_len)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(library().pkv_paged_decode_partitions(
+        ctypes.byref(desc), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables), block_tables.shape[1],
+        _ptr(context_lens), q.shape[0], mctx, float(scale), int(partition), _ptr(out), _ptr(workspace),
+        wbytes, _stream(stream)), "pkv_paged_decode_partitions")
+
+
+def paged_decode_reduce(q, k_pool, v_pool, block_tables, context_lens, partition: int, out, workspace,
+                        k_scale=None, v_scale=None, max_context_len=None, stream=None) -> None:
+    """Second kernel of ``paged_decode``: merge the partition partials into ``out``."""
+    desc, out = _decode_checks(q, k_pool, v_pool, block_tables, context_lens, k_scale, v_scale, out)
+    mctx = _max_ctx(block_tables, max_context_len)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(library().pkv_paged_decode_reduce(
+        ctypes.byref(desc), block_tables.shape[1], _ptr(context_lens), q.shape[0], mctx, int(partition),
+        _ptr(out), _ptr(workspace), wbytes, _stream(stream)), "pkv_paged_decode_reduce")

@@ -1,0 +1,121 @@
+"""The C-ABI library loads, exports every declared entry point, and rejects
+bad arguments on the host before any HIP call (no GPU needed)."""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from paged_kv_cache_23_amd import ops
+from paged_kv_cache_23_amd.build import LIB_PATH
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pkv.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB_PATH), reason="libpkv.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pkv_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for required in ("pkv_kv_append", "pkv_paged_decode", "pkv_paged_decode_partitions",
+                     "pkv_paged_decode_reduce", "pkv_decode_workspace_bytes", "pkv_strerror"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (pkv_\w+)", out))
+    assert set(declared_functions()) <= exported
+
+
+def _desc(**kw):
+    d = dict(num_blocks=8, block_size=16, num_kv_heads=2, num_q_heads=8, head_dim=128,
+             kv_dtype=ops.BF16, q_dtype=ops.BF16, k_scale=None, v_scale=None)
+    d.update(kw)
+    return ops.CacheDesc(**d)
+
+
+EINVAL, EUNSUPPORTED, EWORKSPACE = -1, -2, -3
+FAKE = 0x10000  # a non-null, 16-byte aligned address that is never dereferenced
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(block_size=32), EINVAL),
+    (dict(num_blocks=0), EINVAL),
+    (dict(num_q_heads=7), EINVAL),
+    (dict(num_q_heads=64), EUNSUPPORTED),   # 32 query heads per kv head
+    (dict(head_dim=96), EUNSUPPORTED),
+    (dict(kv_dtype=ops.F32), EUNSUPPORTED),  # f32 cache with bf16 queries
+    (dict(kv_dtype=ops.FP8_E4M3), EINVAL),   # fp8 without scales
+    (dict(kv_dtype=7), EINVAL),
+    (dict(k_scale=FAKE), EINVAL),            # scales on a bf16 cache
+])
+def test_bad_descriptors_are_rejected(kw, code):
+    lib = ops.library()
+    d = _desc(**kw)
+    assert lib.pkv_kv_append(ctypes.byref(d), FAKE, FAKE, FAKE, 1, FAKE, FAKE, None) == code
+    assert lib.pkv_paged_decode(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 64, 0.1,
+                                FAKE, None, 0, None) == code
+
+
+def test_null_and_size_errors():
+    lib = ops.library()
+    d = _desc()
+    assert lib.pkv_kv_append(None, FAKE, FAKE, FAKE, 1, FAKE, FAKE, None) == EINVAL
+    assert lib.pkv_kv_append(ctypes.byref(d), None, FAKE, FAKE, 1, FAKE, FAKE, None) == EINVAL
+    assert lib.pkv_kv_append(ctypes.byref(d), FAKE, FAKE, FAKE, -1, FAKE, FAKE, None) == EINVAL
+    assert lib.pkv_kv_append(ctypes.byref(d), None, None, None, 0, None, None, None) == 0  # no-op
+    assert lib.pkv_paged_decode(ctypes.byref(d), None, FAKE, FAKE, FAKE, 4, FAKE, 2, 64, 0.1,
+                                FAKE, None, 0, None) == EINVAL
+    assert lib.pkv_paged_decode(ctypes.byref(d), FAKE + 8, FAKE, FAKE, FAKE, 4, FAKE, 2, 64, 0.1,
+                                FAKE, None, 0, None) == EINVAL          # misaligned q
+    assert lib.pkv_paged_decode_partitions(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 64, 0.1,
+                                           48, FAKE, None, 0, None) == EINVAL   # partition not /32
+    assert lib.pkv_paged_decode_partitions(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 64, 0.1,
+                                           4096, FAKE, None, 0, None) == EINVAL  # partition too long
+
+
+def test_workspace_sizing_and_check():
+    lib = ops.library()
+    d = _desc()
+    # one partition: no workspace
+    assert lib.pkv_decode_workspace_bytes(ctypes.byref(d), 4, 64, 512) == 0
+    # 3 partitions of 64 tokens over 4 seqs x 8 heads: acc (rounded to 256 B) + (max, sum)
+    rows = 4 * 8 * 3
+    acc = -(-rows * 128 * 4 // 256) * 256
+    need = lib.pkv_decode_workspace_bytes(ctypes.byref(d), 4, 150, 64)
+    assert need == acc + rows * 2 * 4
+    st = lib.pkv_paged_decode_partitions(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 16, FAKE, 4, 150, 0.1,
+                                         64, FAKE, FAKE, need - 1, None)
+    assert st == EWORKSPACE
+    st = lib.pkv_paged_decode_reduce(ctypes.byref(d), 16, FAKE, 4, 150, 64, FAKE, None, 0, None)
+    assert st == EWORKSPACE
+
+
+def test_default_partition_is_a_multiple_of_32_within_limits():
+    lib = ops.library()
+    for (B, Hkv, ctx) in [(64, 8, 4096), (8, 8, 131072), (256, 8, 8192), (1, 1, 10), (4, 2, 64)]:
+        d = _desc(num_kv_heads=Hkv, num_q_heads=4 * Hkv)
+        p = lib.pkv_partition_tokens(ctypes.byref(d), B, ctx)
+        assert p > 0 and p % 32 == 0 and p <= 2048
+
+
+def test_strerror_and_version():
+    lib = ops.library()
+    assert lib.pkv_strerror(0) == b"ok"
+    assert b"workspace" in lib.pkv_strerror(EWORKSPACE)
+    assert lib.pkv_strerror(12345) == b"unknown status"
+    assert b"gfx950" in lib.pkv_version()

@@ -1,0 +1,149 @@
+"""Invariants of the GPU decode that need no tolerance: bit-identity under
+block-id permutation, prefix sharing and identity-vs-shuffled tables (the
+arithmetic order depends on logical positions only), normalisation (V = 1
+gives exactly 1), poison in masked slots and unused table entries, and the
+two-kernel form equal to the fused call."""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from paged_kv_cache_23_amd import ops
+from paged_kv_cache_23_amd.workloads import build_workload
+from tests.gpu_util import Dev, max_err, oracle_full, out_f64, TOL
+
+pytestmark = pytest.mark.gpu
+
+LENS = [1, 17, 64, 100, 333, 1500, 4000]
+
+
+def _wl(kv_dtype, **kw):
+    D = 64 if kv_dtype == "f32" else 128
+    return build_workload("inv", LENS, 8, 2, D, kv_dtype, seed=77, **kw)
+
+
+def _bits(t: torch.Tensor) -> np.ndarray:
+    t = t.cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy()
+    return t.numpy().view(np.uint32)
+
+
+@pytest.mark.parametrize("kv_dtype", ["f32", "bf16", "fp8"])
+def test_block_permutation_bit_identity(kv_dtype):
+    wl = _wl(kv_dtype)
+    dev = Dev(wl)
+    base = dev.decode()
+    pi = torch.from_numpy(np.random.default_rng(1).permutation(wl.num_blocks)).to(dev.k_pool.device)
+    kp = torch.empty_like(dev.k_pool)
+    vp = torch.empty_like(dev.v_pool)
+    kp[pi] = dev.k_pool
+    vp[pi] = dev.v_pool
+    t = dev.tables.long()
+    t2 = torch.where(t >= 0, pi[t.clamp(min=0)], t).to(torch.int32)
+    got = dev.decode(k_pool=kp, v_pool=vp, tables=t2)
+    assert np.array_equal(_bits(got), _bits(base))
+
+
+def test_identity_tables_bit_identity():
+    """A slab expressed as a table (each sequence's blocks consecutive) gives
+    the same bits as the shuffled placement."""
+    wl = _wl("bf16")
+    dev = Dev(wl)
+    base = dev.decode()
+    # relocate every sequence's blocks into consecutive ids
+    t = wl.block_tables
+    order = [int(x) for row in t for x in row if x >= 0]
+    mapping = {old: new for new, old in enumerate(order)}
+    kp = torch.zeros_like(dev.k_pool)
+    vp = torch.zeros_like(dev.v_pool)
+    src = torch.tensor(order, device=kp.device)
+    kp[: len(order)] = dev.k_pool[src]
+    vp[: len(order)] = dev.v_pool[src]
+    t2 = torch.tensor([[mapping[int(x)] if x >= 0 else -1 for x in row] for row in t], dtype=torch.int32)
+    got = dev.decode(k_pool=kp, v_pool=vp, tables=t2.to(kp.device))
+    assert np.array_equal(_bits(got), _bits(base))
+
+
+def test_shared_prefix_equals_private_copies_bitwise():
+    wl = build_workload("share", [4096 + 5, 4096 + 77, 4096 + 300, 4096 + 16], 32, 8, 128, "bf16",
+                        seed=12, shared_prefix=4096)
+    dev = Dev(wl)
+    shared = dev.decode()
+    # give every sequence but the first a private copy of the 256 prefix blocks
+    t = wl.block_tables.clone()
+    NB = wl.num_blocks
+    extra = 3 * 256
+    kp = torch.cat([dev.k_pool, torch.empty((extra,) + tuple(dev.k_pool.shape[1:]), dtype=dev.k_pool.dtype,
+                                            device=dev.k_pool.device)])
+    vp = torch.cat([dev.v_pool, torch.empty((extra,) + tuple(dev.v_pool.shape[1:]), dtype=dev.v_pool.dtype,
+                                            device=dev.v_pool.device)])
+    nxt = NB
+    for b in range(1, 4):
+        for j in range(256):
+            kp[nxt] = dev.k_pool[int(t[b, j])]
+            vp[nxt] = dev.v_pool[int(t[b, j])]
+            t[b, j] = nxt
+            nxt += 1
+    private = dev.decode(k_pool=kp, v_pool=vp, tables=t.to(kp.device))
+    assert np.array_equal(_bits(private), _bits(shared))
+
+
+@pytest.mark.parametrize("kv_dtype", ["f32", "bf16", "fp8"])
+def test_unit_values_give_exactly_one(kv_dtype):
+    """V = 1 everywhere: every output is exactly 1 (the normalisation divides by
+    the same sum the weights were accumulated with)."""
+    wl = _wl(kv_dtype)
+    if kv_dtype == "fp8":
+        wl.v_pool.fill_(0x38)          # E4M3 code of 1.0
+        wl.v_scale = torch.ones_like(wl.v_scale)
+    else:
+        wl.v_pool.fill_(1.0)
+    got = out_f64(Dev(wl).decode())
+    if kv_dtype == "f32":   # float32 output: the two sums may round apart by an ulp or two
+        assert np.max(np.abs(got - 1.0)) <= 4 * 2.0 ** -24
+    else:                   # bf16 output: rounds to exactly 1
+        assert np.array_equal(got, np.ones_like(got))
+
+
+@pytest.mark.parametrize("kv_dtype", ["f32", "bf16", "fp8"])
+def test_poisoned_tails_and_stale_table_entries(kv_dtype):
+    """NaN in slots past each sequence's end and -1 / huge ids in unused table
+    entries change nothing."""
+    wl = _wl(kv_dtype)
+    dev = Dev(wl)
+    base = dev.decode()
+    kp, vp = dev.k_pool.clone(), dev.v_pool.clone()
+    nan = 0x7F if kv_dtype == "fp8" else float("nan")
+    for b, n in enumerate(LENS):
+        if n % 16:
+            last = int(wl.block_tables[b, (n - 1) // 16])
+            kp[last, :, n % 16:, :] = nan
+            vp[last, :, :, n % 16:] = nan
+    t = dev.tables.clone()
+    used = (torch.tensor(LENS) + 15) // 16
+    for b in range(len(LENS)):
+        t[b, int(used[b]):] = -1 if b % 2 else 2 ** 31 - 1
+    got = dev.decode(k_pool=kp, v_pool=vp, tables=t)
+    assert np.array_equal(_bits(got), _bits(base))
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+def test_two_kernel_form_equals_fused_call(kv_dtype):
+    wl = _wl(kv_dtype)
+    dev = Dev(wl)
+    fused = dev.decode()
+    part = ops.partition_tokens(dev.k_pool, dev.v_pool, 8, len(LENS), max(LENS), dev.k_scale, dev.v_scale)
+    split = dev.decode(partition=part)
+    assert np.array_equal(_bits(split), _bits(fused))
+    assert max_err(split, oracle_full(wl)) <= TOL[kv_dtype]
+
+
+def test_repeated_calls_are_deterministic():
+    wl = _wl("bf16")
+    dev = Dev(wl)
+    a = dev.decode()
+    b = dev.decode()
+    assert np.array_equal(_bits(a), _bits(b))
