@@ -28,8 +28,8 @@ library stores tiles so that one (block, kv-head) tile is contiguous):
 
 * K pool: ``[num_blocks, num_kv_heads, 16, head_dim]``  (token-major tile)
 * V pool: ``[num_blocks, num_kv_heads, head_dim, 16]``  (dim-major tile)
-* slot s (int64, >= 0) names block ``s // 16`` and offset ``s % 16``;
-  negative slots are padding and write nothing.
+* slot s (int64) names block ``s // 16`` and offset ``s % 16``; a slot
+  outside ``[0, num_blocks * 16)`` is padding and writes nothing.
 
 Storage dtypes are given by name: ``"f32"`` (float32 arrays), ``"bf16"``
 (uint16 arrays holding the bf16 bit patterns) and ``"fp8"`` (uint8 arrays
@@ -146,9 +146,10 @@ def oracle_append(k_pool, v_pool, k_new, v_new, slot_mapping, kv_dtype: str,
     slots = np.asarray(slot_mapping, dtype=np.int64)
     T = slots.shape[0]
     num_kv_heads = k_out.shape[1]
+    num_slots = k_out.shape[0] * BLOCK_SIZE
     for i in range(T):
         s = int(slots[i])
-        if s < 0:
+        if s < 0 or s >= num_slots:
             continue  # padding token: nothing to write
         blk, off = s // BLOCK_SIZE, s % BLOCK_SIZE
         for h in range(num_kv_heads):

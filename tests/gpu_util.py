@@ -97,6 +97,26 @@ def max_err(out: torch.Tensor, ref: np.ndarray) -> float:
     return float(np.max(np.abs(got - ref))) if ref.size else 0.0
 
 
+def half_ulp_bf16(ref: np.ndarray) -> np.ndarray:
+    """Half a bf16 ulp at |ref|: the most that rounding the output to bf16 adds."""
+    a = np.maximum(np.abs(ref), 2.0 ** -126)
+    return np.exp2(np.floor(np.log2(a)) - 8)
+
+
+def assert_close(out: torch.Tensor, ref: np.ndarray, kv_dtype: str) -> float:
+    """|got - ref| <= tolerance of the cache dtype, plus, for bf16 outputs, the
+    half ulp that the final rounding to bf16 adds at that magnitude."""
+    got = out_f64(out) if isinstance(out, torch.Tensor) else out
+    assert np.all(np.isfinite(got)), "non-finite output"
+    if ref.size == 0:
+        return 0.0
+    err = np.abs(got - ref)
+    bound = TOL[kv_dtype] + (0.0 if kv_dtype == "f32" else half_ulp_bf16(ref))
+    worst = np.unravel_index(np.argmax(err - bound), err.shape)
+    assert np.all(err <= bound), f"max|err| {err.max():.4g}; worst at {worst}: {err[worst]:.4g} > {np.broadcast_to(bound, err.shape)[worst]:.4g}"
+    return float(err.max())
+
+
 def pair_rows(out: torch.Tensor, pairs, G: int) -> np.ndarray:
     got = out_f64(out)
     return np.stack([got[b, g * G:(g + 1) * G] for b, g in pairs])

@@ -13,7 +13,7 @@ import torch
 import oracle
 from paged_kv_cache_23_amd import workloads as W
 from paged_kv_cache_23_amd.workloads import build_workload, storage_numpy
-from tests.gpu_util import TOL, Dev, max_err, oracle_full, oracle_pairs, out_f64, pair_rows
+from tests.gpu_util import Dev, assert_close, oracle_full, oracle_pairs, out_f64, pair_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -22,13 +22,13 @@ def test_tiny_fp32_before_and_after_append():
     wl = W.tiny_fp32()
     dev = Dev(wl)
     out = dev.decode()
-    assert max_err(out, oracle_full(wl)) <= TOL["f32"]
+    assert_close(out, oracle_full(wl), "f32")
     dev.append()
     out = dev.decode(after_append=True)
     ref_k, ref_v = oracle.oracle_append(storage_numpy(wl.k_pool), storage_numpy(wl.v_pool),
                                         storage_numpy(wl.k_new), storage_numpy(wl.v_new),
                                         wl.slot_mapping.numpy(), "f32")
-    assert max_err(out, oracle_full(wl, ref_k, ref_v, after_append=True)) <= TOL["f32"]
+    assert_close(out, oracle_full(wl, ref_k, ref_v, after_append=True), "f32")
 
 
 LENS = [1, 2, 15, 16, 17, 31, 32, 33, 95, 200, 513, 1000]
@@ -41,7 +41,7 @@ def test_small_shapes(kv_dtype, D, G):
     Hkv = 2
     wl = build_workload("small", LENS, Hkv * G, Hkv, D, kv_dtype, seed=100 + G + D)
     out = Dev(wl).decode()
-    assert max_err(out, oracle_full(wl)) <= TOL[kv_dtype]
+    assert_close(out, oracle_full(wl), kv_dtype)
 
 
 @pytest.mark.parametrize("partition", [32, 64, 96, 256, 2048])
@@ -51,7 +51,7 @@ def test_explicit_partitions(kv_dtype, partition):
     wl = build_workload("parts", [1, 33, 100, 257, 700, 2049], 16, 4, 128 if kv_dtype != "f32" else 64,
                         kv_dtype, seed=partition)
     out = Dev(wl).decode(partition=partition)
-    assert max_err(out, oracle_full(wl)) <= TOL[kv_dtype]
+    assert_close(out, oracle_full(wl), kv_dtype)
 
 
 def test_zero_length_and_single_token():
@@ -95,9 +95,8 @@ def c2():
 def test_llama8b_b64_all_outputs(c2):
     dev = Dev(c2)
     out = dev.decode()
-    err = max_err(out, oracle_full(c2))
+    err = assert_close(out, oracle_full(c2), "bf16")
     print(f"llama3-8b-b64 max|err| = {err:.3g}")
-    assert err <= TOL["bf16"]
 
 
 def test_llama70b_long_sampled_pairs():
@@ -105,9 +104,8 @@ def test_llama70b_long_sampled_pairs():
     out = Dev(wl).decode()
     pairs = [(0, 0), (3, 5), (5, 7), (7, 2)]
     ref = oracle_pairs(wl, pairs)
-    err = float(np.max(np.abs(pair_rows(out, pairs, 8) - ref)))
+    err = assert_close(pair_rows(out, pairs, 8), ref, "bf16")
     print(f"llama3-70b-long sampled max|err| = {err:.3g}")
-    assert err <= TOL["bf16"]
     assert np.all(np.isfinite(out_f64(out)))
 
 
@@ -117,14 +115,13 @@ def test_shared_prefix_256_sampled_pairs():
     rng = np.random.default_rng(0)
     pairs = [(int(b), int(g)) for b, g in zip(rng.integers(0, 256, 24), rng.integers(0, 8, 24))]
     ref = oracle_pairs(wl, pairs)
-    err = float(np.max(np.abs(pair_rows(out, pairs, 4) - ref)))
-    assert err <= TOL["bf16"]
+    assert_close(pair_rows(out, pairs, 4), ref, "bf16")
 
 
 def test_best_of_8_all_outputs():
     wl = W.best_of_8()
     out = Dev(wl).decode()
-    assert max_err(out, oracle_full(wl)) <= TOL["bf16"]
+    assert_close(out, oracle_full(wl), "bf16")
 
 
 def test_fp8_append_then_decode():
@@ -137,6 +134,5 @@ def test_fp8_append_then_decode():
                                         storage_numpy(wl.k_new), storage_numpy(wl.v_new),
                                         wl.slot_mapping.numpy(), "fp8", wl.k_scale.numpy(), wl.v_scale.numpy())
     ref = oracle_full(wl, ref_k, ref_v, after_append=True)
-    err = max_err(out, ref)
+    err = assert_close(out, ref, "fp8")
     print(f"fp8-b256 max|err| = {err:.3g}")
-    assert err <= TOL["fp8"]

@@ -12,7 +12,7 @@ import torch
 
 from paged_kv_cache_23_amd import ops
 from paged_kv_cache_23_amd.workloads import build_workload
-from tests.gpu_util import Dev, max_err, oracle_full, out_f64, TOL
+from tests.gpu_util import Dev, assert_close, oracle_full, out_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -138,7 +138,7 @@ def test_two_kernel_form_equals_fused_call(kv_dtype):
     part = ops.partition_tokens(dev.k_pool, dev.v_pool, 8, len(LENS), max(LENS), dev.k_scale, dev.v_scale)
     split = dev.decode(partition=part)
     assert np.array_equal(_bits(split), _bits(fused))
-    assert max_err(split, oracle_full(wl)) <= TOL[kv_dtype]
+    assert_close(split, oracle_full(wl), kv_dtype)
 
 
 def test_repeated_calls_are_deterministic():
