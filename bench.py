@@ -1,9 +1,9 @@
 #!/usr/bin/env python3
 """Paged decode benchmark on one MI355X.
 
-A step is one decode pass of one layer over the whole batch: the partition
-kernel plus the merge kernel (and, for workloads that append, the kv_append
-of one token per sequence first).  Inputs are seeded synthetic data already
+A step is one decode pass of one layer over the whole batch: one
+pkv_paged_decode call (its split kernel plus its merge kernel; for workloads
+that append, the kv_append of one token per sequence first).  Inputs are seeded synthetic data already
 resident in HBM; successive steps rotate over ``--layers`` distinct copies of
 the pool so that the bytes touched between reuses of one copy exceed the
 256 MB Infinity Cache.
@@ -55,7 +55,7 @@ def kernel_source_hash() -> str:
 def committed_traffic(workload: str):
     """HBM bytes per decode-kernel launch from the committed rocprofv3 counter
     summary, if it was taken on the current kernel source; else None."""
-    path = os.path.join(PROFILE_DIR, f"decode_partitions_{workload}_pmc.txt")
+    path = os.path.join(PROFILE_DIR, f"decode_split_{workload}_pmc.txt")
     if not os.path.exists(path):
         return None
     text = open(path).read()
@@ -69,7 +69,7 @@ def committed_traffic(workload: str):
 class Runner:
     """Pre-marshalled C-ABI calls for one workload on the current stream."""
 
-    def __init__(self, wl, layers: int, partition: int = 0, identity_tables: bool = False):
+    def __init__(self, wl, layers: int, workers: int = 0, identity_tables: bool = False):
         import torch
         from paged_kv_cache_23_amd import ops
 
@@ -111,8 +111,11 @@ class Runner:
         self.desc = ops.cache_desc(k0, v0, wl.num_q_heads, self.k_scale, self.v_scale)
         lib = ops.library()
         self.lib = lib
-        self.part = partition or lib.pkv_partition_tokens(ctypes.byref(self.desc), self.B, self.max_ctx)
-        nbytes = lib.pkv_decode_workspace_bytes(ctypes.byref(self.desc), self.B, self.max_ctx, self.part)
+        self.explicit_workers = bool(workers)
+        self.workers = workers or lib.pkv_decode_workers(ctypes.byref(self.desc), self.B, self.max_ctx)
+        if self.workers <= 0:
+            raise RuntimeError(f"pkv_decode_workers failed: {self.workers}")
+        nbytes = lib.pkv_decode_workspace_bytes(ctypes.byref(self.desc), self.B, self.max_ctx, self.workers)
         self.ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
         self.ws_bytes = self.ws.numel()
         self.kv_bytes = wl.kv_bytes(after_append=self.append)
@@ -132,27 +135,39 @@ class Runner:
         if st:
             raise RuntimeError(f"pkv_kv_append failed: {st}")
 
-    def partitions(self, layer: int, stream):
-        st = self.lib.pkv_paged_decode_partitions(
+    def decode(self, layer: int, stream):
+        """The fused call: split kernel then merge kernel."""
+        st = self.lib.pkv_paged_decode(
             ctypes.byref(self.desc), self.q.data_ptr(), self.k_pools[layer].data_ptr(),
             self.v_pools[layer].data_ptr(), self.tables.data_ptr(), self.tables.shape[1], self.lens.data_ptr(),
-            self.B, self.max_ctx, self.wl.scale, self.part, self.out.data_ptr(), self.ws.data_ptr(),
+            self.B, self.max_ctx, self.wl.scale, self.out.data_ptr(), self.ws.data_ptr(), self.ws_bytes, stream)
+        if st:
+            raise RuntimeError(f"pkv_paged_decode failed: {st}")
+
+    def split(self, layer: int, stream):
+        st = self.lib.pkv_paged_decode_split(
+            ctypes.byref(self.desc), self.q.data_ptr(), self.k_pools[layer].data_ptr(),
+            self.v_pools[layer].data_ptr(), self.tables.data_ptr(), self.tables.shape[1], self.lens.data_ptr(),
+            self.B, self.max_ctx, self.wl.scale, self.workers, self.out.data_ptr(), self.ws.data_ptr(),
             self.ws_bytes, stream)
         if st:
-            raise RuntimeError(f"pkv_paged_decode_partitions failed: {st}")
+            raise RuntimeError(f"pkv_paged_decode_split failed: {st}")
 
-    def reduce(self, stream):
-        st = self.lib.pkv_paged_decode_reduce(ctypes.byref(self.desc), self.tables.shape[1], self.lens.data_ptr(),
-                                              self.B, self.max_ctx, self.part, self.out.data_ptr(),
-                                              self.ws.data_ptr(), self.ws_bytes, stream)
+    def merge(self, stream):
+        st = self.lib.pkv_paged_decode_merge(ctypes.byref(self.desc), self.tables.shape[1], self.lens.data_ptr(),
+                                             self.B, self.max_ctx, self.workers, self.out.data_ptr(),
+                                             self.ws.data_ptr(), self.ws_bytes, stream)
         if st:
-            raise RuntimeError(f"pkv_paged_decode_reduce failed: {st}")
+            raise RuntimeError(f"pkv_paged_decode_merge failed: {st}")
 
     def step(self, layer: int, stream):
         if self.append:
             self.append_step(layer, stream)
-        self.partitions(layer, stream)
-        self.reduce(stream)
+        if self.explicit_workers:
+            self.split(layer, stream)
+            self.merge(stream)
+        else:
+            self.decode(layer, stream)
 
 
 def check_against_oracle(runner, sample_seqs: int = 4) -> float:
@@ -221,8 +236,8 @@ def run_bench(args) -> dict:
     wl = W.WORKLOADS[args.workload]()
     log(f"workload {wl.name}: B={wl.batch} Hq={wl.num_q_heads} Hkv={wl.num_kv_heads} D={wl.head_dim} "
         f"kv={wl.kv_dtype} blocks={wl.num_blocks} KV={wl.kv_bytes() / 1e6:.1f} MB")
-    runner = Runner(wl, args.layers, args.partition, args.identity_tables)
-    log(f"partition={runner.part} tokens, workspace={runner.ws_bytes} B, layers={args.layers}")
+    runner = Runner(wl, args.layers, args.workers, args.identity_tables)
+    log(f"workers={runner.workers} waves, workspace={runner.ws_bytes} B, layers={args.layers}")
     torch.cuda.synchronize()
 
     # one checked step on layer 0 (the output is compared with the oracle below)
@@ -237,30 +252,36 @@ def run_bench(args) -> dict:
         runner.step(i % L, s)
     torch.cuda.synchronize()
 
+    # timed region: K steps, events only at its two ends
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
-    t_wall0 = time.perf_counter()
     start_ev = torch.cuda.Event(enable_timing=True)
     end_ev = torch.cuda.Event(enable_timing=True)
+    t_wall0 = time.perf_counter()
     start_ev.record()
+    for i in range(K):
+        runner.step(i % L, s)
+    end_ev.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall0
+    total_ms = start_ev.elapsed_time(end_ev)
+    ms_per_step = total_ms / K
+
+    # per-kernel durations: the same steps with HIP events around each kernel
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
     for i in range(K):
         layer = i % L
         if runner.append:
             runner.append_step(layer, s)
         ev[i][0].record()
-        runner.partitions(layer, s)
+        runner.split(layer, s)
         ev[i][1].record()
-        runner.reduce(s)
+        runner.merge(s)
         ev[i][2].record()
-    end_ev.record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t_wall0
-    total_ms = start_ev.elapsed_time(end_ev)
     part_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
     red_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
-    ms_per_step = total_ms / K
-    log(f"{K} steps: {total_ms:.3f} ms on the stream, {wall * 1e3:.3f} ms wall; partition kernel "
-        f"mean {part_ms.mean() * 1e3:.1f} us (p10 {np.percentile(part_ms, 10) * 1e3:.1f}, "
+    log(f"{K} steps: {total_ms:.3f} ms on the stream, {wall * 1e3:.3f} ms wall ({ms_per_step * 1e3:.1f} us/step); "
+        f"split kernel mean {part_ms.mean() * 1e3:.1f} us (p10 {np.percentile(part_ms, 10) * 1e3:.1f}, "
         f"p90 {np.percentile(part_ms, 90) * 1e3:.1f}), merge kernel mean {red_ms.mean() * 1e3:.1f} us")
 
     step_bytes = runner.kv_bytes + runner.append_bytes
@@ -287,13 +308,13 @@ def run_bench(args) -> dict:
             "batch": wl.batch,
             "context_tokens": int((wl.context_lens_after if runner.append else wl.context_lens).sum()),
             "kv_bytes_per_step": step_bytes,
-            "partition_tokens": runner.part,
+            "worker_waves": runner.workers,
         },
         "hbm_peak_frac": round(gbs / HBM_PEAK_GBS, 4),
         "decode_tokens_per_s": round(wl.batch / (ms_per_step * 1e-3), 1),
         "max_abs_err_sampled": err,
         "roofline": {
-            "kernel": "decode_partitions_kernel",
+            "kernel": "decode_split_kernel",
             "bound": "hbm",
             "achieved": round(kern_gbs, 2),
             "peak": HBM_PEAK_GBS,
@@ -319,7 +340,7 @@ def profile_one(args) -> None:
     from paged_kv_cache_23_amd import workloads as W
 
     wl = W.WORKLOADS[args.workload]()
-    runner = Runner(wl, args.layers, args.partition)
+    runner = Runner(wl, args.layers, args.workers)
     s = runner.stream()
     for i in range(args.warmup):
         runner.step(i % args.layers, s)
@@ -327,7 +348,7 @@ def profile_one(args) -> None:
     for i in range(args.steps):
         runner.step(i % args.layers, s)
     torch.cuda.synchronize()
-    log(f"profiled {args.steps} steps of {wl.name} (partition {runner.part}, {runner.kv_bytes} KV bytes/step)")
+    log(f"profiled {args.steps} steps of {wl.name} ({runner.workers} workers, {runner.kv_bytes} KV bytes/step)")
 
 
 def copy_probe(args) -> None:
@@ -350,7 +371,7 @@ def main() -> int:
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="llama3-8b-b64")
     p.add_argument("--layers", type=int, default=4)
-    p.add_argument("--partition", type=int, default=0, help="partition tokens (0: the library's choice)")
+    p.add_argument("--workers", type=int, default=0, help="split-kernel worker waves (0: the library's choice)")
     p.add_argument("--identity-tables", action="store_true",
                    help="store each sequence's blocks consecutively (the slab layout as a table)")
     p.add_argument("--cpu-seconds", type=float, default=10.0)

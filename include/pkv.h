@@ -2,9 +2,10 @@
  * pkv.h - paged KV-cache decode attention on AMD MI355X (gfx950).
  *
  * Plain C ABI: device pointers, sizes and a HIP stream handle, nothing else.
- * The library allocates no memory, keeps no pointer after a call returns and
- * holds no mutable global state; every call is asynchronous on `stream`
- * (a hipStream_t passed as void*, NULL for the default stream).
+ * The library allocates no memory and keeps no pointer after a call returns;
+ * its only global state is a per-device cache of the compute-unit count.
+ * Every call is asynchronous on `stream` (a hipStream_t passed as void*,
+ * NULL for the default stream).
  *
  * The operation follows the source pages:
  *  - Habr KV-Cache article (habr.com/ru/articles/1021832), section 4
@@ -97,18 +98,20 @@ int pkv_kv_append(const pkv_cache_desc* desc, const void* k_new, const void* v_n
                   const int64_t* slot_mapping, int32_t num_tokens, void* k_pool,
                   void* v_pool, void* stream);
 
-/* Partition size (tokens, a multiple of 32) that pkv_paged_decode uses for
- * this batch shape: long contexts are split into partitions whose partial
- * softmax states are merged by a second kernel.  Returns a negative status
- * on bad arguments. */
-int32_t pkv_partition_tokens(const pkv_cache_desc* desc, int32_t num_seqs,
-                             int32_t max_context_len);
+/* Number of worker waves pkv_paged_decode's first kernel uses for this batch
+ * shape on the current device: one per SIMD slot the kernel's register budget
+ * allows (2 per SIMD, 8 per compute unit), fewer for batches with fewer
+ * 32-token chunks; always a multiple of 4.  Returns a negative status on bad
+ * arguments or when no device is current. */
+int32_t pkv_decode_workers(const pkv_cache_desc* desc, int32_t num_seqs,
+                           int32_t max_context_len);
 
-/* Device workspace bytes that a decode with this shape needs; 0 when no
- * sequence can span more than one partition.  partition_tokens == 0 means
- * pkv_partition_tokens(...).  Returns 0 on bad arguments. */
+/* Device workspace bytes a decode of this shape needs:
+ * (num_workers + num_seqs * num_kv_heads) partial states of group * (head_dim
+ * + 2) floats.  num_workers == 0 means pkv_decode_workers(...).  Returns 0 on
+ * bad arguments. */
 size_t pkv_decode_workspace_bytes(const pkv_cache_desc* desc, int32_t num_seqs,
-                                  int32_t max_context_len, int32_t partition_tokens);
+                                  int32_t max_context_len, int32_t num_workers);
 
 /* Decode attention for one query token per sequence over its paged cache:
  *   out[b][h] = softmax_t(scale * q[b][h] . K_b[t]) V_b[t],  t < context_lens[b]
@@ -119,8 +122,8 @@ size_t pkv_decode_workspace_bytes(const pkv_cache_desc* desc, int32_t num_seqs,
  * Lengths are taken as min(context_lens[b], max_context_len,
  * 16 * max_blocks_per_seq); block ids are clamped into [0, num_blocks).
  * Accumulation is float32; out is rounded once to q_dtype (nearest even).
- *   workspace  device buffer of pkv_decode_workspace_bytes(..., 0) bytes
- *              (may be NULL when that is 0); its contents are scratch. */
+ *   workspace  device buffer of pkv_decode_workspace_bytes(..., 0) bytes,
+ *              16-byte aligned; its contents are scratch. */
 int pkv_paged_decode(const pkv_cache_desc* desc, const void* q, const void* k_pool,
                      const void* v_pool, const int32_t* block_tables,
                      int32_t max_blocks_per_seq, const int32_t* context_lens,
@@ -128,25 +131,28 @@ int pkv_paged_decode(const pkv_cache_desc* desc, const void* q, const void* k_po
                      void* workspace, size_t workspace_bytes, void* stream);
 
 /* The two kernels of pkv_paged_decode as separate calls, with an explicit
- * partition size (a positive multiple of 32 up to 2048, or 0 for the default).
- * pkv_paged_decode_partitions writes the output of every sequence that fits
- * in one partition and a float32 partial state (running max, sum, unnormalised
- * accumulator) per partition of the others into the workspace;
- * pkv_paged_decode_reduce merges those partials into out (section 3's
- * rescale by exp(m_old - m_new), applied across partitions).  Calling them
- * in order on one stream equals pkv_paged_decode with that partition size. */
-int pkv_paged_decode_partitions(const pkv_cache_desc* desc, const void* q,
-                                const void* k_pool, const void* v_pool,
-                                const int32_t* block_tables, int32_t max_blocks_per_seq,
-                                const int32_t* context_lens, int32_t num_seqs,
-                                int32_t max_context_len, float scale,
-                                int32_t partition_tokens, void* out, void* workspace,
-                                size_t workspace_bytes, void* stream);
+ * worker count (a positive multiple of 4, or 0 for the default).
+ * pkv_paged_decode_split: the batch's 32-token chunks of every (sequence,
+ * kv head) pair, pairs in sequence-major order, are cut into num_workers equal
+ * contiguous ranges, one per wave; each wave runs the online softmax of
+ * section 3 over its range, writes the output of every pair it covers
+ * completely and a float32 partial state (running max, sum, unnormalised
+ * accumulator) for each pair it covers in part.
+ * pkv_paged_decode_merge combines the partials of every split pair (the same
+ * rescale by exp(m_old - m_new), applied across waves) and writes zeros for
+ * empty sequences.  Calling them in order on one stream with the same
+ * num_workers equals pkv_paged_decode with that count. */
+int pkv_paged_decode_split(const pkv_cache_desc* desc, const void* q, const void* k_pool,
+                           const void* v_pool, const int32_t* block_tables,
+                           int32_t max_blocks_per_seq, const int32_t* context_lens,
+                           int32_t num_seqs, int32_t max_context_len, float scale,
+                           int32_t num_workers, void* out, void* workspace,
+                           size_t workspace_bytes, void* stream);
 
-int pkv_paged_decode_reduce(const pkv_cache_desc* desc, int32_t max_blocks_per_seq,
-                            const int32_t* context_lens, int32_t num_seqs,
-                            int32_t max_context_len, int32_t partition_tokens, void* out,
-                            const void* workspace, size_t workspace_bytes, void* stream);
+int pkv_paged_decode_merge(const pkv_cache_desc* desc, int32_t max_blocks_per_seq,
+                           const int32_t* context_lens, int32_t num_seqs,
+                           int32_t max_context_len, int32_t num_workers, void* out,
+                           const void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static description of a status code. */
 const char* pkv_strerror(int status);

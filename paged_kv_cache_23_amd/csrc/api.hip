@@ -6,6 +6,8 @@
 
 #include <stdint.h>
 
+#include <atomic>
+
 namespace {
 
 using pkv::DecodeArgs;
@@ -35,35 +37,51 @@ int check_desc(const pkv_cache_desc* d) {
   return PKV_OK;
 }
 
-// Default partition size.  A workgroup streams one partition of one
-// (sequence, kv head); partitions must be long enough that each of its
-// four waves streams several 32-token chunks, and numerous enough that the
-// grid covers the 256 compute units several times over.
-int32_t default_partition(const pkv_cache_desc* d, int32_t num_seqs, int32_t max_ctx) {
-  const int64_t pairs = (int64_t)num_seqs * d->num_kv_heads;
-  int32_t part = 512;
-  // grow the partition while the grid would still hold >= 2048 workgroups
-  while (part < pkv::kMaxPartitionTokens && pairs * ((max_ctx + 2 * part - 1) / (2 * part)) >= 2048) part *= 2;
-  return part;
+// Compute units of the current device, cached per device (the value never
+// changes while the process runs).
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  if (dev >= 0 && dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    return -1;
+  if (dev >= 0 && dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
+  return cus;
 }
 
-int32_t resolve_partition(const pkv_cache_desc* d, int32_t num_seqs, int32_t max_ctx, int32_t part) {
-  if (part == 0) return default_partition(d, num_seqs, max_ctx);
-  if (part < 0 || part % pkv::kChunkTokens != 0 || part > pkv::kMaxPartitionTokens) return -1;
-  return part;
+// Default number of split-kernel worker waves: every SIMD slot the register
+// budget allows (2 waves per SIMD, 4 SIMDs per compute unit), all resident at
+// once; no more than there can be 32-token chunks in the batch.
+int32_t default_workers(const pkv_cache_desc* d, int32_t num_seqs, int32_t max_ctx) {
+  const int cus = device_cus();
+  if (cus <= 0) return PKV_ELAUNCH;
+  const int64_t full = (int64_t)cus * 4 * pkv::kWavesPerSimd;
+  const int64_t chunks = (int64_t)num_seqs * d->num_kv_heads *
+                         (((int64_t)max_ctx + pkv::kChunkTokens - 1) / pkv::kChunkTokens);
+  int64_t w = chunks < full ? chunks : full;
+  w = (w + pkv::kDecodeWaves - 1) / pkv::kDecodeWaves * pkv::kDecodeWaves;
+  return (int32_t)(w < pkv::kDecodeWaves ? pkv::kDecodeWaves : w);
 }
 
-int32_t num_partitions(int32_t max_ctx, int32_t part) {
-  if (max_ctx <= 0) return 1;
-  return (int32_t)(((int64_t)max_ctx + part - 1) / part);
+int32_t resolve_workers(const pkv_cache_desc* d, int32_t num_seqs, int32_t max_ctx, int32_t workers) {
+  if (workers == 0) return default_workers(d, num_seqs, max_ctx);
+  if (workers < 0 || workers % pkv::kDecodeWaves != 0 || workers > (1 << 24)) return PKV_EINVAL;
+  return workers;
 }
 
-size_t workspace_bytes(const pkv_cache_desc* d, int32_t num_seqs, int32_t max_ctx, int32_t part) {
-  const int32_t P = num_partitions(max_ctx, part);
-  if (P <= 1) return 0;
-  const size_t rows = (size_t)num_seqs * d->num_q_heads * P;
-  const size_t acc = (rows * d->head_dim * sizeof(float) + kWsAlign - 1) / kWsAlign * kWsAlign;
-  return acc + rows * 2 * sizeof(float);
+size_t acc_bytes(const pkv_cache_desc* d, int32_t num_seqs, int32_t workers) {
+  const size_t rows = ((size_t)workers + (size_t)num_seqs * d->num_kv_heads) * (d->num_q_heads / d->num_kv_heads);
+  return (rows * d->head_dim * sizeof(float) + kWsAlign - 1) / kWsAlign * kWsAlign;
+}
+
+size_t workspace_bytes(const pkv_cache_desc* d, int32_t num_seqs, int32_t workers) {
+  const size_t rows = ((size_t)workers + (size_t)num_seqs * d->num_kv_heads) * (d->num_q_heads / d->num_kv_heads);
+  return acc_bytes(d, num_seqs, workers) + rows * 2 * sizeof(float);
 }
 
 int check_decode_args(const pkv_cache_desc* d, const void* q, const void* k_pool, const void* v_pool,
@@ -79,7 +97,7 @@ int check_decode_args(const pkv_cache_desc* d, const void* q, const void* k_pool
 
 DecodeArgs make_args(const pkv_cache_desc* d, const void* q, const void* k_pool, const void* v_pool,
                      const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens,
-                     int32_t num_seqs, int32_t max_ctx, float scale, int32_t part, void* out,
+                     int32_t num_seqs, int32_t max_ctx, float scale, int32_t workers, void* out,
                      void* workspace) {
   DecodeArgs a{};
   a.q = q;
@@ -98,16 +116,11 @@ DecodeArgs make_args(const pkv_cache_desc* d, const void* q, const void* k_pool,
   a.max_blocks = max_blocks;
   a.num_blocks = d->num_blocks;
   a.max_context_len = max_ctx;
-  a.part_tokens = part;
-  a.num_parts = num_partitions(max_ctx, part);
+  a.num_workers = workers;
   a.kv_dtype = d->kv_dtype;
   a.scale = scale;
-  if (a.num_parts > 1) {
-    const size_t rows = (size_t)num_seqs * d->num_q_heads * a.num_parts;
-    const size_t acc = (rows * d->head_dim * sizeof(float) + kWsAlign - 1) / kWsAlign * kWsAlign;
-    a.ws_acc = static_cast<float*>(workspace);
-    a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + acc);
-  }
+  a.ws_acc = static_cast<float*>(workspace);
+  a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + acc_bytes(d, num_seqs, workers));
   return a;
 }
 
@@ -141,69 +154,66 @@ int pkv_kv_append(const pkv_cache_desc* desc, const void* k_new, const void* v_n
   return launch_status(pkv::launch_append(a, static_cast<hipStream_t>(stream)));
 }
 
-int32_t pkv_partition_tokens(const pkv_cache_desc* desc, int32_t num_seqs, int32_t max_context_len) {
+int32_t pkv_decode_workers(const pkv_cache_desc* desc, int32_t num_seqs, int32_t max_context_len) {
   int st = check_desc(desc);
   if (st != PKV_OK) return st;
   if (num_seqs < 0 || max_context_len < 0) return PKV_EINVAL;
-  return default_partition(desc, num_seqs, max_context_len);
+  return default_workers(desc, num_seqs, max_context_len);
 }
 
 size_t pkv_decode_workspace_bytes(const pkv_cache_desc* desc, int32_t num_seqs, int32_t max_context_len,
-                                  int32_t partition_tokens) {
+                                  int32_t num_workers) {
   if (check_desc(desc) != PKV_OK || num_seqs < 0 || max_context_len < 0) return 0;
-  const int32_t part = resolve_partition(desc, num_seqs, max_context_len, partition_tokens);
-  if (part <= 0) return 0;
-  return workspace_bytes(desc, num_seqs, max_context_len, part);
+  const int32_t w = resolve_workers(desc, num_seqs, max_context_len, num_workers);
+  if (w <= 0) return 0;
+  return workspace_bytes(desc, num_seqs, w);
 }
 
-int pkv_paged_decode_partitions(const pkv_cache_desc* desc, const void* q, const void* k_pool,
-                                const void* v_pool, const int32_t* block_tables,
-                                int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
-                                int32_t max_context_len, float scale, int32_t partition_tokens, void* out,
-                                void* workspace, size_t ws_bytes, void* stream) {
+int pkv_paged_decode_split(const pkv_cache_desc* desc, const void* q, const void* k_pool, const void* v_pool,
+                           const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                           int32_t num_seqs, int32_t max_context_len, float scale, int32_t num_workers, void* out,
+                           void* workspace, size_t ws_bytes, void* stream) {
   int st = check_decode_args(desc, q, k_pool, v_pool, block_tables, max_blocks_per_seq, context_lens,
                              num_seqs, max_context_len, out);
   if (st != PKV_OK) return st;
-  const int32_t part = resolve_partition(desc, num_seqs, max_context_len, partition_tokens);
-  if (part <= 0) return PKV_EINVAL;
-  const size_t need = workspace_bytes(desc, num_seqs, max_context_len, part);
-  if (need && (!workspace || ws_bytes < need)) return PKV_EWORKSPACE;
-  if (need && !aligned16(workspace)) return PKV_EINVAL;
+  const int32_t w = resolve_workers(desc, num_seqs, max_context_len, num_workers);
+  if (w <= 0) return w == 0 ? PKV_EINVAL : w;
   if (num_seqs == 0) return PKV_OK;
+  if (!workspace || ws_bytes < workspace_bytes(desc, num_seqs, w)) return PKV_EWORKSPACE;
+  if (!aligned16(workspace)) return PKV_EINVAL;
   DecodeArgs a = make_args(desc, q, k_pool, v_pool, block_tables, max_blocks_per_seq, context_lens, num_seqs,
-                           max_context_len, scale, part, out, workspace);
-  return launch_status(pkv::launch_decode_partitions(a, static_cast<hipStream_t>(stream)));
+                           max_context_len, scale, w, out, workspace);
+  return launch_status(pkv::launch_decode_split(a, static_cast<hipStream_t>(stream)));
 }
 
-int pkv_paged_decode_reduce(const pkv_cache_desc* desc, int32_t max_blocks_per_seq,
-                            const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
-                            int32_t partition_tokens, void* out, const void* workspace, size_t ws_bytes,
-                            void* stream) {
+int pkv_paged_decode_merge(const pkv_cache_desc* desc, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                           int32_t num_seqs, int32_t max_context_len, int32_t num_workers, void* out,
+                           const void* workspace, size_t ws_bytes, void* stream) {
   int st = check_desc(desc);
   if (st != PKV_OK) return st;
   if (!context_lens || !out || num_seqs < 0 || max_context_len < 0 || max_blocks_per_seq <= 0)
     return PKV_EINVAL;
   if (!aligned16(out)) return PKV_EINVAL;
-  const int32_t part = resolve_partition(desc, num_seqs, max_context_len, partition_tokens);
-  if (part <= 0) return PKV_EINVAL;
-  const size_t need = workspace_bytes(desc, num_seqs, max_context_len, part);
-  if (need == 0 || num_seqs == 0) return PKV_OK;   // nothing spans two partitions
-  if (!workspace || ws_bytes < need) return PKV_EWORKSPACE;
+  const int32_t w = resolve_workers(desc, num_seqs, max_context_len, num_workers);
+  if (w <= 0) return w == 0 ? PKV_EINVAL : w;
+  if (num_seqs == 0) return PKV_OK;
+  if (!workspace || ws_bytes < workspace_bytes(desc, num_seqs, w)) return PKV_EWORKSPACE;
+  if (!aligned16(workspace)) return PKV_EINVAL;
   // the merge reads lengths and partials only; q, pools and tables are unused
   DecodeArgs a = make_args(desc, out, out, out, context_lens, max_blocks_per_seq, context_lens, num_seqs,
-                           max_context_len, 1.f, part, out, const_cast<void*>(workspace));
-  return launch_status(pkv::launch_decode_reduce(a, static_cast<hipStream_t>(stream)));
+                           max_context_len, 1.f, w, out, const_cast<void*>(workspace));
+  return launch_status(pkv::launch_decode_merge(a, static_cast<hipStream_t>(stream)));
 }
 
 int pkv_paged_decode(const pkv_cache_desc* desc, const void* q, const void* k_pool, const void* v_pool,
                      const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
                      int32_t num_seqs, int32_t max_context_len, float scale, void* out, void* workspace,
                      size_t ws_bytes, void* stream) {
-  int st = pkv_paged_decode_partitions(desc, q, k_pool, v_pool, block_tables, max_blocks_per_seq, context_lens,
-                                       num_seqs, max_context_len, scale, 0, out, workspace, ws_bytes, stream);
+  int st = pkv_paged_decode_split(desc, q, k_pool, v_pool, block_tables, max_blocks_per_seq, context_lens,
+                                  num_seqs, max_context_len, scale, 0, out, workspace, ws_bytes, stream);
   if (st != PKV_OK) return st;
-  return pkv_paged_decode_reduce(desc, max_blocks_per_seq, context_lens, num_seqs, max_context_len, 0, out,
-                                 workspace, ws_bytes, stream);
+  return pkv_paged_decode_merge(desc, max_blocks_per_seq, context_lens, num_seqs, max_context_len, 0, out,
+                                workspace, ws_bytes, stream);
 }
 
 const char* pkv_strerror(int status) {

@@ -1,4 +1,4 @@
-// Paged decode attention for gfx950: partition kernel + merge kernel.
+// Paged decode attention for gfx950: split kernel + merge kernel.
 //
 // What is computed (Habr KV-Cache article, habr.com/ru/articles/1021832):
 //  - section 3 "Recalling FlashAttention": exact softmax(q K^T * scale) V,
@@ -12,13 +12,14 @@
 // "Chapter 8 - Next-generation KV cache" (LLM Primer VI), section 8.1: the
 // kernel reads keys and values by indirect addressing through the table.
 //
-// Work decomposition.  One workgroup of four waves handles one (sequence,
-// kv head, context partition) and the whole query group of that kv head.
-// Each wave walks the partition in 32-token chunks (two blocks), chunk c
-// going to wave c % 4, and keeps its own running max / sum / accumulator;
-// the four states are merged through LDS at the end.  A sequence that fits
-// in one partition is finished here; longer ones leave one float32 partial
-// state per partition for decode_reduce_kernel.
+// Work decomposition.  The batch is a list of 32-token chunks (two blocks)
+// of every (sequence, kv head) pair.  One worker wave per SIMD slot of the
+// GPU takes an equal contiguous range of that list (stream-K style), so all
+// waves stream the same bytes and none waits on another; it keeps a running
+// max / sum / accumulator per pair segment for the pair's whole query group.
+// A pair that one wave covers completely is finished by that wave; a pair
+// split between waves leaves one float32 partial per wave for
+// decode_merge_kernel.
 //
 // Tile math (CDNA4 MFMA, 64-lane waves).  Scores are computed transposed,
 // S^T[token][head] = K q^T, so that the MFMA output layout (lane l holds rows
@@ -334,85 +335,166 @@ __device__ __forceinline__ int clamp_len(int n, const DecodeArgs& a) {
   return max(n, 0);
 }
 
+// Chunks of one sequence: 32-token steps covering its n tokens.
+__device__ __forceinline__ int chunks_of(int n) { return (n + kChunkTokens - 1) / kChunkTokens; }
+
+// A value every lane holds: keep it in a scalar register.
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) v += __shfl_xor(v, s);
+  return v;
+}
+
+__device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
+#pragma unroll
+  for (int s = 1; s < 64; s <<= 1) {
+    const int t = __shfl_up(v, s);
+    if (lane >= s) v += t;
+  }
+  return v;
+}
+
+// Position of a chunk in the global order: pairs (b, g) sequence-major, chunk
+// c of the pair's cb chunks.  All fields are wave-uniform.
+struct Pos {
+  int b, g, c, cb, n;
+};
+
 // ---------------------------------------------------------------------------
-// Partition kernel
+// Split kernel.
+//
+// The batch's work is the list of 32-token chunks of every (sequence, kv head)
+// pair, pairs ordered sequence-major.  Worker wave w (one per SIMD slot of the
+// GPU, all resident at once) takes the contiguous chunk range
+// [w*K, (w+1)*K), K = ceil(chunks / workers), so every wave streams the same
+// number of bytes.  It walks its range pair by pair with one online-softmax
+// state; a pair that lies wholly inside the range is finished here, the
+// others leave a float32 partial (max, sum, unnormalised accumulator) in slot
+// w + pair of the workspace for the merge kernel.  Slot w + pair is unique:
+// ranges are contiguous and ordered, so a later wave never covers an earlier
+// pair.
 // ---------------------------------------------------------------------------
 template <int KV, int D>
-__device__ __forceinline__ void decode_partitions_body(const DecodeArgs& a) {
+__device__ __forceinline__ void decode_split_body(const DecodeArgs& a, const int32_t* __restrict__ tables,
+                                                  const int32_t* __restrict__ lens,
+                                                  const float* __restrict__ k_scale,
+                                                  const float* __restrict__ v_scale) {
   using T = typename TileOf<KV, D>::type;
   using OutT = typename TileOf<KV, D>::Out;
   using Elem = typename T::Elem;
   constexpr int kTiles = D / 16;
-
-  __shared__ float s_ml[kDecodeWaves][kMaxGroup][2];
-  __shared__ f32x4 s_acc[kDecodeWaves][kMaxGroup][D / 4];
+  constexpr size_t kQBytes = (KV == kF32) ? 4 : 2;
 
   const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15;
   const int j = lane >> 4;
-
-  const int P = a.num_parts;
-  int item = blockIdx.x;
-  const int p = item % P;
-  item /= P;
-  const int g = item % a.num_kv_heads;
-  const int b = item / a.num_kv_heads;
+  const int wid = __builtin_amdgcn_readfirstlane(blockIdx.x * kDecodeWaves + (threadIdx.x >> 6));
+  const int W = a.num_workers;
+  const int B = a.num_seqs;
+  const int Hkv = a.num_kv_heads;
   const int G = a.group;
   const int Hq = a.num_q_heads;
 
-  const int n = clamp_len(a.context_lens[b], a);
-  OutT* out = static_cast<OutT*>(a.out);
-  if (n == 0) {
-    if (p == 0)
-      for (int e = threadIdx.x; e < G * D; e += 64 * kDecodeWaves)
-        out[((size_t)b * Hq + g * G) * D + e] = (OutT)0.f;
-    return;
+  auto seq_len = [&](int b) -> int { return uni(clamp_len(lens[uni(b)], a)); };
+
+  // ---- this wave's chunk range -------------------------------------------
+  int64_t total = 0;   // chunks per kv head over the batch
+  for (int base = 0; base < B; base += 64) {
+    const int bi = base + lane;
+    total += uni(wave_sum(bi < B ? chunks_of(clamp_len(lens[bi], a)) : 0));
   }
-  const int start = p * a.part_tokens;
-  if (start >= n) return;
-  const int end = min(start + a.part_tokens, n);
-  const int nchunks = (end - start + kChunkTokens - 1) / kChunkTokens;
-  const int nblk = (n + kBlockTokens - 1) / kBlockTokens;
-  const bool single = n <= a.part_tokens;
+  const int64_t C = total * Hkv;
+  const int64_t K = (C + W - 1) / W;
+  const int64_t x0 = (int64_t)wid * K;
+  if (x0 >= C) return;
+  const int64_t x1 = min(x0 + K, C);
+  const int nch = (int)(x1 - x0);
 
-  // Softmax runs in log2 units: t = score * scale * log2(e).
-  float sl = a.scale * kLog2e;
-  float out_mul = 1.f;
-  if constexpr (KV == kFP8) {
-    sl *= a.k_scale[g];
-    out_mul = a.v_scale[g];
+  // the sequence holding chunk x0: Hkv*before(b) <= x0 < Hkv*(before(b) + cb)
+  int b0 = 0;
+  int64_t before0 = 0;
+  {
+    int64_t run = 0;
+    for (int base = 0; base < B; base += 64) {
+      const int bi = base + lane;
+      const int cb = bi < B ? chunks_of(clamp_len(lens[bi], a)) : 0;
+      const int incl = wave_inclusive_scan(cb, lane);
+      const int64_t ex = run + incl - cb;
+      const bool hit = cb > 0 && (int64_t)Hkv * ex <= x0 && x0 < (int64_t)Hkv * (ex + cb);
+      const uint64_t mask = __builtin_amdgcn_ballot_w64(hit);
+      if (mask) {
+        const int idx = uni(__builtin_ctzll(mask));
+        b0 = uni(base + idx);
+        before0 = run + uni(__builtin_amdgcn_readlane(incl - cb, idx));
+        break;
+      }
+      run += uni(__builtin_amdgcn_readlane(incl, 63));
+    }
   }
-
-  // Query operand: lane (r, j) holds head g*G + r (zero for padding columns r >= G).
-  constexpr size_t kQBytes = (KV == kF32) ? 4 : 2;
-  const uint8_t* q_row =
-      static_cast<const uint8_t*>(a.q) + ((size_t)b * Hq + g * G + min(r, G - 1)) * D * kQBytes;
-  typename T::Q qop;
-  T::load_q(qop, q_row, r < G, j);
-
-  const size_t blk_stride = (size_t)a.num_kv_heads * kBlockTokens * D;   // elements per block
-  const Elem* kpool = static_cast<const Elem*>(a.k_pool) + (size_t)g * kBlockTokens * D;
-  const Elem* vpool = static_cast<const Elem*>(a.v_pool) + (size_t)g * kBlockTokens * D;
-
-  // Block ids of this partition, one per lane: lane i of id_lo / id_hi holds
-  // partition-relative logical block i / 64 + i.  Entries past the
-  // sequence's last block are never read (the last valid id repeats).
-  const int32_t* table = a.block_tables + (size_t)b * a.max_blocks;
-  const int first_blk = start / kBlockTokens;
-  const int last_blk = nblk - 1;
-  const int id_lo = table[min(first_blk + lane, last_blk)];
-  const int id_hi = a.part_tokens > 64 * kBlockTokens ? table[min(first_blk + 64 + lane, last_blk)] : 0;
-  auto block_off = [&](int rel) -> size_t {   // rel: wave-uniform relative block
-    int id = rel < 64 ? __builtin_amdgcn_readlane(id_lo, rel) : __builtin_amdgcn_readlane(id_hi, rel - 64);
-    id = min(max(id, 0), a.num_blocks - 1);
-    return (size_t)id * blk_stride;
+  Pos pos;
+  pos.b = b0;
+  pos.n = seq_len(b0);
+  pos.cb = chunks_of(pos.n);
+  {
+    const int off = uni((int)(x0 - (int64_t)Hkv * before0));
+    pos.g = uni(off / pos.cb);
+    pos.c = uni(off - pos.g * pos.cb);
+  }
+  auto advance = [&](Pos q) -> Pos {
+    if (++q.c == q.cb) {
+      q.c = 0;
+      if (++q.g == Hkv) {
+        q.g = 0;
+        do {   // skip empty sequences; a next chunk exists, so this ends
+          ++q.b;
+          q.n = seq_len(q.b);
+          q.cb = chunks_of(q.n);
+        } while (q.cb == 0);
+      }
+    }
+    return q;
   };
-  auto issue = [&](typename T::K& kb, typename T::V& vb, int c) {
-    const size_t o0 = block_off(2 * c);
-    const size_t o1 = block_off(2 * c + 1);
-    T::load_k(kb, kpool + ((r >> 3) ? o1 : o0), r, j);
-    T::load_v(vb, vpool + ((j >> 1) ? o1 : o0), r, j);
+
+  const size_t blk_stride = (size_t)Hkv * kBlockTokens * D;   // elements per block
+  auto block_ids = [&](const Pos& q, int& id0, int& id1) {   // scalar loads
+    const int32_t* table = tables + (size_t)q.b * a.max_blocks;
+    const int last = (q.n + kBlockTokens - 1) / kBlockTokens - 1;
+    id0 = uni(min(max(table[uni(min(2 * q.c, last))], 0), a.num_blocks - 1));
+    id1 = uni(min(max(table[uni(min(2 * q.c + 1, last))], 0), a.num_blocks - 1));
+  };
+
+  // Query operand (and fp8 scales) of a pair.  Lane (r, j) holds head g*G + r;
+  // padding columns r >= G hold zeros.  The chunk that opens a pair loads the
+  // pair's query into its own buffer's slot (qA / qB) together with its K/V;
+  // the operand qop takes it over when that chunk is computed.  One slot per
+  // buffer keeps the load counters exact: a prefetch never writes a register
+  // the current chunk reads.
+  typename T::Q qop, qA, qB;
+  auto load_q = [&](typename T::Q& qq, const Pos& q) {
+    const uint8_t* row = static_cast<const uint8_t*>(a.q) +
+                         ((size_t)q.b * Hq + q.g * G + min(r, G - 1)) * D * kQBytes;
+    T::load_q(qq, row, r < G, j);
+  };
+  auto log2_scale = [&](int g) -> float {
+    float sl = a.scale * kLog2e;
+    if constexpr (KV == kFP8) sl *= k_scale[g];
+    return sl;
+  };
+  auto out_scale = [&](int g) -> float {
+    if constexpr (KV == kFP8) return v_scale[g];
+    return 1.f;
+  };
+
+  auto issue = [&](typename T::K& kb, typename T::V& vb, typename T::Q& qn, const Pos& q) {
+    int id0, id1;
+    block_ids(q, id0, id1);
+    const Elem* kp = static_cast<const Elem*>(a.k_pool) + (size_t)q.g * kBlockTokens * D;
+    const Elem* vp = static_cast<const Elem*>(a.v_pool) + (size_t)q.g * kBlockTokens * D;
+    T::load_k(kb, kp + (size_t)((r >> 3) ? id1 : id0) * blk_stride, r, j);
+    T::load_v(vb, vp + (size_t)((j >> 1) ? id1 : id0) * blk_stride, r, j);
+    if (q.c == 0) load_q(qn, q);   // first chunk of a pair: its query rides along
   };
 
   f32x4 acc[kTiles];
@@ -420,15 +502,53 @@ __device__ __forceinline__ void decode_partitions_body(const DecodeArgs& a) {
   for (int t = 0; t < kTiles; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY;
   float l_run = 0.f;
+  float sl = log2_scale(pos.g);
+  int seg_c0 = pos.c;      // first chunk of the current segment
+  OutT* out = static_cast<OutT*>(a.out);
 
-  auto compute = [&](typename T::K& kb, typename T::V& vb, int c) {
-    const int t0 = start + c * kChunkTokens;
+  auto flush = [&](const Pos& q) {
+    const float l_tot = row_sum4(l_run);
+    const float mul = out_scale(q.g);
+    const bool complete = seg_c0 == 0 && q.c == q.cb - 1;
+    if (complete) {
+      if (r < G) {
+        OutT* dst = out + ((size_t)q.b * Hq + q.g * G + r) * D + 4 * j;
+        const float f = mul / l_tot;
+#pragma unroll
+        for (int t = 0; t < kTiles; ++t) store4<OutT>(dst + 16 * t, acc[t] * f);
+      }
+    } else {
+      const size_t slot = (size_t)wid + (size_t)q.b * Hkv + q.g;
+      if (r < G) {
+        float* dst = a.ws_acc + (slot * G + r) * D + 4 * j;
+#pragma unroll
+        for (int t = 0; t < kTiles; ++t) *reinterpret_cast<f32x4*>(dst + 16 * t) = acc[t] * mul;
+        if (j == 0) {
+          a.ws_ml[(slot * G + r) * 2] = m_run;
+          a.ws_ml[(slot * G + r) * 2 + 1] = l_tot;
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < kTiles; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_run = -INFINITY;
+    l_run = 0.f;
+    seg_c0 = 0;
+  };
+
+  auto compute = [&](typename T::K& kb, typename T::V& vb, const typename T::Q& qn, const Pos& q,
+                     bool last_of_range) {
+    if (q.c == 0) {   // a new pair begins: switch query and scales
+      qop = qn;
+      sl = log2_scale(q.g);
+    }
+    const int t0 = q.c * kChunkTokens;
     f32x4 sx, sy;
     T::scores(kb, qop, sx, sy);
     float t[8] = {sx[0] * sl, sx[1] * sl, sx[2] * sl, sx[3] * sl,
                   sy[0] * sl, sy[1] * sl, sy[2] * sl, sy[3] * sl};
-    if (t0 + kChunkTokens > end) {   // tail chunk: mask tokens at or past the end
-      const int nvalid = min(max(end - (t0 + 8 * j), 0), 8);
+    if (t0 + kChunkTokens > q.n) {   // tail chunk: mask tokens at or past the end
+      const int nvalid = min(max(q.n - (t0 + 8 * j), 0), 8);
 #pragma unroll
       for (int k = 0; k < 8; ++k)
         if (k >= nvalid) t[k] = -INFINITY;
@@ -441,7 +561,7 @@ __device__ __forceinline__ void decode_partitions_body(const DecodeArgs& a) {
     if (__builtin_amdgcn_ballot_w64(m_new != m_run)) {
       const float corr = exp2_fast(m_run - m_new);
 #pragma unroll
-      for (int q = 0; q < kTiles; ++q) acc[q] *= corr;
+      for (int u = 0; u < kTiles; ++u) acc[u] *= corr;
       l_run *= corr;
     }
     m_run = m_new;
@@ -449,146 +569,156 @@ __device__ __forceinline__ void decode_partitions_body(const DecodeArgs& a) {
 #pragma unroll
     for (int k = 0; k < 8; ++k) pk[k] = exp2_fast(t[k] - m_new);
     l_run += T::pv(acc, vb, pk);
+    if (q.c == q.cb - 1 || last_of_range) flush(q);
   };
 
   // Two register buffers: chunk k+1's loads are in flight while chunk k is
   // computed.  The steady-state loop issues its prefetch unconditionally so
   // that the compiler's load counters wait only for the buffer in use.
-  const int my_chunks = wave < nchunks ? (nchunks - 1 - wave) / kDecodeWaves + 1 : 0;
+  load_q(qop, pos);
   typename T::K kA, kB;
   typename T::V vA, vB;
-  if (my_chunks > 0) {
-    issue(kA, vA, wave);
-    int k = 0;
-    for (; k + 2 < my_chunks; k += 2) {
-      issue(kB, vB, wave + (k + 1) * kDecodeWaves);
-      compute(kA, vA, wave + k * kDecodeWaves);
-      issue(kA, vA, wave + (k + 2) * kDecodeWaves);
-      compute(kB, vB, wave + (k + 1) * kDecodeWaves);
-    }
-    if (k + 1 < my_chunks) {
-      issue(kB, vB, wave + (k + 1) * kDecodeWaves);
-      compute(kA, vA, wave + k * kDecodeWaves);
-      compute(kB, vB, wave + (k + 1) * kDecodeWaves);
-    } else {
-      compute(kA, vA, wave + k * kDecodeWaves);
-    }
+  Pos pa = pos, pb;
+  issue(kA, vA, qA, pa);
+  int k = 0;
+  for (; k + 2 < nch; k += 2) {
+    pb = advance(pa);
+    issue(kB, vB, qB, pb);
+    compute(kA, vA, qA, pa, false);
+    pa = advance(pb);
+    issue(kA, vA, qA, pa);
+    compute(kB, vB, qB, pb, false);
   }
-
-  // Per-head totals of this wave; every lane of head r now agrees on m, l.
-  l_run = row_sum4(l_run);
-  if (j == 0) {
-    s_ml[wave][r][0] = m_run;
-    s_ml[wave][r][1] = l_run;
-  }
-  if (r < G) {
-#pragma unroll
-    for (int t = 0; t < kTiles; ++t) s_acc[wave][r][4 * t + j] = acc[t];
-  }
-  __syncthreads();
-
-  // Merge the four wave states (the same rescaling as within a wave).
-  for (int e = threadIdx.x; e < G * (D / 4); e += 64 * kDecodeWaves) {
-    const int h = e / (D / 4);
-    const int q4 = e % (D / 4);
-    float M = s_ml[0][h][0];
-#pragma unroll
-    for (int w = 1; w < kDecodeWaves; ++w) M = fmaxf(M, s_ml[w][h][0]);
-    float L = 0.f;
-    f32x4 o = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int w = 0; w < kDecodeWaves; ++w) {
-      const float f = exp2_fast(s_ml[w][h][0] - M);   // a wave without tokens has m = -inf
-      L += f * s_ml[w][h][1];
-      o += f * s_acc[w][h][q4];
-    }
-    const int qh = g * G + h;
-    if (single) {
-      store4<OutT>(out + ((size_t)b * Hq + qh) * D + 4 * q4, o * (out_mul / L));
-    } else {
-      const size_t slot = ((size_t)b * Hq + qh) * P + p;
-      *reinterpret_cast<f32x4*>(a.ws_acc + slot * D + 4 * q4) = o * out_mul;
-      if (q4 == 0) {
-        a.ws_ml[2 * slot] = M;
-        a.ws_ml[2 * slot + 1] = L;
-      }
-    }
+  if (k + 1 < nch) {
+    pb = advance(pa);
+    issue(kB, vB, qB, pb);
+    compute(kA, vA, qA, pa, false);
+    compute(kB, vB, qB, pb, true);
+  } else {
+    compute(kA, vA, qA, pa, true);
   }
 }
 
-// Two waves per SIMD (at most 256 VGPRs each) keep 8 waves' loads in flight
-// per compute unit; the float32 path at head_dim 128 needs more registers
-// for its double buffer and runs one wave per SIMD instead of spilling.
+// Two waves per SIMD (at most 256 VGPRs each) are resident together; the
+// float32 path at head_dim 128 needs more registers for its double buffer
+// and runs one wave per SIMD instead of spilling.
+// Tables, lengths and scales are passed again as restrict parameters: nothing
+// the kernel writes aliases them, so their wave-uniform reads go through the
+// scalar cache and never wait behind the vector loads in flight.
 template <int KV, int D>
 __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void decode_partitions_kernel(DecodeArgs a) {
-  decode_partitions_body<KV, D>(a);
+void decode_split_kernel(DecodeArgs a, const int32_t* __restrict__ tables, const int32_t* __restrict__ lens,
+                         const float* __restrict__ k_scale, const float* __restrict__ v_scale) {
+  decode_split_body<KV, D>(a, tables, lens, k_scale, v_scale);
 }
 
 template <int KV, int D>
-__global__ __launch_bounds__(64 * kDecodeWaves) void decode_partitions_kernel_wide(DecodeArgs a) {
-  decode_partitions_body<KV, D>(a);
+__global__ __launch_bounds__(64 * kDecodeWaves) void decode_split_kernel_wide(
+    DecodeArgs a, const int32_t* __restrict__ tables, const int32_t* __restrict__ lens,
+    const float* __restrict__ k_scale, const float* __restrict__ v_scale) {
+  decode_split_body<KV, D>(a, tables, lens, k_scale, v_scale);
 }
 
 // ---------------------------------------------------------------------------
-// Merge kernel: one workgroup per (sequence, query head) spanning > 1 partition.
+// Merge kernel: one workgroup per (sequence, kv head) pair.  Pairs finished
+// by one wave return at once; split pairs combine their partials with the
+// same rescaling as the online softmax; empty sequences get zeros.
 // ---------------------------------------------------------------------------
 template <typename OutT, int D>
-__global__ __launch_bounds__(128) void decode_reduce_kernel(DecodeArgs a) {
-  const int bh = blockIdx.x;
-  const int b = bh / a.num_q_heads;
-  const int n = clamp_len(a.context_lens[b], a);
-  const int np = min((n + a.part_tokens - 1) / a.part_tokens, a.num_parts);
-  if (np <= 1) return;   // finished by the partition kernel
-  const float* ml = a.ws_ml + (size_t)bh * a.num_parts * 2;
-  const float* acc = a.ws_acc + (size_t)bh * a.num_parts * D;
-  float M = -INFINITY;
-  for (int p = 0; p < np; ++p) M = fmaxf(M, ml[2 * p]);
-  for (int d = threadIdx.x; d < D; d += 128) {
-    float L = 0.f, o = 0.f;
-    for (int p = 0; p < np; ++p) {
-      const float f = exp2_fast(ml[2 * p] - M);
-      L += f * ml[2 * p + 1];
-      o += f * acc[(size_t)p * D + d];
+__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
+  __shared__ int64_t s_sum[2][4];
+  const int p = blockIdx.x;
+  const int Hkv = a.num_kv_heads;
+  const int b = p / Hkv;
+  const int g = p % Hkv;
+  const int G = a.group;
+  const int tid = threadIdx.x;
+
+  int64_t tot = 0, before = 0;
+  for (int i = tid; i < a.num_seqs; i += 256) {
+    const int cb = chunks_of(clamp_len(a.context_lens[i], a));
+    tot += cb;
+    if (i < b) before += cb;
+  }
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) {
+    tot += __shfl_xor(tot, s);
+    before += __shfl_xor(before, s);
+  }
+  if ((tid & 63) == 0) {
+    s_sum[0][tid >> 6] = tot;
+    s_sum[1][tid >> 6] = before;
+  }
+  __syncthreads();
+  tot = s_sum[0][0] + s_sum[0][1] + s_sum[0][2] + s_sum[0][3];
+  before = s_sum[1][0] + s_sum[1][1] + s_sum[1][2] + s_sum[1][3];
+
+  OutT* out = static_cast<OutT*>(a.out) + ((size_t)b * a.num_q_heads + g * G) * D;
+  const int cb = chunks_of(clamp_len(a.context_lens[b], a));
+  if (cb == 0) {
+    for (int e = tid; e < G * D; e += 256) out[e] = (OutT)0.f;
+    return;
+  }
+  const int64_t C = tot * Hkv;
+  const int64_t K = (C + a.num_workers - 1) / a.num_workers;
+  const int64_t s = before * Hkv + (int64_t)g * cb;
+  const int w_first = (int)(s / K);
+  const int w_last = (int)((s + cb - 1) / K);
+  if (w_first == w_last) return;   // one wave covered the pair and wrote out
+
+  for (int e = tid; e < G * (D / 4); e += 256) {
+    const int h = e / (D / 4);
+    const int q4 = e % (D / 4);
+    float M = -INFINITY;
+    for (int w = w_first; w <= w_last; ++w) M = fmaxf(M, a.ws_ml[(((size_t)w + p) * G + h) * 2]);
+    float L = 0.f;
+    f32x4 o = {0.f, 0.f, 0.f, 0.f};
+    for (int w = w_first; w <= w_last; ++w) {
+      const size_t slot = ((size_t)w + p) * G + h;
+      const float f = exp2_fast(a.ws_ml[slot * 2] - M);
+      L += f * a.ws_ml[slot * 2 + 1];
+      o += f * *reinterpret_cast<const f32x4*>(a.ws_acc + slot * D + 4 * q4);
     }
-    static_cast<OutT*>(a.out)[(size_t)bh * D + d] = (OutT)(o / L);
+    store4<OutT>(out + (size_t)h * D + 4 * q4, o * (1.f / L));
   }
 }
 
 template <int KV, int D>
-hipError_t launch_partitions_t(const DecodeArgs& a, hipStream_t stream) {
-  const unsigned grid = (unsigned)a.num_seqs * (unsigned)a.num_kv_heads * (unsigned)a.num_parts;
+hipError_t launch_split_t(const DecodeArgs& a, hipStream_t stream) {
+  const unsigned grid = (unsigned)(a.num_workers / kDecodeWaves);
   if constexpr (KV == kF32 && D == 128)
-    hipLaunchKernelGGL((decode_partitions_kernel_wide<KV, D>), dim3(grid), dim3(64 * kDecodeWaves), 0, stream, a);
+    hipLaunchKernelGGL((decode_split_kernel_wide<KV, D>), dim3(grid), dim3(64 * kDecodeWaves), 0, stream, a,
+                       a.block_tables, a.context_lens, a.k_scale, a.v_scale);
   else
-    hipLaunchKernelGGL((decode_partitions_kernel<KV, D>), dim3(grid), dim3(64 * kDecodeWaves), 0, stream, a);
+    hipLaunchKernelGGL((decode_split_kernel<KV, D>), dim3(grid), dim3(64 * kDecodeWaves), 0, stream, a,
+                       a.block_tables, a.context_lens, a.k_scale, a.v_scale);
   return hipGetLastError();
 }
 
 template <typename OutT, int D>
-hipError_t launch_reduce_t(const DecodeArgs& a, hipStream_t stream) {
-  const unsigned grid = (unsigned)a.num_seqs * (unsigned)a.num_q_heads;
-  hipLaunchKernelGGL((decode_reduce_kernel<OutT, D>), dim3(grid), dim3(128), 0, stream, a);
+hipError_t launch_merge_t(const DecodeArgs& a, hipStream_t stream) {
+  const unsigned grid = (unsigned)a.num_seqs * (unsigned)a.num_kv_heads;
+  hipLaunchKernelGGL((decode_merge_kernel<OutT, D>), dim3(grid), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_decode_partitions(const DecodeArgs& a, hipStream_t stream) {
+hipError_t launch_decode_split(const DecodeArgs& a, hipStream_t stream) {
   if (a.head_dim == 64) {
-    if (a.kv_dtype == kF32) return launch_partitions_t<kF32, 64>(a, stream);
-    if (a.kv_dtype == kBF16) return launch_partitions_t<kBF16, 64>(a, stream);
-    return launch_partitions_t<kFP8, 64>(a, stream);
+    if (a.kv_dtype == kF32) return launch_split_t<kF32, 64>(a, stream);
+    if (a.kv_dtype == kBF16) return launch_split_t<kBF16, 64>(a, stream);
+    return launch_split_t<kFP8, 64>(a, stream);
   }
-  if (a.kv_dtype == kF32) return launch_partitions_t<kF32, 128>(a, stream);
-  if (a.kv_dtype == kBF16) return launch_partitions_t<kBF16, 128>(a, stream);
-  return launch_partitions_t<kFP8, 128>(a, stream);
+  if (a.kv_dtype == kF32) return launch_split_t<kF32, 128>(a, stream);
+  if (a.kv_dtype == kBF16) return launch_split_t<kBF16, 128>(a, stream);
+  return launch_split_t<kFP8, 128>(a, stream);
 }
 
-hipError_t launch_decode_reduce(const DecodeArgs& a, hipStream_t stream) {
+hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t stream) {
   const bool f32 = a.kv_dtype == kF32;
-  if (a.head_dim == 64) return f32 ? launch_reduce_t<float, 64>(a, stream) : launch_reduce_t<__bf16, 64>(a, stream);
-  return f32 ? launch_reduce_t<float, 128>(a, stream) : launch_reduce_t<__bf16, 128>(a, stream);
+  if (a.head_dim == 64) return f32 ? launch_merge_t<float, 64>(a, stream) : launch_merge_t<__bf16, 64>(a, stream);
+  return f32 ? launch_merge_t<float, 128>(a, stream) : launch_merge_t<__bf16, 128>(a, stream);
 }
 
 }  // namespace pkv

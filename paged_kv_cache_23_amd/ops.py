@@ -55,11 +55,11 @@ def library() -> ctypes.CDLL:
         D = ctypes.POINTER(CacheDesc)
         sigs = {
             "pkv_kv_append": (ctypes.c_int, [D, P, P, P, I32, P, P, P]),
-            "pkv_partition_tokens": (I32, [D, I32, I32]),
+            "pkv_decode_workers": (I32, [D, I32, I32]),
             "pkv_decode_workspace_bytes": (SZ, [D, I32, I32, I32]),
             "pkv_paged_decode": (ctypes.c_int, [D, P, P, P, P, I32, P, I32, I32, F, P, P, SZ, P]),
-            "pkv_paged_decode_partitions": (ctypes.c_int, [D, P, P, P, P, I32, P, I32, I32, F, I32, P, P, SZ, P]),
-            "pkv_paged_decode_reduce": (ctypes.c_int, [D, I32, P, I32, I32, I32, P, P, SZ, P]),
+            "pkv_paged_decode_split": (ctypes.c_int, [D, P, P, P, P, I32, P, I32, I32, F, I32, P, P, SZ, P]),
+            "pkv_paged_decode_merge": (ctypes.c_int, [D, I32, P, I32, I32, I32, P, P, SZ, P]),
             "pkv_strerror": (ctypes.c_char_p, [ctypes.c_int]),
             "pkv_version": (ctypes.c_char_p, []),
         }
@@ -173,18 +173,19 @@ def _max_ctx(block_tables: torch.Tensor, max_context_len: Optional[int]) -> int:
     return int(max_context_len) if max_context_len is not None else BLOCK_SIZE * block_tables.shape[1]
 
 
-def partition_tokens(k_pool, v_pool, num_q_heads: int, num_seqs: int, max_context_len: int,
-                     k_scale=None, v_scale=None) -> int:
+def decode_workers(k_pool, v_pool, num_q_heads: int, num_seqs: int, max_context_len: int,
+                   k_scale=None, v_scale=None) -> int:
+    """Worker waves the decode uses for this shape on the current device."""
     desc = cache_desc(k_pool, v_pool, num_q_heads, k_scale, v_scale)
-    res = library().pkv_partition_tokens(ctypes.byref(desc), num_seqs, max_context_len)
-    _check(min(res, 0), "pkv_partition_tokens")
+    res = library().pkv_decode_workers(ctypes.byref(desc), num_seqs, max_context_len)
+    _check(min(res, 0), "pkv_decode_workers")
     return res
 
 
 def decode_workspace_bytes(k_pool, v_pool, num_q_heads: int, num_seqs: int, max_context_len: int,
-                           partition: int = 0, k_scale=None, v_scale=None) -> int:
+                           num_workers: int = 0, k_scale=None, v_scale=None) -> int:
     desc = cache_desc(k_pool, v_pool, num_q_heads, k_scale, v_scale)
-    return int(library().pkv_decode_workspace_bytes(ctypes.byref(desc), num_seqs, max_context_len, partition))
+    return int(library().pkv_decode_workspace_bytes(ctypes.byref(desc), num_seqs, max_context_len, num_workers))
 
 
 def _workspace(nbytes: int, like: torch.Tensor, workspace: Optional[torch.Tensor]):
@@ -214,25 +215,25 @@ def paged_decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
     return out
 
 
-def paged_decode_partitions(q, k_pool, v_pool, block_tables, context_lens, scale, partition: int,
-                            out, workspace, k_scale=None, v_scale=None, max_context_len=None,
-                            stream=None) -> None:
-    """First kernel of ``paged_decode`` with an explicit partition size."""
+def paged_decode_split(q, k_pool, v_pool, block_tables, context_lens, scale, num_workers: int,
+                       out, workspace, k_scale=None, v_scale=None, max_context_len=None,
+                       stream=None) -> None:
+    """First kernel of ``paged_decode`` with an explicit worker-wave count."""
     desc, out = _decode_checks(q, k_pool, v_pool, block_tables, context_lens, k_scale, v_scale, out)
     mctx = _max_ctx(block_tables, max_context_len)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(library().pkv_paged_decode_partitions(
+    _check(library().pkv_paged_decode_split(
         ctypes.byref(desc), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables), block_tables.shape[1],
-        _ptr(context_lens), q.shape[0], mctx, float(scale), int(partition), _ptr(out), _ptr(workspace),
-        wbytes, _stream(stream)), "pkv_paged_decode_partitions")
+        _ptr(context_lens), q.shape[0], mctx, float(scale), int(num_workers), _ptr(out), _ptr(workspace),
+        wbytes, _stream(stream)), "pkv_paged_decode_split")
 
 
-def paged_decode_reduce(q, k_pool, v_pool, block_tables, context_lens, partition: int, out, workspace,
-                        k_scale=None, v_scale=None, max_context_len=None, stream=None) -> None:
-    """Second kernel of ``paged_decode``: merge the partition partials into ``out``."""
+def paged_decode_merge(q, k_pool, v_pool, block_tables, context_lens, num_workers: int, out, workspace,
+                       k_scale=None, v_scale=None, max_context_len=None, stream=None) -> None:
+    """Second kernel of ``paged_decode``: merge the split pairs' partials into ``out``."""
     desc, out = _decode_checks(q, k_pool, v_pool, block_tables, context_lens, k_scale, v_scale, out)
     mctx = _max_ctx(block_tables, max_context_len)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(library().pkv_paged_decode_reduce(
-        ctypes.byref(desc), block_tables.shape[1], _ptr(context_lens), q.shape[0], mctx, int(partition),
-        _ptr(out), _ptr(workspace), wbytes, _stream(stream)), "pkv_paged_decode_reduce")
+    _check(library().pkv_paged_decode_merge(
+        ctypes.byref(desc), block_tables.shape[1], _ptr(context_lens), q.shape[0], mctx, int(num_workers),
+        _ptr(out), _ptr(workspace), wbytes, _stream(stream)), "pkv_paged_decode_merge")

@@ -27,8 +27,9 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for required in ("pkv_kv_append", "pkv_paged_decode", "pkv_paged_decode_partitions",
-                     "pkv_paged_decode_reduce", "pkv_decode_workspace_bytes", "pkv_strerror"):
+    for required in ("pkv_kv_append", "pkv_paged_decode", "pkv_paged_decode_split",
+                     "pkv_paged_decode_merge", "pkv_decode_workspace_bytes", "pkv_decode_workers",
+                     "pkv_strerror"):
         assert required in names
 
 
@@ -82,35 +83,32 @@ def test_null_and_size_errors():
                                 FAKE, None, 0, None) == EINVAL
     assert lib.pkv_paged_decode(ctypes.byref(d), FAKE + 8, FAKE, FAKE, FAKE, 4, FAKE, 2, 64, 0.1,
                                 FAKE, None, 0, None) == EINVAL          # misaligned q
-    assert lib.pkv_paged_decode_partitions(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 64, 0.1,
-                                           48, FAKE, None, 0, None) == EINVAL   # partition not /32
-    assert lib.pkv_paged_decode_partitions(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 64, 0.1,
-                                           4096, FAKE, None, 0, None) == EINVAL  # partition too long
+    assert lib.pkv_paged_decode_split(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 64, 0.1,
+                                      6, FAKE, None, 0, None) == EINVAL    # workers not a multiple of 4
+    assert lib.pkv_paged_decode_split(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 64, 0.1,
+                                      -4, FAKE, None, 0, None) == EINVAL   # negative workers
 
 
 def test_workspace_sizing_and_check():
     lib = ops.library()
-    d = _desc()
-    # one partition: no workspace
-    assert lib.pkv_decode_workspace_bytes(ctypes.byref(d), 4, 64, 512) == 0
-    # 3 partitions of 64 tokens over 4 seqs x 8 heads: acc (rounded to 256 B) + (max, sum)
-    rows = 4 * 8 * 3
+    d = _desc()                                 # 8 q heads / 2 kv heads: group 4, head_dim 128
+    # (workers + seqs * kv heads) partial states: acc rows rounded to 256 B, then (max, sum)
+    rows = (64 + 4 * 2) * 4
     acc = -(-rows * 128 * 4 // 256) * 256
     need = lib.pkv_decode_workspace_bytes(ctypes.byref(d), 4, 150, 64)
     assert need == acc + rows * 2 * 4
-    st = lib.pkv_paged_decode_partitions(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 16, FAKE, 4, 150, 0.1,
-                                         64, FAKE, FAKE, need - 1, None)
+    assert lib.pkv_decode_workspace_bytes(ctypes.byref(d), 4, 150, 6) == 0     # bad worker count
+    st = lib.pkv_paged_decode_split(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 16, FAKE, 4, 150, 0.1,
+                                    64, FAKE, FAKE, need - 1, None)
     assert st == EWORKSPACE
-    st = lib.pkv_paged_decode_reduce(ctypes.byref(d), 16, FAKE, 4, 150, 64, FAKE, None, 0, None)
+    st = lib.pkv_paged_decode_split(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 16, FAKE, 4, 150, 0.1,
+                                    64, FAKE, None, need, None)
     assert st == EWORKSPACE
-
-
-def test_default_partition_is_a_multiple_of_32_within_limits():
-    lib = ops.library()
-    for (B, Hkv, ctx) in [(64, 8, 4096), (8, 8, 131072), (256, 8, 8192), (1, 1, 10), (4, 2, 64)]:
-        d = _desc(num_kv_heads=Hkv, num_q_heads=4 * Hkv)
-        p = lib.pkv_partition_tokens(ctypes.byref(d), B, ctx)
-        assert p > 0 and p % 32 == 0 and p <= 2048
+    st = lib.pkv_paged_decode_merge(ctypes.byref(d), 16, FAKE, 4, 150, 64, FAKE, None, 0, None)
+    assert st == EWORKSPACE
+    # zero sequences: nothing to do, nothing launched
+    assert lib.pkv_paged_decode_split(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 16, FAKE, 0, 150, 0.1,
+                                      64, FAKE, None, 0, None) == 0
 
 
 def test_strerror_and_version():

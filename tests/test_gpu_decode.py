@@ -44,14 +44,26 @@ def test_small_shapes(kv_dtype, D, G):
     assert_close(out, oracle_full(wl), kv_dtype)
 
 
-@pytest.mark.parametrize("partition", [32, 64, 96, 256, 2048])
+@pytest.mark.parametrize("workers", [4, 8, 12, 64, 512, 2048])
 @pytest.mark.parametrize("kv_dtype", ["f32", "bf16", "fp8"])
-def test_explicit_partitions(kv_dtype, partition):
-    """Split-context partitions + merge kernel give the same answer for any partition size."""
-    wl = build_workload("parts", [1, 33, 100, 257, 700, 2049], 16, 4, 128 if kv_dtype != "f32" else 64,
-                        kv_dtype, seed=partition)
-    out = Dev(wl).decode(partition=partition)
+def test_explicit_workers(kv_dtype, workers):
+    """Any worker count (so any split points between waves, merged by the
+    second kernel) gives the same answer within tolerance."""
+    wl = build_workload("split", [1, 33, 100, 257, 700, 2049], 16, 4, 128 if kv_dtype != "f32" else 64,
+                        kv_dtype, seed=workers)
+    out = Dev(wl).decode(workers=workers)
     assert_close(out, oracle_full(wl), kv_dtype)
+
+
+def test_runs_of_one_chunk_sequences():
+    """Many sequences of at most 32 tokens back to back: consecutive chunks each
+    open a new (sequence, kv head) pair."""
+    lens = [1, 5, 32, 0, 17, 31, 2, 0, 9, 32, 33, 3]
+    for kv_dtype in ("bf16", "fp8"):
+        wl = build_workload("short", lens, 8, 2, 128, kv_dtype, seed=9)
+        for workers in (None, 4, 8):
+            out = Dev(wl).decode(workers=workers)
+            assert_close(out, oracle_full(wl), kv_dtype)
 
 
 def test_zero_length_and_single_token():

@@ -135,8 +135,8 @@ def test_two_kernel_form_equals_fused_call(kv_dtype):
     wl = _wl(kv_dtype)
     dev = Dev(wl)
     fused = dev.decode()
-    part = ops.partition_tokens(dev.k_pool, dev.v_pool, 8, len(LENS), max(LENS), dev.k_scale, dev.v_scale)
-    split = dev.decode(partition=part)
+    workers = ops.decode_workers(dev.k_pool, dev.v_pool, 8, len(LENS), max(LENS), dev.k_scale, dev.v_scale)
+    split = dev.decode(workers=workers)
     assert np.array_equal(_bits(split), _bits(fused))
     assert_close(split, oracle_full(wl), kv_dtype)
 
