@@ -2,8 +2,8 @@
 """Paged decode benchmark on one MI355X.
 
 A step is one decode pass of one layer over the whole batch: one
-pkv_paged_decode call (its split kernel plus its merge kernel; for workloads
-that append, the kv_append of one token per sequence first).  Inputs are seeded synthetic data already
+pkv_paged_decode call (a single kernel launch; for workloads that append, the
+kv_append of one token per sequence first).  Inputs are seeded synthetic data already
 resident in HBM; successive steps rotate over ``--layers`` distinct copies of
 the pool so that the bytes touched between reuses of one copy exceed the
 256 MB Infinity Cache.
@@ -55,7 +55,7 @@ def kernel_source_hash() -> str:
 def committed_traffic(workload: str):
     """HBM bytes per decode-kernel launch from the committed rocprofv3 counter
     summary, if it was taken on the current kernel source; else None."""
-    path = os.path.join(PROFILE_DIR, f"decode_split_{workload}_pmc.txt")
+    path = os.path.join(PROFILE_DIR, f"decode_kernel_{workload}_pmc.txt")
     if not os.path.exists(path):
         return None
     text = open(path).read()
@@ -116,7 +116,7 @@ class Runner:
         if self.workers <= 0:
             raise RuntimeError(f"pkv_decode_workers failed: {self.workers}")
         nbytes = lib.pkv_decode_workspace_bytes(ctypes.byref(self.desc), self.B, self.max_ctx, self.workers)
-        self.ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+        self.ws = ops.new_workspace(nbytes, dev)
         self.ws_bytes = self.ws.numel()
         self.kv_bytes = wl.kv_bytes(after_append=self.append)
         self.append_bytes = 0
@@ -136,38 +136,18 @@ class Runner:
             raise RuntimeError(f"pkv_kv_append failed: {st}")
 
     def decode(self, layer: int, stream):
-        """The fused call: split kernel then merge kernel."""
-        st = self.lib.pkv_paged_decode(
+        st = self.lib.pkv_paged_decode_ex(
             ctypes.byref(self.desc), self.q.data_ptr(), self.k_pools[layer].data_ptr(),
             self.v_pools[layer].data_ptr(), self.tables.data_ptr(), self.tables.shape[1], self.lens.data_ptr(),
-            self.B, self.max_ctx, self.wl.scale, self.out.data_ptr(), self.ws.data_ptr(), self.ws_bytes, stream)
+            self.B, self.max_ctx, self.wl.scale, self.workers if self.explicit_workers else 0,
+            self.out.data_ptr(), self.ws.data_ptr(), self.ws_bytes, stream)
         if st:
-            raise RuntimeError(f"pkv_paged_decode failed: {st}")
-
-    def split(self, layer: int, stream):
-        st = self.lib.pkv_paged_decode_split(
-            ctypes.byref(self.desc), self.q.data_ptr(), self.k_pools[layer].data_ptr(),
-            self.v_pools[layer].data_ptr(), self.tables.data_ptr(), self.tables.shape[1], self.lens.data_ptr(),
-            self.B, self.max_ctx, self.wl.scale, self.workers, self.out.data_ptr(), self.ws.data_ptr(),
-            self.ws_bytes, stream)
-        if st:
-            raise RuntimeError(f"pkv_paged_decode_split failed: {st}")
-
-    def merge(self, stream):
-        st = self.lib.pkv_paged_decode_merge(ctypes.byref(self.desc), self.tables.shape[1], self.lens.data_ptr(),
-                                             self.B, self.max_ctx, self.workers, self.out.data_ptr(),
-                                             self.ws.data_ptr(), self.ws_bytes, stream)
-        if st:
-            raise RuntimeError(f"pkv_paged_decode_merge failed: {st}")
+            raise RuntimeError(f"pkv_paged_decode_ex failed: {st}")
 
     def step(self, layer: int, stream):
         if self.append:
             self.append_step(layer, stream)
-        if self.explicit_workers:
-            self.split(layer, stream)
-            self.merge(stream)
-        else:
-            self.decode(layer, stream)
+        self.decode(layer, stream)
 
 
 def check_against_oracle(runner, sample_seqs: int = 4) -> float:
@@ -266,23 +246,21 @@ def run_bench(args) -> dict:
     total_ms = start_ev.elapsed_time(end_ev)
     ms_per_step = total_ms / K
 
-    # per-kernel durations: the same steps with HIP events around each kernel
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    # per-launch durations of the decode kernel: the same steps, HIP events
+    # around each launch on the stream it runs on
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
     for i in range(K):
         layer = i % L
         if runner.append:
             runner.append_step(layer, s)
         ev[i][0].record()
-        runner.split(layer, s)
+        runner.decode(layer, s)
         ev[i][1].record()
-        runner.merge(s)
-        ev[i][2].record()
     torch.cuda.synchronize()
     part_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
-    red_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
     log(f"{K} steps: {total_ms:.3f} ms on the stream, {wall * 1e3:.3f} ms wall ({ms_per_step * 1e3:.1f} us/step); "
-        f"split kernel mean {part_ms.mean() * 1e3:.1f} us (p10 {np.percentile(part_ms, 10) * 1e3:.1f}, "
-        f"p90 {np.percentile(part_ms, 90) * 1e3:.1f}), merge kernel mean {red_ms.mean() * 1e3:.1f} us")
+        f"decode kernel mean {part_ms.mean() * 1e3:.1f} us (p10 {np.percentile(part_ms, 10) * 1e3:.1f}, "
+        f"p90 {np.percentile(part_ms, 90) * 1e3:.1f})")
 
     step_bytes = runner.kv_bytes + runner.append_bytes
     gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
@@ -314,7 +292,7 @@ def run_bench(args) -> dict:
         "decode_tokens_per_s": round(wl.batch / (ms_per_step * 1e-3), 1),
         "max_abs_err_sampled": err,
         "roofline": {
-            "kernel": "decode_split_kernel",
+            "kernel": "decode_kernel",
             "bound": "hbm",
             "achieved": round(kern_gbs, 2),
             "peak": HBM_PEAK_GBS,
@@ -323,7 +301,6 @@ def run_bench(args) -> dict:
             "traffic": traffic,
             "algorithmic_bytes_per_launch": runner.kv_bytes,
             "mean_launch_us": round(float(part_ms.mean()) * 1e3, 2),
-            "merge_kernel_mean_us": round(float(red_ms.mean()) * 1e3, 2),
         },
     }
     if not args.no_cpu_baseline:
@@ -371,7 +348,7 @@ def main() -> int:
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="llama3-8b-b64")
     p.add_argument("--layers", type=int, default=4)
-    p.add_argument("--workers", type=int, default=0, help="split-kernel worker waves (0: the library's choice)")
+    p.add_argument("--workers", type=int, default=0, help="decode worker waves (0: the library's choice)")
     p.add_argument("--identity-tables", action="store_true",
                    help="store each sequence's blocks consecutively (the slab layout as a table)")
     p.add_argument("--cpu-seconds", type=float, default=10.0)

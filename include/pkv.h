@@ -98,18 +98,18 @@ int pkv_kv_append(const pkv_cache_desc* desc, const void* k_new, const void* v_n
                   const int64_t* slot_mapping, int32_t num_tokens, void* k_pool,
                   void* v_pool, void* stream);
 
-/* Number of worker waves pkv_paged_decode's first kernel uses for this batch
- * shape on the current device: one per SIMD slot the kernel's register budget
- * allows (2 per SIMD, 8 per compute unit), fewer for batches with fewer
- * 32-token chunks; always a multiple of 4.  Returns a negative status on bad
- * arguments or when no device is current. */
+/* Number of worker waves pkv_paged_decode uses for this batch shape on the
+ * current device: one per SIMD slot the kernel's register budget allows
+ * (2 per SIMD, 8 per compute unit), fewer for batches with fewer 32-token
+ * chunks; always a multiple of 4.  Returns a negative status on bad arguments
+ * or when no device is current. */
 int32_t pkv_decode_workers(const pkv_cache_desc* desc, int32_t num_seqs,
                            int32_t max_context_len);
 
-/* Device workspace bytes a decode of this shape needs:
- * (num_workers + num_seqs * num_kv_heads) partial states of group * (head_dim
- * + 2) floats.  num_workers == 0 means pkv_decode_workers(...).  Returns 0 on
- * bad arguments. */
+/* Device workspace bytes a decode of this shape needs: (num_workers +
+ * num_seqs * num_kv_heads) partial states of group * (head_dim + 2) floats,
+ * then one int32 counter per (sequence, kv head) pair.  num_workers == 0 means
+ * pkv_decode_workers(...).  Returns 0 on bad arguments. */
 size_t pkv_decode_workspace_bytes(const pkv_cache_desc* desc, int32_t num_seqs,
                                   int32_t max_context_len, int32_t num_workers);
 
@@ -122,37 +122,33 @@ size_t pkv_decode_workspace_bytes(const pkv_cache_desc* desc, int32_t num_seqs,
  * Lengths are taken as min(context_lens[b], max_context_len,
  * 16 * max_blocks_per_seq); block ids are clamped into [0, num_blocks).
  * Accumulation is float32; out is rounded once to q_dtype (nearest even).
+ *
+ * One kernel launch.  The batch's 32-token chunks of every (sequence, kv head)
+ * pair, pairs in sequence-major order, are cut into equal contiguous ranges,
+ * one per worker wave; each wave runs section 3's online softmax over its
+ * range.  A pair split between waves is finished by its last contributor,
+ * which merges the float32 partial states (running max, sum, unnormalised
+ * accumulator) with the same rescale by exp(m_old - m_new).
  *   workspace  device buffer of pkv_decode_workspace_bytes(..., 0) bytes,
- *              16-byte aligned; its contents are scratch. */
+ *              16-byte aligned.  Its counter region must be zero before the
+ *              first call (zero-fill the whole buffer once); every call
+ *              leaves it zero again.  The rest is scratch.  Calls that share
+ *              one workspace must be ordered (one stream). */
 int pkv_paged_decode(const pkv_cache_desc* desc, const void* q, const void* k_pool,
                      const void* v_pool, const int32_t* block_tables,
                      int32_t max_blocks_per_seq, const int32_t* context_lens,
                      int32_t num_seqs, int32_t max_context_len, float scale, void* out,
                      void* workspace, size_t workspace_bytes, void* stream);
 
-/* The two kernels of pkv_paged_decode as separate calls, with an explicit
- * worker count (a positive multiple of 4, or 0 for the default).
- * pkv_paged_decode_split: the batch's 32-token chunks of every (sequence,
- * kv head) pair, pairs in sequence-major order, are cut into num_workers equal
- * contiguous ranges, one per wave; each wave runs the online softmax of
- * section 3 over its range, writes the output of every pair it covers
- * completely and a float32 partial state (running max, sum, unnormalised
- * accumulator) for each pair it covers in part.
- * pkv_paged_decode_merge combines the partials of every split pair (the same
- * rescale by exp(m_old - m_new), applied across waves) and writes zeros for
- * empty sequences.  Calling them in order on one stream with the same
- * num_workers equals pkv_paged_decode with that count. */
-int pkv_paged_decode_split(const pkv_cache_desc* desc, const void* q, const void* k_pool,
-                           const void* v_pool, const int32_t* block_tables,
-                           int32_t max_blocks_per_seq, const int32_t* context_lens,
-                           int32_t num_seqs, int32_t max_context_len, float scale,
-                           int32_t num_workers, void* out, void* workspace,
-                           size_t workspace_bytes, void* stream);
-
-int pkv_paged_decode_merge(const pkv_cache_desc* desc, int32_t max_blocks_per_seq,
-                           const int32_t* context_lens, int32_t num_seqs,
-                           int32_t max_context_len, int32_t num_workers, void* out,
-                           const void* workspace, size_t workspace_bytes, void* stream);
+/* pkv_paged_decode with an explicit worker count (a positive multiple of 4, or
+ * 0 for pkv_decode_workers(...)); the workspace must be sized for that count.
+ * Any count gives the same result up to float32 rounding. */
+int pkv_paged_decode_ex(const pkv_cache_desc* desc, const void* q, const void* k_pool,
+                        const void* v_pool, const int32_t* block_tables,
+                        int32_t max_blocks_per_seq, const int32_t* context_lens,
+                        int32_t num_seqs, int32_t max_context_len, float scale,
+                        int32_t num_workers, void* out, void* workspace,
+                        size_t workspace_bytes, void* stream);
 
 /* Static description of a status code. */
 const char* pkv_strerror(int status);

@@ -1,5 +1,5 @@
-// C ABI of libpkv: host-side argument checks, partition choice, workspace
-// layout and kernel dispatch.  Declarations and contracts: include/pkv.h.
+// C ABI of libpkv: host-side argument checks, worker count, workspace layout
+// and kernel dispatch.  Declarations and contracts: include/pkv.h.
 
 #include "pkv.h"
 #include "pkv_internal.h"
@@ -74,14 +74,25 @@ int32_t resolve_workers(const pkv_cache_desc* d, int32_t num_seqs, int32_t max_c
   return workers;
 }
 
+// Workspace: partial accumulators, then (max, sum) pairs, then one counter
+// per (sequence, kv head) pair; each region starts on a 256-byte boundary.
+size_t align_up(size_t n) { return (n + kWsAlign - 1) / kWsAlign * kWsAlign; }
+
+size_t partial_rows(const pkv_cache_desc* d, int32_t num_seqs, int32_t workers) {
+  return ((size_t)workers + (size_t)num_seqs * d->num_kv_heads) * (d->num_q_heads / d->num_kv_heads);
+}
+
 size_t acc_bytes(const pkv_cache_desc* d, int32_t num_seqs, int32_t workers) {
-  const size_t rows = ((size_t)workers + (size_t)num_seqs * d->num_kv_heads) * (d->num_q_heads / d->num_kv_heads);
-  return (rows * d->head_dim * sizeof(float) + kWsAlign - 1) / kWsAlign * kWsAlign;
+  return align_up(partial_rows(d, num_seqs, workers) * d->head_dim * sizeof(float));
+}
+
+size_t ml_bytes(const pkv_cache_desc* d, int32_t num_seqs, int32_t workers) {
+  return align_up(partial_rows(d, num_seqs, workers) * 2 * sizeof(float));
 }
 
 size_t workspace_bytes(const pkv_cache_desc* d, int32_t num_seqs, int32_t workers) {
-  const size_t rows = ((size_t)workers + (size_t)num_seqs * d->num_kv_heads) * (d->num_q_heads / d->num_kv_heads);
-  return acc_bytes(d, num_seqs, workers) + rows * 2 * sizeof(float);
+  return acc_bytes(d, num_seqs, workers) + ml_bytes(d, num_seqs, workers) +
+         align_up((size_t)num_seqs * d->num_kv_heads * sizeof(int32_t));
 }
 
 int check_decode_args(const pkv_cache_desc* d, const void* q, const void* k_pool, const void* v_pool,
@@ -119,8 +130,10 @@ DecodeArgs make_args(const pkv_cache_desc* d, const void* q, const void* k_pool,
   a.num_workers = workers;
   a.kv_dtype = d->kv_dtype;
   a.scale = scale;
-  a.ws_acc = static_cast<float*>(workspace);
-  a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + acc_bytes(d, num_seqs, workers));
+  char* ws = static_cast<char*>(workspace);
+  a.ws_acc = reinterpret_cast<float*>(ws);
+  a.ws_ml = reinterpret_cast<float*>(ws + acc_bytes(d, num_seqs, workers));
+  a.counters = reinterpret_cast<int32_t*>(ws + acc_bytes(d, num_seqs, workers) + ml_bytes(d, num_seqs, workers));
   return a;
 }
 
@@ -169,10 +182,10 @@ size_t pkv_decode_workspace_bytes(const pkv_cache_desc* desc, int32_t num_seqs, 
   return workspace_bytes(desc, num_seqs, w);
 }
 
-int pkv_paged_decode_split(const pkv_cache_desc* desc, const void* q, const void* k_pool, const void* v_pool,
-                           const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
-                           int32_t num_seqs, int32_t max_context_len, float scale, int32_t num_workers, void* out,
-                           void* workspace, size_t ws_bytes, void* stream) {
+int pkv_paged_decode_ex(const pkv_cache_desc* desc, const void* q, const void* k_pool, const void* v_pool,
+                        const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                        int32_t num_seqs, int32_t max_context_len, float scale, int32_t num_workers, void* out,
+                        void* workspace, size_t ws_bytes, void* stream) {
   int st = check_decode_args(desc, q, k_pool, v_pool, block_tables, max_blocks_per_seq, context_lens,
                              num_seqs, max_context_len, out);
   if (st != PKV_OK) return st;
@@ -183,37 +196,15 @@ int pkv_paged_decode_split(const pkv_cache_desc* desc, const void* q, const void
   if (!aligned16(workspace)) return PKV_EINVAL;
   DecodeArgs a = make_args(desc, q, k_pool, v_pool, block_tables, max_blocks_per_seq, context_lens, num_seqs,
                            max_context_len, scale, w, out, workspace);
-  return launch_status(pkv::launch_decode_split(a, static_cast<hipStream_t>(stream)));
-}
-
-int pkv_paged_decode_merge(const pkv_cache_desc* desc, int32_t max_blocks_per_seq, const int32_t* context_lens,
-                           int32_t num_seqs, int32_t max_context_len, int32_t num_workers, void* out,
-                           const void* workspace, size_t ws_bytes, void* stream) {
-  int st = check_desc(desc);
-  if (st != PKV_OK) return st;
-  if (!context_lens || !out || num_seqs < 0 || max_context_len < 0 || max_blocks_per_seq <= 0)
-    return PKV_EINVAL;
-  if (!aligned16(out)) return PKV_EINVAL;
-  const int32_t w = resolve_workers(desc, num_seqs, max_context_len, num_workers);
-  if (w <= 0) return w == 0 ? PKV_EINVAL : w;
-  if (num_seqs == 0) return PKV_OK;
-  if (!workspace || ws_bytes < workspace_bytes(desc, num_seqs, w)) return PKV_EWORKSPACE;
-  if (!aligned16(workspace)) return PKV_EINVAL;
-  // the merge reads lengths and partials only; q, pools and tables are unused
-  DecodeArgs a = make_args(desc, out, out, out, context_lens, max_blocks_per_seq, context_lens, num_seqs,
-                           max_context_len, 1.f, w, out, const_cast<void*>(workspace));
-  return launch_status(pkv::launch_decode_merge(a, static_cast<hipStream_t>(stream)));
+  return launch_status(pkv::launch_decode(a, static_cast<hipStream_t>(stream)));
 }
 
 int pkv_paged_decode(const pkv_cache_desc* desc, const void* q, const void* k_pool, const void* v_pool,
                      const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
                      int32_t num_seqs, int32_t max_context_len, float scale, void* out, void* workspace,
                      size_t ws_bytes, void* stream) {
-  int st = pkv_paged_decode_split(desc, q, k_pool, v_pool, block_tables, max_blocks_per_seq, context_lens,
-                                  num_seqs, max_context_len, scale, 0, out, workspace, ws_bytes, stream);
-  if (st != PKV_OK) return st;
-  return pkv_paged_decode_merge(desc, max_blocks_per_seq, context_lens, num_seqs, max_context_len, 0, out,
-                                workspace, ws_bytes, stream);
+  return pkv_paged_decode_ex(desc, q, k_pool, v_pool, block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                             max_context_len, scale, 0, out, workspace, ws_bytes, stream);
 }
 
 const char* pkv_strerror(int status) {

@@ -1,4 +1,4 @@
-// Paged decode attention for gfx950: split kernel + merge kernel.
+// Paged decode attention for gfx950: one stream-K kernel.
 //
 // What is computed (Habr KV-Cache article, habr.com/ru/articles/1021832):
 //  - section 3 "Recalling FlashAttention": exact softmax(q K^T * scale) V,
@@ -15,11 +15,10 @@
 // Work decomposition.  The batch is a list of 32-token chunks (two blocks)
 // of every (sequence, kv head) pair.  One worker wave per SIMD slot of the
 // GPU takes an equal contiguous range of that list (stream-K style), so all
-// waves stream the same bytes and none waits on another; it keeps a running
-// max / sum / accumulator per pair segment for the pair's whole query group.
-// A pair that one wave covers completely is finished by that wave; a pair
-// split between waves leaves one float32 partial per wave for
-// decode_merge_kernel.
+// waves stream the same bytes; it keeps a running max / sum / accumulator per
+// pair segment for the pair's whole query group.  A pair that one wave covers
+// completely is finished by that wave; a pair split between waves is merged
+// by whichever of its contributors finishes last (see decode_body).
 //
 // Tile math (CDNA4 MFMA, 64-lane waves).  Scores are computed transposed,
 // S^T[token][head] = K q^T, so that the MFMA output layout (lane l holds rows
@@ -357,30 +356,34 @@ __device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
 }
 
 // Position of a chunk in the global order: pairs (b, g) sequence-major, chunk
-// c of the pair's cb chunks.  All fields are wave-uniform.
+// c of the pair's cb chunks, global chunk index x.  All fields are
+// wave-uniform.
 struct Pos {
   int b, g, c, cb, n;
+  int64_t x;
 };
 
 // ---------------------------------------------------------------------------
-// Split kernel.
+// Decode kernel.
 //
 // The batch's work is the list of 32-token chunks of every (sequence, kv head)
 // pair, pairs ordered sequence-major.  Worker wave w (one per SIMD slot of the
 // GPU, all resident at once) takes the contiguous chunk range
 // [w*K, (w+1)*K), K = ceil(chunks / workers), so every wave streams the same
 // number of bytes.  It walks its range pair by pair with one online-softmax
-// state; a pair that lies wholly inside the range is finished here, the
-// others leave a float32 partial (max, sum, unnormalised accumulator) in slot
-// w + pair of the workspace for the merge kernel.  Slot w + pair is unique:
-// ranges are contiguous and ordered, so a later wave never covers an earlier
-// pair.
+// state.  A pair that lies wholly inside the range is finished at once.  A
+// pair shared with other waves (at most the first and the last pair of a
+// range) leaves a float32 partial (max, sum, unnormalised accumulator) in slot
+// w + pair of the workspace; slots are unique because ranges are contiguous
+// and ordered.  Each contributor then bumps the pair's counter (agent-scope
+// release), and the one that completes the count (acquire) merges all the
+// pair's partials after its own streaming loop and resets the counter to zero
+// for the next call.  Nobody waits on anybody, so every wave exits.
 // ---------------------------------------------------------------------------
 template <int KV, int D>
-__device__ __forceinline__ void decode_split_body(const DecodeArgs& a, const int32_t* __restrict__ tables,
-                                                  const int32_t* __restrict__ lens,
-                                                  const float* __restrict__ k_scale,
-                                                  const float* __restrict__ v_scale) {
+__device__ __forceinline__ void decode_body(const DecodeArgs& a, const int32_t* __restrict__ tables,
+                                            const int32_t* __restrict__ lens, const float* __restrict__ k_scale,
+                                            const float* __restrict__ v_scale) {
   using T = typename TileOf<KV, D>::type;
   using OutT = typename TileOf<KV, D>::Out;
   using Elem = typename T::Elem;
@@ -396,14 +399,24 @@ __device__ __forceinline__ void decode_split_body(const DecodeArgs& a, const int
   const int Hkv = a.num_kv_heads;
   const int G = a.group;
   const int Hq = a.num_q_heads;
+  OutT* out = static_cast<OutT*>(a.out);
 
   auto seq_len = [&](int b) -> int { return uni(clamp_len(lens[uni(b)], a)); };
 
-  // ---- this wave's chunk range -------------------------------------------
+  // ---- chunk totals; wave 0 also writes the zero output of empty sequences ----
   int64_t total = 0;   // chunks per kv head over the batch
+  int cb_lane = 0;     // chunks of sequence `lane` (kept when the batch has <= 64 sequences)
   for (int base = 0; base < B; base += 64) {
     const int bi = base + lane;
-    total += uni(wave_sum(bi < B ? chunks_of(clamp_len(lens[bi], a)) : 0));
+    const int n = bi < B ? clamp_len(lens[bi], a) : 1;
+    cb_lane = chunks_of(n);
+    total += uni(wave_sum(bi < B ? cb_lane : 0));
+    if (wid == 0) {
+      for (uint64_t empty = __builtin_amdgcn_ballot_w64(n == 0); empty; empty &= empty - 1) {
+        const int b = uni(base + __builtin_ctzll(empty));
+        for (int e = lane; e < Hq * D; e += 64) out[(size_t)b * Hq * D + e] = (OutT)0.f;
+      }
+    }
   }
   const int64_t C = total * Hkv;
   const int64_t K = (C + W - 1) / W;
@@ -419,7 +432,7 @@ __device__ __forceinline__ void decode_split_body(const DecodeArgs& a, const int
     int64_t run = 0;
     for (int base = 0; base < B; base += 64) {
       const int bi = base + lane;
-      const int cb = bi < B ? chunks_of(clamp_len(lens[bi], a)) : 0;
+      const int cb = bi < B ? (B <= 64 ? cb_lane : chunks_of(clamp_len(lens[bi], a))) : 0;
       const int incl = wave_inclusive_scan(cb, lane);
       const int64_t ex = run + incl - cb;
       const bool hit = cb > 0 && (int64_t)Hkv * ex <= x0 && x0 < (int64_t)Hkv * (ex + cb);
@@ -437,12 +450,14 @@ __device__ __forceinline__ void decode_split_body(const DecodeArgs& a, const int
   pos.b = b0;
   pos.n = seq_len(b0);
   pos.cb = chunks_of(pos.n);
+  pos.x = x0;
   {
     const int off = uni((int)(x0 - (int64_t)Hkv * before0));
     pos.g = uni(off / pos.cb);
     pos.c = uni(off - pos.g * pos.cb);
   }
   auto advance = [&](Pos q) -> Pos {
+    ++q.x;
     if (++q.c == q.cb) {
       q.c = 0;
       if (++q.g == Hkv) {
@@ -504,7 +519,11 @@ __device__ __forceinline__ void decode_split_body(const DecodeArgs& a, const int
   float l_run = 0.f;
   float sl = log2_scale(pos.g);
   int seg_c0 = pos.c;      // first chunk of the current segment
-  OutT* out = static_cast<OutT*>(a.out);
+  // Pairs this wave must merge after its loop (it completed their counters):
+  // at most its first and its last pair.
+  int merge_n = 0;
+  int mb0 = 0, mg0 = 0, mb1 = 0, mg1 = 0;
+  int64_t ms0 = 0, ms1 = 0;
 
   auto flush = [&](const Pos& q) {
     const float l_tot = row_sum4(l_run);
@@ -518,7 +537,8 @@ __device__ __forceinline__ void decode_split_body(const DecodeArgs& a, const int
         for (int t = 0; t < kTiles; ++t) store4<OutT>(dst + 16 * t, acc[t] * f);
       }
     } else {
-      const size_t slot = (size_t)wid + (size_t)q.b * Hkv + q.g;
+      const int pair = q.b * Hkv + q.g;
+      const size_t slot = (size_t)wid + pair;
       if (r < G) {
         float* dst = a.ws_acc + (slot * G + r) * D + 4 * j;
 #pragma unroll
@@ -527,6 +547,25 @@ __device__ __forceinline__ void decode_split_body(const DecodeArgs& a, const int
           a.ws_ml[(slot * G + r) * 2] = m_run;
           a.ws_ml[(slot * G + r) * 2 + 1] = l_tot;
         }
+      }
+      // contributors of this pair: the waves whose ranges meet [s, s + cb)
+      const int64_t s0 = q.x - q.c;
+      const int parts = (int)((s0 + q.cb - 1) / K - s0 / K) + 1;
+      int old = 0;
+      if (lane == 0)   // release: this wave's partial is visible before its count
+        old = __hip_atomic_fetch_add(a.counters + pair, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      old = uni(old);
+      if (old == parts - 1) {
+        if (merge_n == 0) {
+          mb0 = q.b;
+          mg0 = q.g;
+          ms0 = s0;
+        } else {
+          mb1 = q.b;
+          mg1 = q.g;
+          ms1 = s0;
+        }
+        ++merge_n;
       }
     }
 #pragma unroll
@@ -576,149 +615,112 @@ __device__ __forceinline__ void decode_split_body(const DecodeArgs& a, const int
   // computed.  The steady-state loop issues its prefetch unconditionally so
   // that the compiler's load counters wait only for the buffer in use.
   load_q(qop, pos);
-  typename T::K kA, kB;
-  typename T::V vA, vB;
-  Pos pa = pos, pb;
-  issue(kA, vA, qA, pa);
-  int k = 0;
-  for (; k + 2 < nch; k += 2) {
-    pb = advance(pa);
-    issue(kB, vB, qB, pb);
-    compute(kA, vA, qA, pa, false);
-    pa = advance(pb);
+  {
+    typename T::K kA, kB;
+    typename T::V vA, vB;
+    Pos pa = pos, pb;
     issue(kA, vA, qA, pa);
-    compute(kB, vB, qB, pb, false);
+    int k = 0;
+    for (; k + 2 < nch; k += 2) {
+      pb = advance(pa);
+      issue(kB, vB, qB, pb);
+      compute(kA, vA, qA, pa, false);
+      pa = advance(pb);
+      issue(kA, vA, qA, pa);
+      compute(kB, vB, qB, pb, false);
+    }
+    if (k + 1 < nch) {
+      pb = advance(pa);
+      issue(kB, vB, qB, pb);
+      compute(kA, vA, qA, pa, false);
+      compute(kB, vB, qB, pb, true);
+    } else {
+      compute(kA, vA, qA, pa, true);
+    }
   }
-  if (k + 1 < nch) {
-    pb = advance(pa);
-    issue(kB, vB, qB, pb);
-    compute(kA, vA, qA, pa, false);
-    compute(kB, vB, qB, pb, true);
-  } else {
-    compute(kA, vA, qA, pa, true);
+
+  // ---- merges of the pairs whose last contributor this wave was ----
+  if (merge_n == 0) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");   // other waves' partials are visible
+  for (int i = 0; i < merge_n; ++i) {
+    const int b = i ? mb1 : mb0, g = i ? mg1 : mg0;
+    const int64_t s0 = i ? ms1 : ms0;
+    const int pair = b * Hkv + g;
+    const int cb = chunks_of(seq_len(b));
+    const int w_first = (int)(s0 / K);
+    const int w_last = (int)((s0 + cb - 1) / K);
+    const int rr = min(r, G - 1);
+    float M = -INFINITY, L = 0.f;
+    f32x4 o[kTiles];
+#pragma unroll
+    for (int t = 0; t < kTiles; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int w = w_first; w <= w_last; ++w) {
+      const size_t slot = ((size_t)w + pair) * G + rr;
+      const float m_w = a.ws_ml[slot * 2];
+      const float l_w = a.ws_ml[slot * 2 + 1];
+      const float M2 = fmaxf(M, m_w);
+      const float f_old = exp2_fast(M - M2);
+      const float f_new = exp2_fast(m_w - M2);
+      L = L * f_old + l_w * f_new;
+      const float* src = a.ws_acc + slot * D + 4 * j;
+#pragma unroll
+      for (int t = 0; t < kTiles; ++t)
+        o[t] = o[t] * f_old + *reinterpret_cast<const f32x4*>(src + 16 * t) * f_new;
+      M = M2;
+    }
+    if (r < G) {
+      OutT* dst = out + ((size_t)b * Hq + g * G + r) * D + 4 * j;
+      const float f = 1.f / L;
+#pragma unroll
+      for (int t = 0; t < kTiles; ++t) store4<OutT>(dst + 16 * t, o[t] * f);
+    }
+    if (lane == 0) a.counters[pair] = 0;   // ready for the next call
   }
 }
 
-// Two waves per SIMD (at most 256 VGPRs each) are resident together; the
-// float32 path at head_dim 128 needs more registers for its double buffer
-// and runs one wave per SIMD instead of spilling.
 // Tables, lengths and scales are passed again as restrict parameters: nothing
 // the kernel writes aliases them, so their wave-uniform reads go through the
-// scalar cache and never wait behind the vector loads in flight.
+// scalar cache and never wait behind the vector loads in flight.  Two waves
+// per SIMD (at most 256 VGPRs each) are resident together; the float32 path at
+// head_dim 128 needs more registers for its double buffer and runs one wave
+// per SIMD instead of spilling.
 template <int KV, int D>
 __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void decode_split_kernel(DecodeArgs a, const int32_t* __restrict__ tables, const int32_t* __restrict__ lens,
-                         const float* __restrict__ k_scale, const float* __restrict__ v_scale) {
-  decode_split_body<KV, D>(a, tables, lens, k_scale, v_scale);
+void decode_kernel(DecodeArgs a, const int32_t* __restrict__ tables, const int32_t* __restrict__ lens,
+                   const float* __restrict__ k_scale, const float* __restrict__ v_scale) {
+  decode_body<KV, D>(a, tables, lens, k_scale, v_scale);
 }
 
 template <int KV, int D>
-__global__ __launch_bounds__(64 * kDecodeWaves) void decode_split_kernel_wide(
+__global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel_wide(
     DecodeArgs a, const int32_t* __restrict__ tables, const int32_t* __restrict__ lens,
     const float* __restrict__ k_scale, const float* __restrict__ v_scale) {
-  decode_split_body<KV, D>(a, tables, lens, k_scale, v_scale);
-}
-
-// ---------------------------------------------------------------------------
-// Merge kernel: one workgroup per (sequence, kv head) pair.  Pairs finished
-// by one wave return at once; split pairs combine their partials with the
-// same rescaling as the online softmax; empty sequences get zeros.
-// ---------------------------------------------------------------------------
-template <typename OutT, int D>
-__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
-  __shared__ int64_t s_sum[2][4];
-  const int p = blockIdx.x;
-  const int Hkv = a.num_kv_heads;
-  const int b = p / Hkv;
-  const int g = p % Hkv;
-  const int G = a.group;
-  const int tid = threadIdx.x;
-
-  int64_t tot = 0, before = 0;
-  for (int i = tid; i < a.num_seqs; i += 256) {
-    const int cb = chunks_of(clamp_len(a.context_lens[i], a));
-    tot += cb;
-    if (i < b) before += cb;
-  }
-#pragma unroll
-  for (int s = 32; s >= 1; s >>= 1) {
-    tot += __shfl_xor(tot, s);
-    before += __shfl_xor(before, s);
-  }
-  if ((tid & 63) == 0) {
-    s_sum[0][tid >> 6] = tot;
-    s_sum[1][tid >> 6] = before;
-  }
-  __syncthreads();
-  tot = s_sum[0][0] + s_sum[0][1] + s_sum[0][2] + s_sum[0][3];
-  before = s_sum[1][0] + s_sum[1][1] + s_sum[1][2] + s_sum[1][3];
-
-  OutT* out = static_cast<OutT*>(a.out) + ((size_t)b * a.num_q_heads + g * G) * D;
-  const int cb = chunks_of(clamp_len(a.context_lens[b], a));
-  if (cb == 0) {
-    for (int e = tid; e < G * D; e += 256) out[e] = (OutT)0.f;
-    return;
-  }
-  const int64_t C = tot * Hkv;
-  const int64_t K = (C + a.num_workers - 1) / a.num_workers;
-  const int64_t s = before * Hkv + (int64_t)g * cb;
-  const int w_first = (int)(s / K);
-  const int w_last = (int)((s + cb - 1) / K);
-  if (w_first == w_last) return;   // one wave covered the pair and wrote out
-
-  for (int e = tid; e < G * (D / 4); e += 256) {
-    const int h = e / (D / 4);
-    const int q4 = e % (D / 4);
-    float M = -INFINITY;
-    for (int w = w_first; w <= w_last; ++w) M = fmaxf(M, a.ws_ml[(((size_t)w + p) * G + h) * 2]);
-    float L = 0.f;
-    f32x4 o = {0.f, 0.f, 0.f, 0.f};
-    for (int w = w_first; w <= w_last; ++w) {
-      const size_t slot = ((size_t)w + p) * G + h;
-      const float f = exp2_fast(a.ws_ml[slot * 2] - M);
-      L += f * a.ws_ml[slot * 2 + 1];
-      o += f * *reinterpret_cast<const f32x4*>(a.ws_acc + slot * D + 4 * q4);
-    }
-    store4<OutT>(out + (size_t)h * D + 4 * q4, o * (1.f / L));
-  }
+  decode_body<KV, D>(a, tables, lens, k_scale, v_scale);
 }
 
 template <int KV, int D>
-hipError_t launch_split_t(const DecodeArgs& a, hipStream_t stream) {
+hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
   const unsigned grid = (unsigned)(a.num_workers / kDecodeWaves);
   if constexpr (KV == kF32 && D == 128)
-    hipLaunchKernelGGL((decode_split_kernel_wide<KV, D>), dim3(grid), dim3(64 * kDecodeWaves), 0, stream, a,
+    hipLaunchKernelGGL((decode_kernel_wide<KV, D>), dim3(grid), dim3(64 * kDecodeWaves), 0, stream, a,
                        a.block_tables, a.context_lens, a.k_scale, a.v_scale);
   else
-    hipLaunchKernelGGL((decode_split_kernel<KV, D>), dim3(grid), dim3(64 * kDecodeWaves), 0, stream, a,
+    hipLaunchKernelGGL((decode_kernel<KV, D>), dim3(grid), dim3(64 * kDecodeWaves), 0, stream, a,
                        a.block_tables, a.context_lens, a.k_scale, a.v_scale);
-  return hipGetLastError();
-}
-
-template <typename OutT, int D>
-hipError_t launch_merge_t(const DecodeArgs& a, hipStream_t stream) {
-  const unsigned grid = (unsigned)a.num_seqs * (unsigned)a.num_kv_heads;
-  hipLaunchKernelGGL((decode_merge_kernel<OutT, D>), dim3(grid), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_decode_split(const DecodeArgs& a, hipStream_t stream) {
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   if (a.head_dim == 64) {
-    if (a.kv_dtype == kF32) return launch_split_t<kF32, 64>(a, stream);
-    if (a.kv_dtype == kBF16) return launch_split_t<kBF16, 64>(a, stream);
-    return launch_split_t<kFP8, 64>(a, stream);
+    if (a.kv_dtype == kF32) return launch_t<kF32, 64>(a, stream);
+    if (a.kv_dtype == kBF16) return launch_t<kBF16, 64>(a, stream);
+    return launch_t<kFP8, 64>(a, stream);
   }
-  if (a.kv_dtype == kF32) return launch_split_t<kF32, 128>(a, stream);
-  if (a.kv_dtype == kBF16) return launch_split_t<kBF16, 128>(a, stream);
-  return launch_split_t<kFP8, 128>(a, stream);
-}
-
-hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t stream) {
-  const bool f32 = a.kv_dtype == kF32;
-  if (a.head_dim == 64) return f32 ? launch_merge_t<float, 64>(a, stream) : launch_merge_t<__bf16, 64>(a, stream);
-  return f32 ? launch_merge_t<float, 128>(a, stream) : launch_merge_t<__bf16, 128>(a, stream);
+  if (a.kv_dtype == kF32) return launch_t<kF32, 128>(a, stream);
+  if (a.kv_dtype == kBF16) return launch_t<kBF16, 128>(a, stream);
+  return launch_t<kFP8, 128>(a, stream);
 }
 
 }  // namespace pkv

@@ -11,7 +11,7 @@ constexpr int kBlockTokens = 16;    // tokens per cache block
 constexpr int kChunkTokens = 32;    // tokens one wave consumes per step: two blocks
 constexpr int kDecodeWaves = 4;     // worker waves per decode workgroup
 constexpr int kMaxGroup = 16;       // query heads per kv head that one MFMA column tile holds
-constexpr int kWavesPerSimd = 2;    // resident split-kernel waves per SIMD (register budget)
+constexpr int kWavesPerSimd = 2;    // resident decode waves per SIMD (register budget)
 
 enum KvType : int32_t { kF32 = 0, kBF16 = 1, kFP8 = 2 };
 
@@ -26,6 +26,7 @@ struct DecodeArgs {
   void* out;
   float* ws_acc;   // [num_workers + pairs][group][head_dim]  partial accumulators
   float* ws_ml;    // [num_workers + pairs][group][2]         (max in log2 units, sum)
+  int32_t* counters;   // [pairs] partials received; zero between calls
   int32_t num_seqs;
   int32_t num_q_heads;
   int32_t num_kv_heads;
@@ -34,7 +35,7 @@ struct DecodeArgs {
   int32_t max_blocks;
   int32_t num_blocks;
   int32_t max_context_len;
-  int32_t num_workers;   // split-kernel waves; a multiple of kDecodeWaves
+  int32_t num_workers;   // decode worker waves; a multiple of kDecodeWaves
   int32_t kv_dtype;
   float scale;
 };
@@ -54,8 +55,7 @@ struct AppendArgs {
   int32_t kv_dtype;
 };
 
-hipError_t launch_decode_split(const DecodeArgs& a, hipStream_t stream);
-hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
 
 }  // namespace pkv

@@ -58,8 +58,7 @@ def library() -> ctypes.CDLL:
             "pkv_decode_workers": (I32, [D, I32, I32]),
             "pkv_decode_workspace_bytes": (SZ, [D, I32, I32, I32]),
             "pkv_paged_decode": (ctypes.c_int, [D, P, P, P, P, I32, P, I32, I32, F, P, P, SZ, P]),
-            "pkv_paged_decode_split": (ctypes.c_int, [D, P, P, P, P, I32, P, I32, I32, F, I32, P, P, SZ, P]),
-            "pkv_paged_decode_merge": (ctypes.c_int, [D, I32, P, I32, I32, I32, P, P, SZ, P]),
+            "pkv_paged_decode_ex": (ctypes.c_int, [D, P, P, P, P, I32, P, I32, I32, F, I32, P, P, SZ, P]),
             "pkv_strerror": (ctypes.c_char_p, [ctypes.c_int]),
             "pkv_version": (ctypes.c_char_p, []),
         }
@@ -188,52 +187,37 @@ def decode_workspace_bytes(k_pool, v_pool, num_q_heads: int, num_seqs: int, max_
     return int(library().pkv_decode_workspace_bytes(ctypes.byref(desc), num_seqs, max_context_len, num_workers))
 
 
-def _workspace(nbytes: int, like: torch.Tensor, workspace: Optional[torch.Tensor]):
-    if nbytes == 0:
-        return workspace, 0
-    if workspace is None:
-        workspace = torch.empty(nbytes, dtype=torch.uint8, device=like.device)
-    if workspace.device.type != "cuda" or workspace.numel() * workspace.element_size() < nbytes:
-        raise ValueError(f"workspace must be a device buffer of at least {nbytes} bytes")
-    return workspace, workspace.numel() * workspace.element_size()
+def new_workspace(nbytes: int, device) -> torch.Tensor:
+    """A decode workspace: zero-filled once (its counters must start at zero;
+    every decode call leaves them zero again, so it can be reused)."""
+    return torch.zeros(max(int(nbytes), 16), dtype=torch.uint8, device=device)
 
 
 def paged_decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
                  block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
                  out: Optional[torch.Tensor] = None, k_scale: Optional[torch.Tensor] = None,
                  v_scale: Optional[torch.Tensor] = None, max_context_len: Optional[int] = None,
-                 workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """Decode attention of one query per sequence over its paged K/V; returns ``out``."""
+                 workspace: Optional[torch.Tensor] = None, num_workers: int = 0,
+                 stream=None) -> torch.Tensor:
+    """Decode attention of one query per sequence over its paged K/V; returns ``out``.
+
+    ``workspace`` (optional) must come from ``new_workspace`` (or be zero-filled
+    before its first use) and hold ``decode_workspace_bytes`` bytes for the same
+    shape and ``num_workers``; calls sharing it must run on one stream.
+    """
     desc, out = _decode_checks(q, k_pool, v_pool, block_tables, context_lens, k_scale, v_scale, out)
     mctx = _max_ctx(block_tables, max_context_len)
     lib = library()
-    need = lib.pkv_decode_workspace_bytes(ctypes.byref(desc), q.shape[0], mctx, 0)
-    workspace, wbytes = _workspace(need, q, workspace)
-    _check(lib.pkv_paged_decode(ctypes.byref(desc), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
-                                block_tables.shape[1], _ptr(context_lens), q.shape[0], mctx, float(scale),
-                                _ptr(out), _ptr(workspace), wbytes, _stream(stream)), "pkv_paged_decode")
+    need = lib.pkv_decode_workspace_bytes(ctypes.byref(desc), q.shape[0], mctx, int(num_workers))
+    if need == 0 and q.shape[0] > 0:
+        _check(-1, "pkv_decode_workspace_bytes")
+    if workspace is None:
+        workspace = new_workspace(need, q.device)
+    wbytes = workspace.numel() * workspace.element_size()
+    if workspace.device.type != "cuda" or wbytes < need:
+        raise ValueError(f"workspace must be a device buffer of at least {need} bytes")
+    _check(lib.pkv_paged_decode_ex(ctypes.byref(desc), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
+                                   block_tables.shape[1], _ptr(context_lens), q.shape[0], mctx, float(scale),
+                                   int(num_workers), _ptr(out), _ptr(workspace), wbytes, _stream(stream)),
+           "pkv_paged_decode_ex")
     return out
-
-
-def paged_decode_split(q, k_pool, v_pool, block_tables, context_lens, scale, num_workers: int,
-                       out, workspace, k_scale=None, v_scale=None, max_context_len=None,
-                       stream=None) -> None:
-    """First kernel of ``paged_decode`` with an explicit worker-wave count."""
-    desc, out = _decode_checks(q, k_pool, v_pool, block_tables, context_lens, k_scale, v_scale, out)
-    mctx = _max_ctx(block_tables, max_context_len)
-    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(library().pkv_paged_decode_split(
-        ctypes.byref(desc), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables), block_tables.shape[1],
-        _ptr(context_lens), q.shape[0], mctx, float(scale), int(num_workers), _ptr(out), _ptr(workspace),
-        wbytes, _stream(stream)), "pkv_paged_decode_split")
-
-
-def paged_decode_merge(q, k_pool, v_pool, block_tables, context_lens, num_workers: int, out, workspace,
-                       k_scale=None, v_scale=None, max_context_len=None, stream=None) -> None:
-    """Second kernel of ``paged_decode``: merge the split pairs' partials into ``out``."""
-    desc, out = _decode_checks(q, k_pool, v_pool, block_tables, context_lens, k_scale, v_scale, out)
-    mctx = _max_ctx(block_tables, max_context_len)
-    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(library().pkv_paged_decode_merge(
-        ctypes.byref(desc), block_tables.shape[1], _ptr(context_lens), q.shape[0], mctx, int(num_workers),
-        _ptr(out), _ptr(workspace), wbytes, _stream(stream)), "pkv_paged_decode_merge")

@@ -37,7 +37,7 @@ class Dev:
         ops.kv_append(self.k_new, self.v_new, self.slots, self.k_pool, self.v_pool,
                       self.k_scale, self.v_scale)
 
-    def decode(self, after_append=False, k_pool=None, v_pool=None, tables=None, workers=None):
+    def decode(self, after_append=False, k_pool=None, v_pool=None, tables=None, workers=0, workspace=None):
         wl = self.wl
         lens = self.lens_after if after_append else self.lens
         tables = (self.tables_after if after_append else self.tables) if tables is None else tables
@@ -45,18 +45,9 @@ class Dev:
         mctx = int(host_lens.max()) if host_lens.numel() else 0
         kp = self.k_pool if k_pool is None else k_pool
         vp = self.v_pool if v_pool is None else v_pool
-        if workers is None:
-            return ops.paged_decode(self.q, kp, vp, tables, lens, wl.scale, k_scale=self.k_scale,
-                                    v_scale=self.v_scale, max_context_len=mctx)
-        out = torch.empty_like(self.q)
-        nbytes = ops.decode_workspace_bytes(kp, vp, self.q.shape[1], self.q.shape[0], mctx, workers,
-                                            self.k_scale, self.v_scale)
-        ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=self.q.device)
-        ops.paged_decode_split(self.q, kp, vp, tables, lens, wl.scale, workers, out, ws,
-                               self.k_scale, self.v_scale, mctx)
-        ops.paged_decode_merge(self.q, kp, vp, tables, lens, workers, out, ws,
-                               self.k_scale, self.v_scale, mctx)
-        return out
+        return ops.paged_decode(self.q, kp, vp, tables, lens, wl.scale, k_scale=self.k_scale,
+                                v_scale=self.v_scale, max_context_len=mctx, num_workers=workers,
+                                workspace=workspace)
 
 
 def host(t: torch.Tensor) -> np.ndarray:

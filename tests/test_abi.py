@@ -27,9 +27,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for required in ("pkv_kv_append", "pkv_paged_decode", "pkv_paged_decode_split",
-                     "pkv_paged_decode_merge", "pkv_decode_workspace_bytes", "pkv_decode_workers",
-                     "pkv_strerror"):
+    for required in ("pkv_kv_append", "pkv_paged_decode", "pkv_paged_decode_ex",
+                     "pkv_decode_workspace_bytes", "pkv_decode_workers", "pkv_strerror"):
         assert required in names
 
 
@@ -83,32 +82,31 @@ def test_null_and_size_errors():
                                 FAKE, None, 0, None) == EINVAL
     assert lib.pkv_paged_decode(ctypes.byref(d), FAKE + 8, FAKE, FAKE, FAKE, 4, FAKE, 2, 64, 0.1,
                                 FAKE, None, 0, None) == EINVAL          # misaligned q
-    assert lib.pkv_paged_decode_split(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 64, 0.1,
+    assert lib.pkv_paged_decode_ex(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 64, 0.1,
                                       6, FAKE, None, 0, None) == EINVAL    # workers not a multiple of 4
-    assert lib.pkv_paged_decode_split(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 64, 0.1,
+    assert lib.pkv_paged_decode_ex(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 64, 0.1,
                                       -4, FAKE, None, 0, None) == EINVAL   # negative workers
 
 
 def test_workspace_sizing_and_check():
     lib = ops.library()
     d = _desc()                                 # 8 q heads / 2 kv heads: group 4, head_dim 128
-    # (workers + seqs * kv heads) partial states: acc rows rounded to 256 B, then (max, sum)
+    # (workers + seqs * kv heads) partial states: acc rows, (max, sum) rows and one
+    # counter per pair, each region rounded up to 256 bytes
     rows = (64 + 4 * 2) * 4
-    acc = -(-rows * 128 * 4 // 256) * 256
+    up = lambda n: -(-n // 256) * 256
     need = lib.pkv_decode_workspace_bytes(ctypes.byref(d), 4, 150, 64)
-    assert need == acc + rows * 2 * 4
+    assert need == up(rows * 128 * 4) + up(rows * 2 * 4) + up(4 * 2 * 4)
     assert lib.pkv_decode_workspace_bytes(ctypes.byref(d), 4, 150, 6) == 0     # bad worker count
-    st = lib.pkv_paged_decode_split(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 16, FAKE, 4, 150, 0.1,
-                                    64, FAKE, FAKE, need - 1, None)
+    st = lib.pkv_paged_decode_ex(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 16, FAKE, 4, 150, 0.1,
+                                 64, FAKE, FAKE, need - 1, None)
     assert st == EWORKSPACE
-    st = lib.pkv_paged_decode_split(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 16, FAKE, 4, 150, 0.1,
-                                    64, FAKE, None, need, None)
-    assert st == EWORKSPACE
-    st = lib.pkv_paged_decode_merge(ctypes.byref(d), 16, FAKE, 4, 150, 64, FAKE, None, 0, None)
+    st = lib.pkv_paged_decode_ex(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 16, FAKE, 4, 150, 0.1,
+                                 64, FAKE, None, need, None)
     assert st == EWORKSPACE
     # zero sequences: nothing to do, nothing launched
-    assert lib.pkv_paged_decode_split(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 16, FAKE, 0, 150, 0.1,
-                                      64, FAKE, None, 0, None) == 0
+    assert lib.pkv_paged_decode_ex(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 16, FAKE, 0, 150, 0.1,
+                                   64, FAKE, None, 0, None) == 0
 
 
 def test_strerror_and_version():

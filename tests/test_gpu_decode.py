@@ -47,8 +47,8 @@ def test_small_shapes(kv_dtype, D, G):
 @pytest.mark.parametrize("workers", [4, 8, 12, 64, 512, 2048])
 @pytest.mark.parametrize("kv_dtype", ["f32", "bf16", "fp8"])
 def test_explicit_workers(kv_dtype, workers):
-    """Any worker count (so any split points between waves, merged by the
-    second kernel) gives the same answer within tolerance."""
+    """Any worker count (so any split points between waves, merged by each
+    split pair's last contributor) gives the same answer within tolerance."""
     wl = build_workload("split", [1, 33, 100, 257, 700, 2049], 16, 4, 128 if kv_dtype != "f32" else 64,
                         kv_dtype, seed=workers)
     out = Dev(wl).decode(workers=workers)
@@ -61,7 +61,7 @@ def test_runs_of_one_chunk_sequences():
     lens = [1, 5, 32, 0, 17, 31, 2, 0, 9, 32, 33, 3]
     for kv_dtype in ("bf16", "fp8"):
         wl = build_workload("short", lens, 8, 2, 128, kv_dtype, seed=9)
-        for workers in (None, 4, 8):
+        for workers in (0, 4, 8):
             out = Dev(wl).decode(workers=workers)
             assert_close(out, oracle_full(wl), kv_dtype)
 

@@ -131,14 +131,14 @@ def test_poisoned_tails_and_stale_table_entries(kv_dtype):
 
 
 @pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
-def test_two_kernel_form_equals_fused_call(kv_dtype):
+def test_explicit_default_worker_count_is_bit_identical(kv_dtype):
     wl = _wl(kv_dtype)
     dev = Dev(wl)
-    fused = dev.decode()
+    default = dev.decode()
     workers = ops.decode_workers(dev.k_pool, dev.v_pool, 8, len(LENS), max(LENS), dev.k_scale, dev.v_scale)
-    split = dev.decode(workers=workers)
-    assert np.array_equal(_bits(split), _bits(fused))
-    assert_close(split, oracle_full(wl), kv_dtype)
+    explicit = dev.decode(workers=workers)
+    assert np.array_equal(_bits(explicit), _bits(default))
+    assert_close(explicit, oracle_full(wl), kv_dtype)
 
 
 def test_repeated_calls_are_deterministic():
@@ -147,3 +147,23 @@ def test_repeated_calls_are_deterministic():
     a = dev.decode()
     b = dev.decode()
     assert np.array_equal(_bits(a), _bits(b))
+
+
+def test_reused_workspace_stays_valid():
+    """One workspace across many calls and shapes: every call leaves its
+    counters at zero, so later calls merge correctly."""
+    big = build_workload("ws-a", LENS, 8, 2, 128, "bf16", seed=5)
+    small = build_workload("ws-b", [40, 3000, 7], 8, 2, 128, "bf16", seed=6)
+    dev_big, dev_small = Dev(big), Dev(small)
+    nbytes = max(ops.decode_workspace_bytes(dev_big.k_pool, dev_big.v_pool, 8, len(LENS), max(LENS), 8),
+                 ops.decode_workspace_bytes(dev_small.k_pool, dev_small.v_pool, 8, 3, 3000, 8))
+    ws = ops.new_workspace(nbytes, dev_big.q.device)
+    ref_big, ref_small = oracle_full(big), oracle_full(small)
+    first = None
+    for i in range(6):
+        out = dev_big.decode(workers=8, workspace=ws)
+        if first is None:
+            first = _bits(out)
+        assert np.array_equal(_bits(out), first)
+        assert_close(out, ref_big, "bf16")
+        assert_close(dev_small.decode(workers=8, workspace=ws), ref_small, "bf16")
