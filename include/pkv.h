@@ -108,8 +108,9 @@ int32_t pkv_decode_workers(const pkv_cache_desc* desc, int32_t num_seqs,
 
 /* Device workspace bytes a decode of this shape needs: (num_workers +
  * num_seqs * num_kv_heads) partial states of group * (head_dim + 2) floats,
- * then one int32 counter per (sequence, kv head) pair.  num_workers == 0 means
- * pkv_decode_workers(...).  Returns 0 on bad arguments. */
+ * then one (first wave, parts) record of two int32 per (sequence, kv head)
+ * pair.  num_workers == 0 means pkv_decode_workers(...).  Returns 0 on bad
+ * arguments. */
 size_t pkv_decode_workspace_bytes(const pkv_cache_desc* desc, int32_t num_seqs,
                                   int32_t max_context_len, int32_t num_workers);
 
@@ -123,17 +124,16 @@ size_t pkv_decode_workspace_bytes(const pkv_cache_desc* desc, int32_t num_seqs,
  * 16 * max_blocks_per_seq); block ids are clamped into [0, num_blocks).
  * Accumulation is float32; out is rounded once to q_dtype (nearest even).
  *
- * One kernel launch.  The batch's 32-token chunks of every (sequence, kv head)
- * pair, pairs in sequence-major order, are cut into equal contiguous ranges,
- * one per worker wave; each wave runs section 3's online softmax over its
- * range.  A pair split between waves is finished by its last contributor,
- * which merges the float32 partial states (running max, sum, unnormalised
- * accumulator) with the same rescale by exp(m_old - m_new).
+ * Two kernels on `stream`.  The batch's 32-token chunks of every (sequence,
+ * kv head) pair, pairs in sequence-major order, are cut into equal contiguous
+ * ranges, one per worker wave; each wave runs section 3's online softmax over
+ * its range and finishes every pair it covers completely.  For a pair split
+ * between waves each wave leaves a float32 partial state (running max, sum,
+ * unnormalised accumulator); the second kernel merges them with the same
+ * rescale by exp(m_old - m_new) and writes zeros for empty sequences.
  *   workspace  device buffer of pkv_decode_workspace_bytes(..., 0) bytes,
- *              16-byte aligned.  Its counter region must be zero before the
- *              first call (zero-fill the whole buffer once); every call
- *              leaves it zero again.  The rest is scratch.  Calls that share
- *              one workspace must be ordered (one stream). */
+ *              16-byte aligned; scratch, needs no initialisation.  Calls that
+ *              share one workspace must be ordered (one stream). */
 int pkv_paged_decode(const pkv_cache_desc* desc, const void* q, const void* k_pool,
                      const void* v_pool, const int32_t* block_tables,
                      int32_t max_blocks_per_seq, const int32_t* context_lens,

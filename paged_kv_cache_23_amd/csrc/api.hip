@@ -74,8 +74,9 @@ int32_t resolve_workers(const pkv_cache_desc* d, int32_t num_seqs, int32_t max_c
   return workers;
 }
 
-// Workspace: partial accumulators, then (max, sum) pairs, then one counter
-// per (sequence, kv head) pair; each region starts on a 256-byte boundary.
+// Workspace: partial accumulators, then (max, sum) pairs, then one (first
+// wave, parts) record per (sequence, kv head) pair; each region starts on a
+// 256-byte boundary.
 size_t align_up(size_t n) { return (n + kWsAlign - 1) / kWsAlign * kWsAlign; }
 
 size_t partial_rows(const pkv_cache_desc* d, int32_t num_seqs, int32_t workers) {
@@ -92,7 +93,7 @@ size_t ml_bytes(const pkv_cache_desc* d, int32_t num_seqs, int32_t workers) {
 
 size_t workspace_bytes(const pkv_cache_desc* d, int32_t num_seqs, int32_t workers) {
   return acc_bytes(d, num_seqs, workers) + ml_bytes(d, num_seqs, workers) +
-         align_up((size_t)num_seqs * d->num_kv_heads * sizeof(int32_t));
+         align_up((size_t)num_seqs * d->num_kv_heads * 2 * sizeof(int32_t));
 }
 
 int check_decode_args(const pkv_cache_desc* d, const void* q, const void* k_pool, const void* v_pool,
@@ -133,7 +134,7 @@ DecodeArgs make_args(const pkv_cache_desc* d, const void* q, const void* k_pool,
   char* ws = static_cast<char*>(workspace);
   a.ws_acc = reinterpret_cast<float*>(ws);
   a.ws_ml = reinterpret_cast<float*>(ws + acc_bytes(d, num_seqs, workers));
-  a.counters = reinterpret_cast<int32_t*>(ws + acc_bytes(d, num_seqs, workers) + ml_bytes(d, num_seqs, workers));
+  a.pair_meta = reinterpret_cast<int2*>(ws + acc_bytes(d, num_seqs, workers) + ml_bytes(d, num_seqs, workers));
   return a;
 }
 

@@ -1,4 +1,4 @@
-// Paged decode attention for gfx950: one stream-K kernel.
+// Paged decode attention for gfx950: stream-K split kernel + merge kernel.
 //
 // What is computed (Habr KV-Cache article, habr.com/ru/articles/1021832):
 //  - section 3 "Recalling FlashAttention": exact softmax(q K^T * scale) V,
@@ -17,8 +17,8 @@
 // GPU takes an equal contiguous range of that list (stream-K style), so all
 // waves stream the same bytes; it keeps a running max / sum / accumulator per
 // pair segment for the pair's whole query group.  A pair that one wave covers
-// completely is finished by that wave; a pair split between waves is merged
-// by whichever of its contributors finishes last (see decode_body).
+// completely is finished by that wave; a pair split between waves leaves one
+// float32 partial per wave, combined by decode_merge_kernel.
 //
 // Tile math (CDNA4 MFMA, 64-lane waves).  Scores are computed transposed,
 // S^T[token][head] = K q^T, so that the MFMA output layout (lane l holds rows
@@ -364,7 +364,7 @@ struct Pos {
 };
 
 // ---------------------------------------------------------------------------
-// Decode kernel.
+// Split kernel.
 //
 // The batch's work is the list of 32-token chunks of every (sequence, kv head)
 // pair, pairs ordered sequence-major.  Worker wave w (one per SIMD slot of the
@@ -375,13 +375,11 @@ struct Pos {
 // pair shared with other waves (at most the first and the last pair of a
 // range) leaves a float32 partial (max, sum, unnormalised accumulator) in slot
 // w + pair of the workspace; slots are unique because ranges are contiguous
-// and ordered.  Each contributor then bumps the pair's counter (agent-scope
-// release), and the one that completes the count (acquire) merges all the
-// pair's partials after its own streaming loop and resets the counter to zero
-// for the next call.  Nobody waits on anybody, so every wave exits.
+// and ordered.  The wave that holds a pair's first chunk records the pair's
+// first wave and number of parts for the merge kernel.
 // ---------------------------------------------------------------------------
 template <int KV, int D>
-__device__ __forceinline__ void decode_body(const DecodeArgs& a, const int32_t* __restrict__ tables,
+__device__ __forceinline__ void split_body(const DecodeArgs& a, const int32_t* __restrict__ tables,
                                             const int32_t* __restrict__ lens, const float* __restrict__ k_scale,
                                             const float* __restrict__ v_scale) {
   using T = typename TileOf<KV, D>::type;
@@ -403,20 +401,13 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, const int32_t* 
 
   auto seq_len = [&](int b) -> int { return uni(clamp_len(lens[uni(b)], a)); };
 
-  // ---- chunk totals; wave 0 also writes the zero output of empty sequences ----
+  // ---- chunk totals over the batch ----
   int64_t total = 0;   // chunks per kv head over the batch
   int cb_lane = 0;     // chunks of sequence `lane` (kept when the batch has <= 64 sequences)
   for (int base = 0; base < B; base += 64) {
     const int bi = base + lane;
-    const int n = bi < B ? clamp_len(lens[bi], a) : 1;
-    cb_lane = chunks_of(n);
-    total += uni(wave_sum(bi < B ? cb_lane : 0));
-    if (wid == 0) {
-      for (uint64_t empty = __builtin_amdgcn_ballot_w64(n == 0); empty; empty &= empty - 1) {
-        const int b = uni(base + __builtin_ctzll(empty));
-        for (int e = lane; e < Hq * D; e += 64) out[(size_t)b * Hq * D + e] = (OutT)0.f;
-      }
-    }
+    cb_lane = bi < B ? chunks_of(clamp_len(lens[bi], a)) : 0;
+    total += uni(wave_sum(cb_lane));
   }
   const int64_t C = total * Hkv;
   const int64_t K = (C + W - 1) / W;
@@ -519,17 +510,17 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, const int32_t* 
   float l_run = 0.f;
   float sl = log2_scale(pos.g);
   int seg_c0 = pos.c;      // first chunk of the current segment
-  // Pairs this wave must merge after its loop (it completed their counters):
-  // at most its first and its last pair.
-  int merge_n = 0;
-  int mb0 = 0, mg0 = 0, mb1 = 0, mg1 = 0;
-  int64_t ms0 = 0, ms1 = 0;
 
   auto flush = [&](const Pos& q) {
     const float l_tot = row_sum4(l_run);
     const float mul = out_scale(q.g);
-    const bool complete = seg_c0 == 0 && q.c == q.cb - 1;
-    if (complete) {
+    const int pair = q.b * Hkv + q.g;
+    if (seg_c0 == 0) {   // this wave holds the pair's first chunk: record its parts
+      const int64_t s0 = q.x - q.c;
+      const int parts = (int)((s0 + q.cb - 1) / K - s0 / K) + 1;
+      if (lane == 0) a.pair_meta[pair] = int2{wid, parts};
+    }
+    if (seg_c0 == 0 && q.c == q.cb - 1) {   // the whole pair: finish it here
       if (r < G) {
         OutT* dst = out + ((size_t)q.b * Hq + q.g * G + r) * D + 4 * j;
         const float f = mul / l_tot;
@@ -537,7 +528,6 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, const int32_t* 
         for (int t = 0; t < kTiles; ++t) store4<OutT>(dst + 16 * t, acc[t] * f);
       }
     } else {
-      const int pair = q.b * Hkv + q.g;
       const size_t slot = (size_t)wid + pair;
       if (r < G) {
         float* dst = a.ws_acc + (slot * G + r) * D + 4 * j;
@@ -547,25 +537,6 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, const int32_t* 
           a.ws_ml[(slot * G + r) * 2] = m_run;
           a.ws_ml[(slot * G + r) * 2 + 1] = l_tot;
         }
-      }
-      // contributors of this pair: the waves whose ranges meet [s, s + cb)
-      const int64_t s0 = q.x - q.c;
-      const int parts = (int)((s0 + q.cb - 1) / K - s0 / K) + 1;
-      int old = 0;
-      if (lane == 0)   // release: this wave's partial is visible before its count
-        old = __hip_atomic_fetch_add(a.counters + pair, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-      old = uni(old);
-      if (old == parts - 1) {
-        if (merge_n == 0) {
-          mb0 = q.b;
-          mg0 = q.g;
-          ms0 = s0;
-        } else {
-          mb1 = q.b;
-          mg1 = q.g;
-          ms1 = s0;
-        }
-        ++merge_n;
       }
     }
 #pragma unroll
@@ -639,43 +610,6 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, const int32_t* 
     }
   }
 
-  // ---- merges of the pairs whose last contributor this wave was ----
-  if (merge_n == 0) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");   // other waves' partials are visible
-  for (int i = 0; i < merge_n; ++i) {
-    const int b = i ? mb1 : mb0, g = i ? mg1 : mg0;
-    const int64_t s0 = i ? ms1 : ms0;
-    const int pair = b * Hkv + g;
-    const int cb = chunks_of(seq_len(b));
-    const int w_first = (int)(s0 / K);
-    const int w_last = (int)((s0 + cb - 1) / K);
-    const int rr = min(r, G - 1);
-    float M = -INFINITY, L = 0.f;
-    f32x4 o[kTiles];
-#pragma unroll
-    for (int t = 0; t < kTiles; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int w = w_first; w <= w_last; ++w) {
-      const size_t slot = ((size_t)w + pair) * G + rr;
-      const float m_w = a.ws_ml[slot * 2];
-      const float l_w = a.ws_ml[slot * 2 + 1];
-      const float M2 = fmaxf(M, m_w);
-      const float f_old = exp2_fast(M - M2);
-      const float f_new = exp2_fast(m_w - M2);
-      L = L * f_old + l_w * f_new;
-      const float* src = a.ws_acc + slot * D + 4 * j;
-#pragma unroll
-      for (int t = 0; t < kTiles; ++t)
-        o[t] = o[t] * f_old + *reinterpret_cast<const f32x4*>(src + 16 * t) * f_new;
-      M = M2;
-    }
-    if (r < G) {
-      OutT* dst = out + ((size_t)b * Hq + g * G + r) * D + 4 * j;
-      const float f = 1.f / L;
-#pragma unroll
-      for (int t = 0; t < kTiles; ++t) store4<OutT>(dst + 16 * t, o[t] * f);
-    }
-    if (lane == 0) a.counters[pair] = 0;   // ready for the next call
-  }
 }
 
 // Tables, lengths and scales are passed again as restrict parameters: nothing
@@ -686,41 +620,99 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, const int32_t* 
 // per SIMD instead of spilling.
 template <int KV, int D>
 __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void decode_kernel(DecodeArgs a, const int32_t* __restrict__ tables, const int32_t* __restrict__ lens,
-                   const float* __restrict__ k_scale, const float* __restrict__ v_scale) {
-  decode_body<KV, D>(a, tables, lens, k_scale, v_scale);
+void decode_split_kernel(DecodeArgs a, const int32_t* __restrict__ tables, const int32_t* __restrict__ lens,
+                         const float* __restrict__ k_scale, const float* __restrict__ v_scale) {
+  split_body<KV, D>(a, tables, lens, k_scale, v_scale);
 }
 
 template <int KV, int D>
-__global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel_wide(
+__global__ __launch_bounds__(64 * kDecodeWaves) void decode_split_kernel_wide(
     DecodeArgs a, const int32_t* __restrict__ tables, const int32_t* __restrict__ lens,
     const float* __restrict__ k_scale, const float* __restrict__ v_scale) {
-  decode_body<KV, D>(a, tables, lens, k_scale, v_scale);
+  split_body<KV, D>(a, tables, lens, k_scale, v_scale);
+}
+
+// ---------------------------------------------------------------------------
+// Merge kernel: one workgroup per (sequence, kv head) pair.  Reads the pair's
+// length and the split kernel's record of it in one round trip; a pair one
+// wave finished returns at once, an empty sequence gets zeros, a split pair
+// combines its partials with the online-softmax rescale (second round trip).
+// ---------------------------------------------------------------------------
+template <typename OutT, int D>
+__global__ __launch_bounds__(128) void decode_merge_kernel(DecodeArgs a, const int32_t* __restrict__ lens,
+                                                           const int2* __restrict__ meta) {
+  const int pair = blockIdx.x;
+  const int Hkv = a.num_kv_heads;
+  const int b = pair / Hkv;
+  const int g = pair % Hkv;
+  const int G = a.group;
+  const int n = clamp_len(lens[b], a);
+  const int2 m = meta[pair];
+  OutT* out = static_cast<OutT*>(a.out) + ((size_t)b * a.num_q_heads + g * G) * D;
+  if (n == 0) {
+    for (int e = threadIdx.x; e < G * D; e += 128) out[e] = (OutT)0.f;
+    return;
+  }
+  if (m.y <= 1) return;   // one wave covered the pair and wrote its output
+  for (int e = threadIdx.x; e < G * (D / 4); e += 128) {
+    const int h = e / (D / 4);
+    const int q4 = e % (D / 4);
+    float M = -INFINITY, L = 0.f;
+    f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int w = m.x; w < m.x + m.y; ++w) {
+      const size_t slot = ((size_t)w + pair) * G + h;
+      const float m_w = a.ws_ml[slot * 2];
+      const float l_w = a.ws_ml[slot * 2 + 1];
+      const f32x4 acc_w = *reinterpret_cast<const f32x4*>(a.ws_acc + slot * D + 4 * q4);
+      const float M2 = fmaxf(M, m_w);
+      const float f_old = exp2_fast(M - M2);
+      const float f_new = exp2_fast(m_w - M2);
+      L = L * f_old + l_w * f_new;
+      o = o * f_old + acc_w * f_new;
+      M = M2;
+    }
+    store4<OutT>(out + (size_t)h * D + 4 * q4, o * (1.f / L));
+  }
 }
 
 template <int KV, int D>
-hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
+hipError_t launch_split_t(const DecodeArgs& a, hipStream_t stream) {
   const unsigned grid = (unsigned)(a.num_workers / kDecodeWaves);
   if constexpr (KV == kF32 && D == 128)
-    hipLaunchKernelGGL((decode_kernel_wide<KV, D>), dim3(grid), dim3(64 * kDecodeWaves), 0, stream, a,
+    hipLaunchKernelGGL((decode_split_kernel_wide<KV, D>), dim3(grid), dim3(64 * kDecodeWaves), 0, stream, a,
                        a.block_tables, a.context_lens, a.k_scale, a.v_scale);
   else
-    hipLaunchKernelGGL((decode_kernel<KV, D>), dim3(grid), dim3(64 * kDecodeWaves), 0, stream, a,
+    hipLaunchKernelGGL((decode_split_kernel<KV, D>), dim3(grid), dim3(64 * kDecodeWaves), 0, stream, a,
                        a.block_tables, a.context_lens, a.k_scale, a.v_scale);
+  return hipGetLastError();
+}
+
+template <typename OutT, int D>
+hipError_t launch_merge_t(const DecodeArgs& a, hipStream_t stream) {
+  const unsigned grid = (unsigned)a.num_seqs * (unsigned)a.num_kv_heads;
+  hipLaunchKernelGGL((decode_merge_kernel<OutT, D>), dim3(grid), dim3(128), 0, stream, a, a.context_lens,
+                     a.pair_meta);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
+  hipError_t e;
   if (a.head_dim == 64) {
-    if (a.kv_dtype == kF32) return launch_t<kF32, 64>(a, stream);
-    if (a.kv_dtype == kBF16) return launch_t<kBF16, 64>(a, stream);
-    return launch_t<kFP8, 64>(a, stream);
+    if (a.kv_dtype == kF32) e = launch_split_t<kF32, 64>(a, stream);
+    else if (a.kv_dtype == kBF16) e = launch_split_t<kBF16, 64>(a, stream);
+    else e = launch_split_t<kFP8, 64>(a, stream);
+  } else {
+    if (a.kv_dtype == kF32) e = launch_split_t<kF32, 128>(a, stream);
+    else if (a.kv_dtype == kBF16) e = launch_split_t<kBF16, 128>(a, stream);
+    else e = launch_split_t<kFP8, 128>(a, stream);
   }
-  if (a.kv_dtype == kF32) return launch_t<kF32, 128>(a, stream);
-  if (a.kv_dtype == kBF16) return launch_t<kBF16, 128>(a, stream);
-  return launch_t<kFP8, 128>(a, stream);
+  if (e != hipSuccess) return e;
+  const bool f32 = a.kv_dtype == kF32;
+  if (a.head_dim == 64) return f32 ? launch_merge_t<float, 64>(a, stream) : launch_merge_t<__bf16, 64>(a, stream);
+  return f32 ? launch_merge_t<float, 128>(a, stream) : launch_merge_t<__bf16, 128>(a, stream);
 }
 
 }  // namespace pkv

@@ -26,7 +26,7 @@ struct DecodeArgs {
   void* out;
   float* ws_acc;   // [num_workers + pairs][group][head_dim]  partial accumulators
   float* ws_ml;    // [num_workers + pairs][group][2]         (max in log2 units, sum)
-  int32_t* counters;   // [pairs] partials received; zero between calls
+  int2* pair_meta;      // [pairs] (first wave, parts) of each non-empty pair
   int32_t num_seqs;
   int32_t num_q_heads;
   int32_t num_kv_heads;
@@ -55,6 +55,7 @@ struct AppendArgs {
   int32_t kv_dtype;
 };
 
+// Split kernel then merge kernel, on `stream`.
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
 

@@ -188,9 +188,8 @@ def decode_workspace_bytes(k_pool, v_pool, num_q_heads: int, num_seqs: int, max_
 
 
 def new_workspace(nbytes: int, device) -> torch.Tensor:
-    """A decode workspace: zero-filled once (its counters must start at zero;
-    every decode call leaves them zero again, so it can be reused)."""
-    return torch.zeros(max(int(nbytes), 16), dtype=torch.uint8, device=device)
+    """A decode workspace (scratch; reusable by calls ordered on one stream)."""
+    return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
 
 
 def paged_decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
@@ -201,9 +200,8 @@ def paged_decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
                  stream=None) -> torch.Tensor:
     """Decode attention of one query per sequence over its paged K/V; returns ``out``.
 
-    ``workspace`` (optional) must come from ``new_workspace`` (or be zero-filled
-    before its first use) and hold ``decode_workspace_bytes`` bytes for the same
-    shape and ``num_workers``; calls sharing it must run on one stream.
+    ``workspace`` (optional) must hold ``decode_workspace_bytes`` bytes for the
+    same shape and ``num_workers``; calls sharing it must run on one stream.
     """
     desc, out = _decode_checks(q, k_pool, v_pool, block_tables, context_lens, k_scale, v_scale, out)
     mctx = _max_ctx(block_tables, max_context_len)
