@@ -99,9 +99,8 @@ int pkv_kv_append(const pkv_cache_desc* desc, const void* k_new, const void* v_n
                   void* v_pool, void* stream);
 
 /* Number of worker waves pkv_paged_decode uses for this batch shape on the
- * current device: one per SIMD slot the kernel's register budget allows
- * (2 per SIMD, 8 per compute unit), fewer for batches with fewer 32-token
- * chunks; always a multiple of 4.  Returns a negative status on bad arguments
+ * current device: one per SIMD (4 per compute unit), fewer for batches with
+ * fewer 32-token chunks; always a multiple of 4.  Returns a negative status on bad arguments
  * or when no device is current. */
 int32_t pkv_decode_workers(const pkv_cache_desc* desc, int32_t num_seqs,
                            int32_t max_context_len);

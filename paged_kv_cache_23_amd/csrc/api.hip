@@ -54,9 +54,10 @@ int device_cus() {
   return cus;
 }
 
-// Default number of split-kernel worker waves: every SIMD slot the register
-// budget allows (2 waves per SIMD, 4 SIMDs per compute unit), all resident at
-// once; no more than there can be 32-token chunks in the batch.
+// Default number of worker waves: one per SIMD (4 per compute unit), all
+// resident at once; no more than there can be 32-token chunks in the batch.
+// With two per SIMD the second wave mostly waits for the first one's memory
+// traffic and only adds split pairs (measured slower on MI355X).
 int32_t default_workers(const pkv_cache_desc* d, int32_t num_seqs, int32_t max_ctx) {
   const int cus = device_cus();
   if (cus <= 0) return PKV_ELAUNCH;

@@ -399,16 +399,20 @@ __device__ __forceinline__ void split_body(const DecodeArgs& a, const int32_t* _
   const int Hq = a.num_q_heads;
   OutT* out = static_cast<OutT*>(a.out);
 
-  auto seq_len = [&](int b) -> int { return uni(clamp_len(lens[uni(b)], a)); };
-
   // ---- chunk totals over the batch ----
   int64_t total = 0;   // chunks per kv head over the batch
-  int cb_lane = 0;     // chunks of sequence `lane` (kept when the batch has <= 64 sequences)
+  int n_lane = 0;      // length of sequence `lane` (kept when the batch has <= 64 sequences)
   for (int base = 0; base < B; base += 64) {
     const int bi = base + lane;
-    cb_lane = bi < B ? chunks_of(clamp_len(lens[bi], a)) : 0;
-    total += uni(wave_sum(cb_lane));
+    n_lane = bi < B ? clamp_len(lens[bi], a) : 0;
+    total += uni(wave_sum(chunks_of(n_lane)));
   }
+  // Length of sequence b: from the registers when the whole batch fits one
+  // wave, else a scalar load.
+  auto seq_len = [&](int b) -> int {
+    if (B <= 64) return uni(__builtin_amdgcn_readlane(n_lane, uni(b)));
+    return uni(clamp_len(lens[uni(b)], a));
+  };
   const int64_t C = total * Hkv;
   const int64_t K = (C + W - 1) / W;
   const int64_t x0 = (int64_t)wid * K;
@@ -423,7 +427,7 @@ __device__ __forceinline__ void split_body(const DecodeArgs& a, const int32_t* _
     int64_t run = 0;
     for (int base = 0; base < B; base += 64) {
       const int bi = base + lane;
-      const int cb = bi < B ? (B <= 64 ? cb_lane : chunks_of(clamp_len(lens[bi], a))) : 0;
+      const int cb = bi < B ? chunks_of(B <= 64 ? n_lane : clamp_len(lens[bi], a)) : 0;
       const int incl = wave_inclusive_scan(cb, lane);
       const int64_t ex = run + incl - cb;
       const bool hit = cb > 0 && (int64_t)Hkv * ex <= x0 && x0 < (int64_t)Hkv * (ex + cb);
@@ -464,11 +468,15 @@ __device__ __forceinline__ void split_body(const DecodeArgs& a, const int32_t* _
   };
 
   const size_t blk_stride = (size_t)Hkv * kBlockTokens * D;   // elements per block
-  auto block_ids = [&](const Pos& q, int& id0, int& id1) {   // scalar loads
+  // Physical ids of a chunk's two blocks (scalar loads).  They are fetched one
+  // chunk ahead of their use, so the table lookup never delays a prefetch.
+  struct Ids {
+    int id0, id1;
+  };
+  auto block_ids = [&](const Pos& q) -> Ids {
     const int32_t* table = tables + (size_t)q.b * a.max_blocks;
     const int last = (q.n + kBlockTokens - 1) / kBlockTokens - 1;
-    id0 = uni(min(max(table[uni(min(2 * q.c, last))], 0), a.num_blocks - 1));
-    id1 = uni(min(max(table[uni(min(2 * q.c + 1, last))], 0), a.num_blocks - 1));
+    return Ids{table[uni(min(2 * q.c, last))], table[uni(min(2 * q.c + 1, last))]};
   };
 
   // Query operand (and fp8 scales) of a pair.  Lane (r, j) holds head g*G + r;
@@ -493,9 +501,9 @@ __device__ __forceinline__ void split_body(const DecodeArgs& a, const int32_t* _
     return 1.f;
   };
 
-  auto issue = [&](typename T::K& kb, typename T::V& vb, typename T::Q& qn, const Pos& q) {
-    int id0, id1;
-    block_ids(q, id0, id1);
+  auto issue = [&](typename T::K& kb, typename T::V& vb, typename T::Q& qn, const Pos& q, const Ids& ids) {
+    const int id0 = uni(min(max(ids.id0, 0), a.num_blocks - 1));
+    const int id1 = uni(min(max(ids.id1, 0), a.num_blocks - 1));
     const Elem* kp = static_cast<const Elem*>(a.k_pool) + (size_t)q.g * kBlockTokens * D;
     const Elem* vp = static_cast<const Elem*>(a.v_pool) + (size_t)q.g * kBlockTokens * D;
     T::load_k(kb, kp + (size_t)((r >> 3) ? id1 : id0) * blk_stride, r, j);
@@ -590,19 +598,28 @@ __device__ __forceinline__ void split_body(const DecodeArgs& a, const int32_t* _
     typename T::K kA, kB;
     typename T::V vA, vB;
     Pos pa = pos, pb;
-    issue(kA, vA, qA, pa);
+    Ids ia = block_ids(pa), ib;
+    issue(kA, vA, qA, pa, ia);
+    if (nch > 1) {
+      pb = advance(pa);
+      ib = block_ids(pb);
+    }
     int k = 0;
     for (; k + 2 < nch; k += 2) {
-      pb = advance(pa);
-      issue(kB, vB, qB, pb);
+      issue(kB, vB, qB, pb, ib);
+      const Pos pn = advance(pb);       // chunk k+2 exists
+      ia = block_ids(pn);
       compute(kA, vA, qA, pa, false);
-      pa = advance(pb);
-      issue(kA, vA, qA, pa);
+      pa = pn;
+      issue(kA, vA, qA, pa, ia);
+      // chunk k+3, when there is one (otherwise its ids are not needed)
+      const Pos pm = k + 3 < nch ? advance(pa) : pa;
+      ib = block_ids(pm);
       compute(kB, vB, qB, pb, false);
+      pb = pm;
     }
     if (k + 1 < nch) {
-      pb = advance(pa);
-      issue(kB, vB, qB, pb);
+      issue(kB, vB, qB, pb, ib);
       compute(kA, vA, qA, pa, false);
       compute(kB, vB, qB, pb, true);
     } else {

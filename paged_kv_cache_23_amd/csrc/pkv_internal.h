@@ -11,7 +11,7 @@ constexpr int kBlockTokens = 16;    // tokens per cache block
 constexpr int kChunkTokens = 32;    // tokens one wave consumes per step: two blocks
 constexpr int kDecodeWaves = 4;     // worker waves per decode workgroup
 constexpr int kMaxGroup = 16;       // query heads per kv head that one MFMA column tile holds
-constexpr int kWavesPerSimd = 2;    // resident decode waves per SIMD (register budget)
+constexpr int kWavesPerSimd = 1;    // worker waves per SIMD: a second one mostly waits on the first
 
 enum KvType : int32_t { kF32 = 0, kBF16 = 1, kFP8 = 2 };
 
