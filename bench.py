@@ -2,8 +2,8 @@
 """Paged decode benchmark on one MI355X.
 
 A step is one decode pass of one layer over the whole batch: one
-pkv_paged_decode call (a single kernel launch; for workloads that append, the
-kv_append of one token per sequence first).  Inputs are seeded synthetic data already
+pkv_paged_decode call (two kernels, split then merge; for workloads that
+append, the kv_append of one token per sequence first).  Inputs are seeded synthetic data already
 resident in HBM; successive steps rotate over ``--layers`` distinct copies of
 the pool so that the bytes touched between reuses of one copy exceed the
 256 MB Infinity Cache.
@@ -53,9 +53,10 @@ def kernel_source_hash() -> str:
 
 
 def committed_traffic(workload: str):
-    """HBM bytes per decode-kernel launch from the committed rocprofv3 counter
-    summary, if it was taken on the current kernel source; else None."""
-    path = os.path.join(PROFILE_DIR, f"decode_kernel_{workload}_pmc.txt")
+    """HBM bytes per pkv_paged_decode call (both kernels) from the committed
+    rocprofv3 counter summary, if it was taken on the current kernel source;
+    else None."""
+    path = os.path.join(PROFILE_DIR, f"paged_decode_{workload}_hbm_traffic.txt")
     if not os.path.exists(path):
         return None
     text = open(path).read()
@@ -246,8 +247,8 @@ def run_bench(args) -> dict:
     total_ms = start_ev.elapsed_time(end_ev)
     ms_per_step = total_ms / K
 
-    # per-launch durations of the decode kernel: the same steps, HIP events
-    # around each launch on the stream it runs on
+    # per-call durations of the decode (split + merge kernels): the same
+    # steps, HIP events around each call on the stream its kernels run on
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
     for i in range(K):
         layer = i % L
@@ -259,7 +260,7 @@ def run_bench(args) -> dict:
     torch.cuda.synchronize()
     part_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
     log(f"{K} steps: {total_ms:.3f} ms on the stream, {wall * 1e3:.3f} ms wall ({ms_per_step * 1e3:.1f} us/step); "
-        f"decode kernel mean {part_ms.mean() * 1e3:.1f} us (p10 {np.percentile(part_ms, 10) * 1e3:.1f}, "
+        f"decode call mean {part_ms.mean() * 1e3:.1f} us (p10 {np.percentile(part_ms, 10) * 1e3:.1f}, "
         f"p90 {np.percentile(part_ms, 90) * 1e3:.1f})")
 
     step_bytes = runner.kv_bytes + runner.append_bytes
@@ -292,7 +293,7 @@ def run_bench(args) -> dict:
         "decode_tokens_per_s": round(wl.batch / (ms_per_step * 1e-3), 1),
         "max_abs_err_sampled": err,
         "roofline": {
-            "kernel": "decode_kernel",
+            "kernel": "pkv_paged_decode (decode_split_kernel + decode_merge_kernel)",
             "bound": "hbm",
             "achieved": round(kern_gbs, 2),
             "peak": HBM_PEAK_GBS,
@@ -300,7 +301,7 @@ def run_bench(args) -> dict:
             "frac": round(kern_gbs / HBM_PEAK_GBS, 4),
             "traffic": traffic,
             "algorithmic_bytes_per_launch": runner.kv_bytes,
-            "mean_launch_us": round(float(part_ms.mean()) * 1e3, 2),
+            "mean_call_us": round(float(part_ms.mean()) * 1e3, 2),
         },
     }
     if not args.no_cpu_baseline:

@@ -126,10 +126,11 @@ size_t pkv_decode_workspace_bytes(const pkv_cache_desc* desc, int32_t num_seqs,
  * Two kernels on `stream`.  The batch's 32-token chunks of every (sequence,
  * kv head) pair, pairs in sequence-major order, are cut into equal contiguous
  * ranges, one per worker wave; each wave runs section 3's online softmax over
- * its range and finishes every pair it covers completely.  For a pair split
- * between waves each wave leaves a float32 partial state (running max, sum,
- * unnormalised accumulator); the second kernel merges them with the same
- * rescale by exp(m_old - m_new) and writes zeros for empty sequences.
+ * its range and finishes every pair it covers completely; sequences of length
+ * 0 get their zero output there too.  For a pair split between waves each wave
+ * leaves a float32 partial state (running max, sum, unnormalised
+ * accumulator); the second kernel merges them with the same rescale by
+ * exp(m_old - m_new).
  *   workspace  device buffer of pkv_decode_workspace_bytes(..., 0) bytes,
  *              16-byte aligned; scratch, needs no initialisation.  Calls that
  *              share one workspace must be ordered (one stream). */

@@ -413,6 +413,16 @@ __device__ __forceinline__ void split_body(const DecodeArgs& a, const int32_t* _
     if (B <= 64) return uni(__builtin_amdgcn_readlane(n_lane, uni(b)));
     return uni(clamp_len(lens[uni(b)], a));
   };
+  // Sequences with no tokens: wave b mod W writes their zero output and a
+  // (first wave 0, parts 0) record per pair, so every pair has a fresh record
+  // and the merge kernel never needs the lengths.
+  for (int b = wid; b < B; b += W) {
+    if (seq_len(b) != 0) continue;
+    OutT* o = out + (size_t)b * Hq * D;
+    for (int e = lane; e < Hq * D; e += 64) o[e] = (OutT)0.f;
+    for (int g = lane; g < Hkv; g += 64) a.pair_meta[b * Hkv + g] = int2{0, 0};
+  }
+
   const int64_t C = total * Hkv;
   const int64_t K = (C + W - 1) / W;
   const int64_t x0 = (int64_t)wid * K;
@@ -650,27 +660,22 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_split_kernel_wide(
 }
 
 // ---------------------------------------------------------------------------
-// Merge kernel: one workgroup per (sequence, kv head) pair.  Reads the pair's
-// length and the split kernel's record of it in one round trip; a pair one
-// wave finished returns at once, an empty sequence gets zeros, a split pair
-// combines its partials with the online-softmax rescale (second round trip).
+// Merge kernel: one workgroup per (sequence, kv head) pair.  Its only input
+// besides the partials is the pair's record, written by the split kernel on
+// every call: a pair one wave finished (or an empty one, already zeroed)
+// returns at once; a split pair combines its partials with the online-softmax
+// rescale.  Two dependent round trips: the record, then the partials.
 // ---------------------------------------------------------------------------
 template <typename OutT, int D>
-__global__ __launch_bounds__(128) void decode_merge_kernel(DecodeArgs a, const int32_t* __restrict__ lens,
-                                                           const int2* __restrict__ meta) {
+__global__ __launch_bounds__(128) void decode_merge_kernel(const int2* __restrict__ meta,
+                                                           const float* __restrict__ ws_acc,
+                                                           const float* __restrict__ ws_ml, OutT* __restrict__ out,
+                                                           int num_kv_heads, int group) {
   const int pair = blockIdx.x;
-  const int Hkv = a.num_kv_heads;
-  const int b = pair / Hkv;
-  const int g = pair % Hkv;
-  const int G = a.group;
-  const int n = clamp_len(lens[b], a);
   const int2 m = meta[pair];
-  OutT* out = static_cast<OutT*>(a.out) + ((size_t)b * a.num_q_heads + g * G) * D;
-  if (n == 0) {
-    for (int e = threadIdx.x; e < G * D; e += 128) out[e] = (OutT)0.f;
-    return;
-  }
   if (m.y <= 1) return;   // one wave covered the pair and wrote its output
+  const int G = group;
+  out += ((size_t)(pair / num_kv_heads) * num_kv_heads * G + (size_t)(pair % num_kv_heads) * G) * D;
   for (int e = threadIdx.x; e < G * (D / 4); e += 128) {
     const int h = e / (D / 4);
     const int q4 = e % (D / 4);
@@ -679,13 +684,12 @@ __global__ __launch_bounds__(128) void decode_merge_kernel(DecodeArgs a, const i
 #pragma unroll 4
     for (int w = m.x; w < m.x + m.y; ++w) {
       const size_t slot = ((size_t)w + pair) * G + h;
-      const float m_w = a.ws_ml[slot * 2];
-      const float l_w = a.ws_ml[slot * 2 + 1];
-      const f32x4 acc_w = *reinterpret_cast<const f32x4*>(a.ws_acc + slot * D + 4 * q4);
-      const float M2 = fmaxf(M, m_w);
+      const float2 ml = *reinterpret_cast<const float2*>(ws_ml + slot * 2);
+      const f32x4 acc_w = *reinterpret_cast<const f32x4*>(ws_acc + slot * D + 4 * q4);
+      const float M2 = fmaxf(M, ml.x);
       const float f_old = exp2_fast(M - M2);
-      const float f_new = exp2_fast(m_w - M2);
-      L = L * f_old + l_w * f_new;
+      const float f_new = exp2_fast(ml.x - M2);
+      L = L * f_old + ml.y * f_new;
       o = o * f_old + acc_w * f_new;
       M = M2;
     }
@@ -708,8 +712,9 @@ hipError_t launch_split_t(const DecodeArgs& a, hipStream_t stream) {
 template <typename OutT, int D>
 hipError_t launch_merge_t(const DecodeArgs& a, hipStream_t stream) {
   const unsigned grid = (unsigned)a.num_seqs * (unsigned)a.num_kv_heads;
-  hipLaunchKernelGGL((decode_merge_kernel<OutT, D>), dim3(grid), dim3(128), 0, stream, a, a.context_lens,
-                     a.pair_meta);
+  hipLaunchKernelGGL((decode_merge_kernel<OutT, D>), dim3(grid), dim3(128), 0, stream,
+                     static_cast<const int2*>(a.pair_meta), static_cast<const float*>(a.ws_acc),
+                     static_cast<const float*>(a.ws_ml), static_cast<OutT*>(a.out), a.num_kv_heads, a.group);
   return hipGetLastError();
 }
 
