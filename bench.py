@@ -151,6 +151,26 @@ class Runner:
         self.decode(layer, stream)
 
 
+def unique_kv_bytes(wl, after_append: bool) -> int:
+    """KV bytes of the distinct physical token slots a decode reads: a block
+    that several sequences share counts once (with the most tokens any of them
+    uses in it)."""
+    import numpy as np
+
+    tables = (wl.block_tables_after if after_append else wl.block_tables).numpy()
+    lens = (wl.context_lens_after if after_append else wl.context_lens).numpy()
+    used = {}
+    for row, n in zip(tables, lens):
+        nb = -(-int(n) // 16)
+        for j in range(nb):
+            t = min(16, int(n) - 16 * j)
+            blk = int(row[j])
+            if used.get(blk, 0) < t:
+                used[blk] = t
+    per_token = wl.kv_bytes(after_append) // max(int(np.sum(lens)), 1)
+    return int(sum(used.values())) * per_token
+
+
 def check_against_oracle(runner, sample_seqs: int = 4) -> float:
     """Max |error| of layer 0's output over a few sequences (oracle on the host copy)."""
     import numpy as np
@@ -267,6 +287,7 @@ def run_bench(args) -> dict:
     gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
     kern_gbs = runner.kv_bytes / (part_ms.mean() * 1e-3) / 1e9
     traffic = committed_traffic(wl.name)
+    unique = unique_kv_bytes(wl, runner.append)
     result = {
         "metric": METRIC,
         "value": round(gbs, 2),
@@ -290,6 +311,8 @@ def run_bench(args) -> dict:
             "worker_waves": runner.workers,
         },
         "hbm_peak_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "unique_kv_bytes_per_step": unique,
+        "unique_kv_gbs": round(unique / (ms_per_step * 1e-3) / 1e9, 2),
         "decode_tokens_per_s": round(wl.batch / (ms_per_step * 1e-3), 1),
         "max_abs_err_sampled": err,
         "roofline": {
