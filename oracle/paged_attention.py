@@ -165,6 +165,31 @@ def oracle_append(k_pool, v_pool, k_new, v_new, slot_mapping, kv_dtype: str,
     return k_out, v_out
 
 
+def oracle_copy_blocks(k_pool, v_pool, src, dst):
+    """Copy whole blocks (every kv head, K and V) from src[i] to dst[i].
+
+    Habr article §4, subsection "Copy-on-Write for parallel sampling": when a
+    sequence must modify a block that other sequences reference, the block
+    is copied first and the original stays untouched; §8 gives the same rule
+    for a speculative correction landing in a shared block.  "Why one
+    character breaks the cache" (PagedAttention as virtual memory): the
+    engine counts references per block and copies at block granularity.
+
+    Pairs whose source or destination lies outside ``[0, num_blocks)`` are
+    skipped.  The pairs are applied in order; the library's contract (distinct
+    destinations, none of them also a source) makes the order irrelevant.
+    """
+    k_out = np.array(k_pool, copy=True)
+    v_out = np.array(v_pool, copy=True)
+    nb = k_out.shape[0]
+    for s_blk, d_blk in zip(np.asarray(src, dtype=np.int64), np.asarray(dst, dtype=np.int64)):
+        if not (0 <= s_blk < nb and 0 <= d_blk < nb):
+            continue
+        k_out[d_blk] = k_out[s_blk]
+        v_out[d_blk] = v_out[s_blk]
+    return k_out, v_out
+
+
 # --------------------------------------------------------------------------
 # Decode
 # --------------------------------------------------------------------------

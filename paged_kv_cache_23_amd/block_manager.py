@@ -26,7 +26,7 @@ from __future__ import annotations
 
 from collections import deque
 from dataclasses import dataclass, field
-from typing import Iterable, List, Optional
+from typing import Iterable, List, Optional, Tuple
 
 import numpy as np
 
@@ -116,7 +116,7 @@ class BlockManager:
 
         A full last block (or none) opens a fresh block; a partially filled
         last block receives the token at its next offset, which requires the
-        block to be private to this sequence.
+        block to be private to this sequence (see ``append_slot_cow``).
         """
         seq = self._seqs[sid]
         off = seq.num_tokens % self.block_size
@@ -152,6 +152,45 @@ class BlockManager:
             self.ref_count[b] += 1
         self._seqs[sid] = child
         return sid
+
+    def copy_on_write(self, sid: int, logical_block: Optional[int] = None) -> Optional[Tuple[int, int]]:
+        """Give the sequence a private copy of one of its blocks if it is shared.
+
+        Habr article §4, "Copy-on-Write for parallel sampling": a sequence
+        that must modify a block other sequences reference copies it first;
+        the original stays untouched for the others.  ``logical_block``
+        defaults to the last block (where the next token goes; §8 names the
+        other case, a speculative correction inside an earlier shared block).
+
+        A private block needs no copy: returns None.  Otherwise a fresh block
+        replaces the shared one in this sequence's table, the shared block
+        loses this sequence's reference, and ``(src, dst)`` is returned for
+        the device copy (``pkv_copy_blocks``), which must run before the
+        sequence's next write.
+        """
+        seq = self._seqs[sid]
+        if not seq.blocks:
+            return None
+        j = len(seq.blocks) - 1 if logical_block is None else int(logical_block)
+        if not 0 <= j < len(seq.blocks):
+            raise IndexError(f"sequence {sid} has no logical block {j}")
+        old = seq.blocks[j]
+        if self.ref_count[old] == 1:
+            return None
+        new = self._pop_free()
+        self.ref_count[old] -= 1   # others still hold it: never reaches zero here
+        seq.blocks[j] = new
+        return old, new
+
+    def append_slot_cow(self, sid: int) -> Tuple[int, Optional[Tuple[int, int]]]:
+        """``append_slot`` after a copy-on-write of a shared partial last block.
+
+        Returns ``(slot, copy)`` where ``copy`` is the ``(src, dst)`` block pair
+        to copy on the device before the token is written, or None.
+        """
+        seq = self._seqs[sid]
+        copy = self.copy_on_write(sid) if seq.num_tokens % self.block_size else None
+        return self.append_slot(sid), copy
 
     def free_sequence(self, sid: int) -> None:
         """Drop a sequence; blocks nobody references any more become free."""

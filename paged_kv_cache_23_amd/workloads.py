@@ -24,7 +24,7 @@ from __future__ import annotations
 
 import math
 from dataclasses import dataclass
-from typing import Optional, Sequence
+from typing import List, Optional, Sequence
 
 import numpy as np
 import torch
@@ -225,6 +225,91 @@ def fp8_b256(seed: int = 5) -> Workload:
     rng = np.random.default_rng(seed)
     lens = np.rint(np.exp(rng.uniform(math.log(128), math.log(8192), size=256))).astype(np.int64)
     return build_workload("fp8-b256", lens, 32, 8, 128, "fp8", seed, with_append=True, rng=rng)
+
+
+@dataclass
+class CowStep:
+    """One decode step of a parallel-sampling batch: block copies to make
+    first, then one new token per sample written to its slot."""
+    copy_src: torch.Tensor      # int32 [C] blocks to copy from (shared originals)
+    copy_dst: torch.Tensor      # int32 [C] fresh private blocks
+    slot_mapping: torch.Tensor  # int64 [S]
+    k_new: torch.Tensor         # [S, Hkv, D] (bf16 for an fp8 pool)
+    v_new: torch.Tensor
+
+
+@dataclass
+class CowScenario:
+    """Parallel sampling over one prompt whose last block is partly filled:
+    every sample forks the whole prompt, so that block is shared and each
+    sample copies it before its first token lands there (copy-on-write)."""
+    name: str
+    kv_dtype: str
+    q_dtype: str
+    num_blocks: int
+    num_kv_heads: int
+    num_q_heads: int
+    head_dim: int
+    k_pool: torch.Tensor          # before any step
+    v_pool: torch.Tensor
+    k_scale: Optional[torch.Tensor]
+    v_scale: Optional[torch.Tensor]
+    steps: List[CowStep]
+    q: torch.Tensor               # [1 + S, Hq, D]: the prompt's own query, then the samples'
+    block_tables: torch.Tensor    # int32 [1 + S, max_blocks] after the last step
+    context_lens: torch.Tensor    # int32 [1 + S] after the last step
+    scale: float
+    prompt_blocks: List[int]      # the prompt's physical blocks (never written)
+
+
+def cow_sampling(name: str, prompt_tokens: int, samples: int, new_tokens: int, num_q_heads: int,
+                 num_kv_heads: int, head_dim: int, kv_dtype: str, seed: int) -> CowScenario:
+    """Seeded parallel-sampling batch (Habr article §4, "Copy-on-Write for
+    parallel sampling"): one prompt of ``prompt_tokens`` tokens, ``samples``
+    forks of it, each appending ``new_tokens`` tokens one step at a time."""
+    if prompt_tokens % BLOCK_SIZE == 0:
+        raise ValueError("the prompt must end inside a block for copy-on-write to occur")
+    rng = np.random.default_rng(seed)
+    gen = torch.Generator().manual_seed(seed)
+    nblk = (prompt_tokens + BLOCK_SIZE - 1) // BLOCK_SIZE
+    extra = samples * (1 + (BLOCK_SIZE - 1 + new_tokens) // BLOCK_SIZE)
+    NB = nblk + extra + 4
+    bm = BlockManager(NB, free_order=rng.permutation(NB))
+    root = bm.new_sequence(prompt_tokens)
+    prompt_blocks = bm.blocks(root)
+    kids = [bm.fork(root) for _ in range(samples)]
+    D, Hkv, Hq = head_dim, num_kv_heads, num_q_heads
+    q_dtype = "f32" if kv_dtype == "f32" else "bf16"
+    new_dtype = _TORCH_DTYPE["bf16" if kv_dtype == "fp8" else kv_dtype]
+    k_scale = v_scale = None
+    if kv_dtype == "fp8":
+        k_pool, k_scale = _fp8_pool((NB, Hkv, BLOCK_SIZE, D), gen)
+        v_pool, v_scale = _fp8_pool((NB, Hkv, D, BLOCK_SIZE), gen)
+    else:
+        k_pool = _randn((NB, Hkv, BLOCK_SIZE, D), gen, _TORCH_DTYPE[kv_dtype])
+        v_pool = _randn((NB, Hkv, D, BLOCK_SIZE), gen, _TORCH_DTYPE[kv_dtype])
+    steps = []
+    for _ in range(new_tokens):
+        src, dst, slots = [], [], []
+        for sid in kids:
+            slot, copy = bm.append_slot_cow(sid)
+            if copy is not None:
+                src.append(copy[0])
+                dst.append(copy[1])
+            slots.append(slot)
+        steps.append(CowStep(copy_src=torch.tensor(src, dtype=torch.int32),
+                             copy_dst=torch.tensor(dst, dtype=torch.int32),
+                             slot_mapping=torch.tensor(slots, dtype=torch.int64),
+                             k_new=_randn((samples, Hkv, D), gen, new_dtype),
+                             v_new=_randn((samples, Hkv, D), gen, new_dtype)))
+    ids = [root] + kids
+    width = max(len(bm.blocks(s)) for s in ids)
+    return CowScenario(name=name, kv_dtype=kv_dtype, q_dtype=q_dtype, num_blocks=NB, num_kv_heads=Hkv,
+                       num_q_heads=Hq, head_dim=D, k_pool=k_pool, v_pool=v_pool, k_scale=k_scale,
+                       v_scale=v_scale, steps=steps, q=_randn((1 + samples, Hq, D), gen, _TORCH_DTYPE[q_dtype]),
+                       block_tables=torch.from_numpy(bm.block_table(ids, width)),
+                       context_lens=torch.from_numpy(bm.context_lens(ids)), scale=1.0 / math.sqrt(D),
+                       prompt_blocks=prompt_blocks)
 
 
 WORKLOADS = {

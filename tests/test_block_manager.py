@@ -131,3 +131,31 @@ def test_block_table_padding():
     assert t.dtype == np.int32 and t.shape == (2, 4)
     assert t.tolist() == [[3, 1, -1, -1], [4, -1, -1, -1]]
     assert bm.context_lens([a, b]).tolist() == [17, 1]
+
+
+def test_copy_on_write_gives_a_private_block():
+    """Habr article §4, "Copy-on-Write for parallel sampling": the sequence that
+    writes gets a fresh copy of the shared block; the other keeps the original;
+    reference counts follow and both can then append."""
+    bm = BlockManager(10)
+    root = bm.new_sequence(20)               # blocks [0, 1]; block 1 holds 4 tokens
+    child = bm.fork(root)
+    assert bm.ref_count[1] == 2
+    assert bm.copy_on_write(child) == (1, 2)
+    assert bm.blocks(child) == [0, 2] and bm.blocks(root) == [0, 1]
+    assert (bm.ref_count[0], bm.ref_count[1], bm.ref_count[2]) == (2, 1, 1)
+    assert bm.copy_on_write(child) is None and bm.copy_on_write(root) is None   # both private now
+    assert bm.append_slot(child) == 2 * 16 + 4
+    assert bm.append_slot(root) == 1 * 16 + 4
+    # an earlier, full shared block (Habr §8: a speculative correction inside it)
+    src, dst = bm.copy_on_write(child, 0)
+    assert src == 0 and bm.blocks(child)[0] == dst and bm.ref_count[0] == 1
+    # the combined call: root now holds 21 tokens
+    c2 = bm.fork(root)
+    slot, copy = bm.append_slot_cow(c2)
+    assert copy == (1, bm.blocks(c2)[1]) and slot == bm.blocks(c2)[1] * 16 + 5
+    assert bm.append_slot_cow(c2)[1] is None  # private already
+    # freeing the copies returns them; the original lives on with the root
+    used = bm.blocks_in_use()
+    bm.free_sequence(c2)
+    assert bm.blocks_in_use() == used - 1 and bm.ref_count[1] == 1

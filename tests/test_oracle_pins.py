@@ -315,3 +315,75 @@ def test_planted_mistakes_are_caught(monkeypatch, mistake):
     elif mistake == "wrong_group":
         monkeypatch.setattr(pa, "oracle_decode_pairs", _decode_pairs_wrong_group)
     assert not _pins_pass()
+
+
+def test_copy_blocks_moves_whole_blocks_only():
+    """Every kv head of K and V of each destination becomes its source; every
+    other block keeps its bits; pairs outside the pool are skipped."""
+    rng = np.random.default_rng(3)
+    kp = rng.standard_normal((6, 2, BS, 8)).astype(np.float32)
+    vp = rng.standard_normal((6, 2, 8, BS)).astype(np.float32)
+    k2, v2 = oracle.oracle_copy_blocks(kp, vp, [1, 4, -1, 3], [5, 0, 2, 9])
+    assert np.array_equal(k2[5], kp[1]) and np.array_equal(v2[5], vp[1])
+    assert np.array_equal(k2[0], kp[4]) and np.array_equal(v2[0], vp[4])
+    for b in (1, 2, 3, 4):
+        assert np.array_equal(k2[b], kp[b]) and np.array_equal(v2[b], vp[b])
+    assert not np.shares_memory(k2, kp)
+
+
+def _run_cow_on_oracle(sc):
+    from paged_kv_cache_23_amd.workloads import storage_numpy
+    kp, vp = storage_numpy(sc.k_pool), storage_numpy(sc.v_pool)
+    ks = None if sc.k_scale is None else sc.k_scale.numpy()
+    vs = None if sc.v_scale is None else sc.v_scale.numpy()
+    for st in sc.steps:
+        kp, vp = oracle.oracle_copy_blocks(kp, vp, st.copy_src.numpy(), st.copy_dst.numpy())
+        kp, vp = oracle.oracle_append(kp, vp, storage_numpy(st.k_new), storage_numpy(st.v_new),
+                                      st.slot_mapping.numpy(), sc.kv_dtype, ks, vs)
+    return kp, vp
+
+
+@pytest.mark.parametrize("kv_dtype", ["f32", "bf16", "fp8"])
+def test_copy_on_write_equals_private_history(kv_dtype):
+    """Parallel sampling over a prompt that ends inside a block (Habr article
+    §4): after copy-then-append steps, each sample's decode equals that of a
+    sample whose blocks were private from the start, and the prompt's own
+    blocks and decode are untouched."""
+    from paged_kv_cache_23_amd.workloads import cow_sampling, storage_numpy
+    D = 64 if kv_dtype == "f32" else 32
+    sc = cow_sampling("cow", prompt_tokens=37, samples=3, new_tokens=13, num_q_heads=4,
+                      num_kv_heads=2, head_dim=D, kv_dtype=kv_dtype, seed=12)
+    kp0, vp0 = storage_numpy(sc.k_pool), storage_numpy(sc.v_pool)
+    ks = None if sc.k_scale is None else sc.k_scale.numpy()
+    vs = None if sc.v_scale is None else sc.v_scale.numpy()
+    kp, vp = _run_cow_on_oracle(sc)
+    tables, lens = sc.block_tables.numpy(), sc.context_lens.numpy()
+    q = storage_numpy(sc.q)
+    shared = oracle.oracle_decode(q, sc.q_dtype, kp, vp, kv_dtype, tables, lens, sc.scale, ks, vs)
+    # the prompt's blocks hold their original bits, so its decode is unchanged
+    for blk in sc.prompt_blocks:
+        assert np.array_equal(kp[blk], kp0[blk]) and np.array_equal(vp[blk], vp0[blk])
+    before = oracle.oracle_decode(q[:1], sc.q_dtype, kp0, vp0, kv_dtype, tables[:1], lens[:1], sc.scale, ks, vs)
+    assert np.array_equal(shared[:1], before)
+    # private history: each sample gets its own copy of every prompt block up
+    # front (test code, not the manager), then the same tokens at the same offsets
+    S = len(lens) - 1
+    nb = kp.shape[0]
+    P = len(sc.prompt_blocks)
+    kq = np.concatenate([kp0] + [kp0[sc.prompt_blocks]] * S)
+    vq = np.concatenate([vp0] + [vp0[sc.prompt_blocks]] * S)
+    t_priv = tables.copy()
+    for s in range(S):
+        for j in range(P):
+            t_priv[1 + s, j] = nb + s * P + j
+    # replay the appended tokens into the private tables' blocks
+    prompt_len = int(lens[0])
+    for k, st in enumerate(sc.steps):
+        slots = []
+        for s in range(S):
+            pos = prompt_len + k
+            slots.append(int(t_priv[1 + s, pos // BS]) * BS + pos % BS)
+        kq, vq = oracle.oracle_append(kq, vq, storage_numpy(st.k_new), storage_numpy(st.v_new),
+                                      np.array(slots, dtype=np.int64), kv_dtype, ks, vs)
+    private = oracle.oracle_decode(q, sc.q_dtype, kq, vq, kv_dtype, t_priv, lens, sc.scale, ks, vs)
+    assert np.array_equal(shared, private)
