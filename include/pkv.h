@@ -98,6 +98,25 @@ int pkv_kv_append(const pkv_cache_desc* desc, const void* k_new, const void* v_n
                   const int64_t* slot_mapping, int32_t num_tokens, void* k_pool,
                   void* v_pool, void* stream);
 
+/* Copy whole blocks, for copy-on-write.  For every i < num_pairs, block
+ * dst[i] of both pools (all kv heads, all 16 token slots) becomes a copy of
+ * block src[i].  (Habr article, section 4, "Copy-on-Write for parallel
+ * sampling": a sequence that must modify a block other sequences reference
+ * copies it first and the original stays untouched; section 8 applies it to
+ * a speculative correction.  The host allocator chooses dst and moves the
+ * sequence's table entry; this call moves the bytes, before any write to
+ * dst.)
+ *   k_pool, v_pool  device pools as for pkv_kv_append, updated in place
+ *   src, dst        device int32 [num_pairs]; a pair with either id outside
+ *                   [0, num_blocks) is skipped
+ * Destinations must be distinct and none may also be a source in the same
+ * call: the pairs are copied in parallel.  Bytes are copied as they are
+ * (any dtype; fp8 codes keep their per-head scales).  num_pairs == 0 is a
+ * no-op. */
+int pkv_copy_blocks(const pkv_cache_desc* desc, void* k_pool, void* v_pool,
+                    const int32_t* src, const int32_t* dst, int32_t num_pairs,
+                    void* stream);
+
 /* Number of worker waves pkv_paged_decode uses for this batch shape on the
  * current device: one per SIMD (4 per compute unit), fewer for batches with
  * fewer 32-token chunks; always a multiple of 4.  Returns a negative status on bad arguments

@@ -169,6 +169,29 @@ int pkv_kv_append(const pkv_cache_desc* desc, const void* k_new, const void* v_n
   return launch_status(pkv::launch_append(a, static_cast<hipStream_t>(stream)));
 }
 
+int pkv_copy_blocks(const pkv_cache_desc* desc, void* k_pool, void* v_pool, const int32_t* src,
+                    const int32_t* dst, int32_t num_pairs, void* stream) {
+  int st = check_desc(desc);
+  if (st != PKV_OK) return st;
+  if (num_pairs < 0) return PKV_EINVAL;
+  if (num_pairs == 0) return PKV_OK;
+  if (!k_pool || !v_pool || !src || !dst) return PKV_EINVAL;
+  if (!aligned16(k_pool) || !aligned16(v_pool)) return PKV_EINVAL;
+  const size_t elt = desc->kv_dtype == PKV_F32 ? 4 : desc->kv_dtype == PKV_BF16 ? 2 : 1;
+  pkv::CopyArgs a{};
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.src = src;
+  a.dst = dst;
+  a.block_bytes = (size_t)desc->num_kv_heads * PKV_BLOCK_SIZE * desc->head_dim * elt;
+  a.num_pairs = num_pairs;
+  a.num_blocks = desc->num_blocks;
+  const size_t slice = pkv::copy_slice_bytes();
+  a.slices_per_block = (uint32_t)((a.block_bytes + slice - 1) / slice);
+  if ((uint64_t)num_pairs * 2u * a.slices_per_block > 0x7FFFFFFFu) return PKV_EUNSUPPORTED;
+  return launch_status(pkv::launch_copy(a, static_cast<hipStream_t>(stream)));
+}
+
 int32_t pkv_decode_workers(const pkv_cache_desc* desc, int32_t num_seqs, int32_t max_context_len) {
   int st = check_desc(desc);
   if (st != PKV_OK) return st;

@@ -55,8 +55,21 @@ struct AppendArgs {
   int32_t kv_dtype;
 };
 
+struct CopyArgs {
+  void* k_pool;
+  void* v_pool;
+  const int32_t* src;
+  const int32_t* dst;
+  size_t block_bytes;          // bytes of one block in one pool (all kv heads)
+  int32_t num_pairs;
+  int32_t num_blocks;
+  uint32_t slices_per_block;   // 8 KiB slices per block and pool
+};
+
 // Split kernel then merge kernel, on `stream`.
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
+hipError_t launch_copy(const CopyArgs& a, hipStream_t stream);
+size_t copy_slice_bytes();
 
 }  // namespace pkv

@@ -11,6 +11,7 @@ Shapes and the cache layout are documented in ``include/pkv.h``:
 * v_pool   ``[NB, Hkv, D, 16]``
 * block_tables ``[B, max_blocks]`` int32, context_lens ``[B]`` int32
 * slot_mapping ``[T]`` int64; k_new / v_new ``[T, Hkv, D]``
+* copy src / dst ``[P]`` int32 block ids
 """
 
 from __future__ import annotations
@@ -55,6 +56,7 @@ def library() -> ctypes.CDLL:
         D = ctypes.POINTER(CacheDesc)
         sigs = {
             "pkv_kv_append": (ctypes.c_int, [D, P, P, P, I32, P, P, P]),
+            "pkv_copy_blocks": (ctypes.c_int, [D, P, P, P, P, I32, P]),
             "pkv_decode_workers": (I32, [D, I32, I32]),
             "pkv_decode_workspace_bytes": (SZ, [D, I32, I32, I32]),
             "pkv_paged_decode": (ctypes.c_int, [D, P, P, P, P, I32, P, I32, I32, F, P, P, SZ, P]),
@@ -146,6 +148,19 @@ def kv_append(k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: torch.Tens
         raise ValueError(f"k_new/v_new must be [{T}, {Hkv}, {desc.head_dim}]")
     _check(library().pkv_kv_append(ctypes.byref(desc), _ptr(k_new), _ptr(v_new), _ptr(slot_mapping),
                                    T, _ptr(k_pool), _ptr(v_pool), _stream(stream)), "pkv_kv_append")
+
+
+def copy_blocks(k_pool: torch.Tensor, v_pool: torch.Tensor, src: torch.Tensor, dst: torch.Tensor,
+                k_scale: Optional[torch.Tensor] = None, v_scale: Optional[torch.Tensor] = None,
+                stream=None) -> None:
+    """Copy block ``src[i]`` to block ``dst[i]`` in both pools (copy-on-write), in place."""
+    desc = cache_desc(k_pool, v_pool, k_pool.shape[1], k_scale, v_scale)
+    _require(src, "src", (torch.int32,), 1)
+    _require(dst, "dst", (torch.int32,), 1)
+    if src.shape != dst.shape:
+        raise ValueError("src and dst must have the same length")
+    _check(library().pkv_copy_blocks(ctypes.byref(desc), _ptr(k_pool), _ptr(v_pool), _ptr(src), _ptr(dst),
+                                     src.shape[0], _stream(stream)), "pkv_copy_blocks")
 
 
 def _decode_checks(q, k_pool, v_pool, block_tables, context_lens, k_scale, v_scale, out):

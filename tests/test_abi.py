@@ -27,7 +27,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for required in ("pkv_kv_append", "pkv_paged_decode", "pkv_paged_decode_ex",
+    for required in ("pkv_kv_append", "pkv_copy_blocks", "pkv_paged_decode", "pkv_paged_decode_ex",
                      "pkv_decode_workspace_bytes", "pkv_decode_workers", "pkv_strerror"):
         assert required in names
 
@@ -86,6 +86,19 @@ def test_null_and_size_errors():
                                       6, FAKE, None, 0, None) == EINVAL    # workers not a multiple of 4
     assert lib.pkv_paged_decode_ex(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 64, 0.1,
                                       -4, FAKE, None, 0, None) == EINVAL   # negative workers
+
+
+def test_copy_blocks_argument_checks():
+    lib = ops.library()
+    d = _desc()
+    assert lib.pkv_copy_blocks(None, FAKE, FAKE, FAKE, FAKE, 1, None) == EINVAL
+    assert lib.pkv_copy_blocks(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, -1, None) == EINVAL
+    assert lib.pkv_copy_blocks(ctypes.byref(d), None, FAKE, FAKE, FAKE, 1, None) == EINVAL
+    assert lib.pkv_copy_blocks(ctypes.byref(d), FAKE, FAKE, None, FAKE, 1, None) == EINVAL
+    assert lib.pkv_copy_blocks(ctypes.byref(d), FAKE + 8, FAKE, FAKE, FAKE, 1, None) == EINVAL   # misaligned pool
+    assert lib.pkv_copy_blocks(ctypes.byref(d), None, None, None, None, 0, None) == 0             # no-op
+    bad = _desc(head_dim=96)
+    assert lib.pkv_copy_blocks(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, 1, None) == EUNSUPPORTED
 
 
 def test_workspace_sizing_and_check():
