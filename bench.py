@@ -13,10 +13,11 @@ sum_b n_b * 2 * Hkv * D * bytes/element), its share of the 8 TB/s HBM peak,
 decode tokens/s (sequences / step time), the dominant kernel's roofline, and
 the CPU oracle timed on this host over the same workload.
 
-Extra modes used by the profiling commands:
+Extra modes:
   --profile-one   warm up, then launch the decode a few times (for rocprofv3)
   --copy-probe    run a plain device-to-device copy of known size (calibrates
                   the FETCH_SIZE / WRITE_SIZE counters)
+  --cow           time the copy-on-write block copy and a parallel-sampling step
 """
 
 from __future__ import annotations
@@ -365,6 +366,75 @@ def copy_probe(args) -> None:
     log(f"copied {n} bytes {args.steps} times")
 
 
+def cow_bench(args) -> dict:
+    """Copy-on-write: pkv_copy_blocks at the parallel-sampling shape (8 samples
+    of a 2005-token prompt: one shared 5-token block copied per sample, 32 KiB
+    per pool at bf16) and at a large batch of pairs, then one whole sampling
+    step (copy + append + decode of the prompt and its 8 samples)."""
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_23_amd import ops
+    from paged_kv_cache_23_amd.workloads import cow_sampling
+
+    dev = torch.device("cuda:0")
+    sc = cow_sampling("cow-8", prompt_tokens=2005, samples=8, new_tokens=1, num_q_heads=32,
+                      num_kv_heads=8, head_dim=128, kv_dtype="bf16", seed=44)
+    kp, vp = sc.k_pool.to(dev), sc.v_pool.to(dev)
+    st = sc.steps[0]
+    src, dst = st.copy_src.to(dev), st.copy_dst.to(dev)
+    block_bytes = sc.num_kv_heads * 16 * sc.head_dim * 2
+
+    def timed(fn, reps):
+        for _ in range(10):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps * 1e3   # us
+
+    small_us = timed(lambda: ops.copy_blocks(kp, vp, src, dst), 500)
+    small_bytes = 2 * 2 * len(st.copy_src) * block_bytes            # read + write, K and V
+    # a large batch: 4096 pairs over a 16384-block pool (distinct, disjoint)
+    NB = 16384
+    big_k = torch.empty((NB, 8, 16, 128), dtype=torch.bfloat16, device=dev).normal_()
+    big_v = torch.empty((NB, 8, 128, 16), dtype=torch.bfloat16, device=dev).normal_()
+    perm = torch.from_numpy(np.random.default_rng(7).permutation(NB).astype(np.int32)).to(dev)
+    bsrc, bdst = perm[:4096].contiguous(), perm[4096:8192].contiguous()
+    big_us = timed(lambda: ops.copy_blocks(big_k, big_v, bsrc, bdst), 50)
+    big_bytes = 2 * 2 * 4096 * block_bytes
+    # one whole sampling step on the scenario (the copy is idempotent to repeat)
+    q, tables, lens = sc.q.to(dev), sc.block_tables.to(dev), sc.context_lens.to(dev)
+    kn, vn, slots = st.k_new.to(dev), st.v_new.to(dev), st.slot_mapping.to(dev)
+    out = torch.empty_like(q)
+    mctx = int(sc.context_lens.max())
+    ws = ops.new_workspace(ops.decode_workspace_bytes(kp, vp, 32, q.shape[0], mctx), dev)
+
+    def step():
+        ops.copy_blocks(kp, vp, src, dst)
+        ops.kv_append(kn, vn, slots, kp, vp)
+        ops.paged_decode(q, kp, vp, tables, lens, sc.scale, out=out, max_context_len=mctx, workspace=ws)
+    step_us = timed(step, 200)
+    log(f"copy 8 pairs: {small_us:.2f} us; copy 4096 pairs: {big_us:.1f} us "
+        f"({big_bytes / big_us / 1e3:.0f} GB/s); sampling step: {step_us:.1f} us")
+    return {
+        "metric": "copy-on-write block copy (pkv_copy_blocks) and parallel-sampling step",
+        "unit": "us",
+        "copy_8_pairs_us": round(small_us, 2),
+        "copy_8_pairs_bytes": small_bytes,
+        "copy_4096_pairs_us": round(big_us, 2),
+        "copy_4096_pairs_bytes": big_bytes,
+        "copy_4096_pairs_gbs": round(big_bytes / big_us / 1e3, 1),
+        "copy_4096_pairs_hbm_frac": round(big_bytes / big_us / 1e3 / HBM_PEAK_GBS, 4),
+        "sampling_step_us": round(step_us, 2),
+        "config": {"workload": "8 samples of a 2005-token prompt, 32 q / 8 kv heads, head_dim 128, bf16"},
+    }
+
+
 def main() -> int:
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
@@ -379,6 +449,7 @@ def main() -> int:
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--profile-one", action="store_true")
     p.add_argument("--copy-probe", action="store_true")
+    p.add_argument("--cow", action="store_true", help="time the copy-on-write block copy instead")
     args = p.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
@@ -389,6 +460,9 @@ def main() -> int:
         return 0
     if args.profile_one:
         profile_one(args)
+        return 0
+    if args.cow:
+        print(json.dumps(cow_bench(args)), flush=True)
         return 0
     result = run_bench(args)
     print(json.dumps(result), flush=True)
