@@ -53,7 +53,8 @@ extern "C" {
 #define PKV_EINVAL (-1)       /* null pointer, bad size or shape */
 #define PKV_EUNSUPPORTED (-2) /* dtype / head_dim / group size not built */
 #define PKV_EWORKSPACE (-3)   /* workspace missing or too small */
-#define PKV_ELAUNCH (-4)      /* the HIP runtime reported an error */
+#define PKV_ELAUNCH (-4)      /* the HIP runtime reported an error (host: out of memory) */
+#define PKV_ENOSPACE (-5)     /* the block pool has too few free blocks */
 
 #define PKV_BLOCK_SIZE 16
 
@@ -168,6 +169,72 @@ int pkv_paged_decode_ex(const pkv_cache_desc* desc, const void* q, const void* k
                         int32_t num_seqs, int32_t max_context_len, float scale,
                         int32_t num_workers, void* out, void* workspace,
                         size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Host block pool with a prefix-cache index (no GPU work; not thread-safe:
+ * one scheduler thread owns a pool).
+ *
+ * Habr article, section 7 "That same Cache Read": every full block carries a
+ * hash of all tokens from the start of the sequence; a flat table maps block
+ * hash -> physical block; a request walks its blocks from block 0 and the
+ * first miss ends the hit; hit blocks gain a reference; unreferenced blocks
+ * stay cached until memory runs short and then the least recently used one
+ * is evicted; cached blocks are never modified.  "Why one character breaks
+ * the cache", section on the git-style hash chain: hash(block j) =
+ * H(hash(block j-1), extra keys, tokens of block j), block 0's parent being a
+ * fixed seed; a hit never covers the request's last token; a hit on a free
+ * block takes it out of the LRU queue.
+ *
+ * Here H is SHA-256 over: the parent hash (32 bytes, all zero for block 0),
+ * extra_key (8 bytes little-endian: a tenant salt, adapter id, ...), and the
+ * block's token ids (4 bytes little-endian each).  Only full blocks are
+ * hashed.  The pool owns no KV memory: block ids index the caller's pools.
+ * ------------------------------------------------------------------------- */
+typedef struct pkv_block_pool pkv_block_pool;
+
+/* A pool of num_blocks free blocks of block_size tokens, handed out in id
+ * order at first.  NULL on bad arguments or when out of host memory. */
+pkv_block_pool* pkv_pool_create(int32_t num_blocks, int32_t block_size);
+void pkv_pool_destroy(pkv_block_pool* pool);
+
+/* Longest cached prefix of a request of num_tokens tokens: walks the chained
+ * hashes of its full blocks from block 0, stops at the first miss and at
+ * floor((num_tokens - 1) / block_size) blocks (the last token is always
+ * computed), and at cap.  Each hit block gains one reference (a free one
+ * leaves the LRU queue); their ids go to blocks_out.  Returns the number of
+ * hit blocks (block_size times that many tokens are reusable) or a negative
+ * status. */
+int32_t pkv_pool_match_prefix(pkv_block_pool* pool, const int32_t* tokens, int32_t num_tokens,
+                              uint64_t extra_key, int32_t* blocks_out, int32_t cap);
+
+/* Take count blocks from the head of the LRU queue (reference count 1); a
+ * cached block is removed from the index first (evicted).  Returns count, or
+ * PKV_ENOSPACE (nothing taken) when fewer blocks are free. */
+int32_t pkv_pool_allocate(pkv_block_pool* pool, int32_t count, int32_t* blocks_out);
+
+/* Index the full blocks of a request whose K/V are now computed: block
+ * blocks[j] holds tokens [j*B, (j+1)*B) of tokens.  A block already indexed,
+ * or whose hash another block already holds, is left as it is.  Every listed
+ * full block must be referenced.  Returns the number of blocks added. */
+int32_t pkv_pool_cache_blocks(pkv_block_pool* pool, const int32_t* tokens, int32_t num_tokens,
+                              uint64_t extra_key, const int32_t* blocks, int32_t num_blocks);
+
+/* Drop one reference from each listed block (a request finished).  Blocks
+ * reaching zero join the tail of the LRU queue, the request's last block
+ * first, so that a chain's tail is evicted before its head; they stay in the
+ * index.  Nothing changes if any id is invalid or over-released. */
+int pkv_pool_free(pkv_block_pool* pool, const int32_t* blocks, int32_t num_blocks);
+
+/* Chained hashes (32 bytes each) of the first min(floor(num_tokens / B), cap)
+ * full blocks of a token sequence.  Returns how many were written. */
+int pkv_pool_block_hash(const pkv_block_pool* pool, const int32_t* tokens, int32_t num_tokens,
+                        uint64_t extra_key, uint8_t* hashes_out, int32_t cap);
+
+/* Counters: free blocks, indexed blocks, references of one block, evictions. */
+int32_t pkv_pool_num_free(const pkv_block_pool* pool);
+int32_t pkv_pool_num_cached(const pkv_block_pool* pool);
+int32_t pkv_pool_ref_count(const pkv_block_pool* pool, int32_t block);
+int64_t pkv_pool_evictions(const pkv_block_pool* pool);
 
 /* Static description of a status code. */
 const char* pkv_strerror(int status);

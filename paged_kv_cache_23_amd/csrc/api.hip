@@ -239,6 +239,7 @@ const char* pkv_strerror(int status) {
     case PKV_EUNSUPPORTED: return "unsupported dtype, head_dim or group size";
     case PKV_EWORKSPACE: return "workspace missing or too small";
     case PKV_ELAUNCH: return "HIP launch failed";
+    case PKV_ENOSPACE: return "not enough free blocks";
     default: return "unknown status";
   }
 }

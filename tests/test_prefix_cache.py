@@ -1,0 +1,240 @@
+"""The host prefix-cache index (``pkv_pool_*``) against the pages' rules and
+worked example, a hash chain built independently with ``hashlib``, and a
+small independent Python model of the same rules driven by random requests.
+No GPU needed."""
+
+from __future__ import annotations
+
+import hashlib
+import json
+import os
+import struct
+from collections import OrderedDict
+
+import numpy as np
+import pytest
+
+from paged_kv_cache_23_amd.build import LIB_PATH
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB_PATH), reason="libpkv.so not built")
+
+BS = 16
+G = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def pool(n, bs=BS):
+    from paged_kv_cache_23_amd.prefix_cache import PrefixCachePool
+    return PrefixCachePool(n, bs)
+
+
+def ref_chain(tokens, extra_key=0, bs=BS):
+    """hashlib SHA-256 over (parent hash, 8-byte extra key, 4-byte token ids),
+    block 0's parent being 32 zero bytes: the serialization the header states."""
+    out, parent = [], bytes(32)
+    for j in range(len(tokens) // bs):
+        msg = parent + struct.pack("<Q", extra_key) + struct.pack(f"<{bs}I", *[t & 0xFFFFFFFF for t in tokens[j * bs:(j + 1) * bs]])
+        parent = hashlib.sha256(msg).digest()
+        out.append(parent)
+    return out
+
+
+def run_request(p, tokens, extra_key=0):
+    """Admit, "compute" and cache a request's full blocks, then finish it."""
+    blocks, hit = p.admit(tokens, extra_key)
+    p.cache_blocks(tokens, blocks, extra_key)
+    p.free(blocks)
+    return blocks, hit
+
+
+def test_block_hashes_match_an_independent_chain():
+    rng = np.random.default_rng(0)
+    p = pool(8)
+    for n, key in ((0, 0), (15, 0), (16, 0), (100, 7), (257, 2**64 - 1)):
+        toks = rng.integers(0, 2**31 - 1, size=n).tolist()
+        assert p.block_hashes(toks, key) == ref_chain(toks, key)
+    toks = [-1, -2**31] + list(range(14))                         # negative ids as 32-bit patterns
+    assert p.block_hashes(toks) == ref_chain(toks)
+
+
+def test_worked_example_2000_token_system_prompt():
+    """Habr §7: a 2000-token system prompt is 125 blocks; request 1 (+200 user
+    tokens) computes 138 blocks; request 2 with the same prompt and another
+    200-token message reuses 125 (their ref_count goes 0 -> 1) and computes 13."""
+    w = json.load(open(os.path.join(G, "prefix_cache_worked_example.json")))
+    rng = np.random.default_rng(1)
+    system = rng.integers(0, 128000, size=w["system_prompt_tokens"]).tolist()
+    assert len(system) // w["block_size"] == w["system_prompt_blocks"]
+    p = pool(1024, w["block_size"])
+    r1 = system + rng.integers(0, 128000, size=w["user_message_tokens"]).tolist()
+    blocks1, hit1 = p.admit(r1)
+    assert hit1 == 0 and len(blocks1) == w["request_1_blocks_computed"]
+    p.cache_blocks(r1, blocks1)
+    p.free(blocks1)                                   # request 1 ends: blocks stay cached, ref 0
+    assert all(p.ref_count(b) == w["request_2_hit_ref_count_before"] for b in blocks1)
+    assert p.num_cached == len(r1) // w["block_size"]
+    r2 = system + rng.integers(0, 128000, size=w["user_message_tokens"]).tolist()
+    blocks2, hit2 = p.admit(r2)
+    assert hit2 == w["request_2_blocks_hit"]
+    assert len(blocks2) - hit2 == w["request_2_blocks_computed"]
+    assert blocks2[:hit2] == blocks1[:hit2]
+    assert all(p.ref_count(b) == w["request_2_hit_ref_count_after"] for b in blocks2[:hit2])
+
+
+def test_hit_never_covers_the_last_token():
+    """The gotacat page: the hit is capped at num_tokens - 1, so even a verbatim
+    repeat computes its last token (here its whole last block)."""
+    rng = np.random.default_rng(2)
+    toks = rng.integers(0, 1000, size=2000).tolist()
+    p = pool(512)
+    run_request(p, toks)
+    assert len(p.match_prefix(toks)) == (2000 - 1) // BS == 124
+    assert len(p.match_prefix(toks + [5])) == 125       # one more token: all 125 full blocks usable
+    assert len(p.match_prefix(toks[:17])) == 1 and len(p.match_prefix(toks[:16])) == 0
+    assert p.match_prefix([]) == []
+
+
+@pytest.mark.parametrize("where", [0, 5 * BS + 3, 40 * BS])
+def test_first_miss_ends_the_hit(where):
+    """Changing one token changes its block's hash and, through the chain,
+    every later one: the hit ends at that block ("one character breaks the cache")."""
+    rng = np.random.default_rng(3)
+    toks = rng.integers(0, 1000, size=50 * BS + 1).tolist()
+    p = pool(256)
+    run_request(p, toks)
+    edited = list(toks)
+    edited[where] += 1
+    assert len(p.match_prefix(edited)) == where // BS
+    h0, h1 = p.block_hashes(toks), p.block_hashes(edited)
+    assert h0[:where // BS] == h1[:where // BS]
+    assert all(a != b for a, b in zip(h0[where // BS:], h1[where // BS:]))
+
+
+def test_useful_tokens_are_whole_blocks():
+    """Airouter: a T-token match is worth floor(T / B) * B tokens."""
+    rng = np.random.default_rng(4)
+    base = rng.integers(0, 1000, size=600).tolist()
+    p = pool(256)
+    run_request(p, base)
+    for T in (0, 1, 15, 16, 17, 100, 257, 599):
+        req = base[:T] + [10**6 + i for i in range(40)]   # diverges right after T tokens
+        blocks = p.match_prefix(req)
+        assert len(blocks) * BS == (T // BS) * BS
+        p.free(blocks)
+
+
+def test_extra_key_isolates_tenants():
+    toks = list(range(100))
+    p = pool(64)
+    run_request(p, toks, extra_key=11)
+    assert p.match_prefix(toks + [1], extra_key=12) == []
+    assert len(p.match_prefix(toks + [1], extra_key=11)) == 100 // BS
+
+
+def test_lru_eviction_keeps_prefixes_and_touch():
+    """Unreferenced cached blocks are evicted least recently used first; a
+    request's tail is released before its head, so its prefix survives
+    longest; a hit on a free block takes it out of the queue."""
+    p = pool(10)
+    a = [1] * 48 + [2]        # 3 full blocks + 1 partial -> 4 blocks
+    b = [3] * 48 + [4]
+    ba, _ = run_request(p, a)
+    bb, _ = run_request(p, b)
+    assert p.num_free == 10 and p.num_cached == 6
+    # queue: 2 never-used blocks, then a's blocks tail first, then b's
+    new = p.allocate(4)
+    assert set(new[2:]) == {ba[3], ba[2]}
+    assert p.evictions == 1                             # a's partial block 3 carried no hash
+    assert len(p.match_prefix(a)) == 2                  # a's head blocks 0, 1 survive
+    assert p.num_free == 10 - 4 - 2                     # the two hits left the free queue
+    assert len(p.match_prefix(b)) == 3
+    p.free(new)
+    with pytest.raises(MemoryError):
+        p.allocate(p.num_free + 1)
+
+
+def test_bad_calls_change_nothing():
+    from paged_kv_cache_23_amd.prefix_cache import PrefixCachePool
+    p = pool(4)
+    blocks = p.allocate(2)
+    with pytest.raises(RuntimeError):
+        p.free([blocks[0], blocks[0]])                  # over-release
+    assert p.ref_count(blocks[0]) == 1 and p.num_free == 2
+    with pytest.raises(RuntimeError):
+        p.free([7])                                      # not a block
+    with pytest.raises(ValueError):
+        PrefixCachePool(0)
+    with pytest.raises(RuntimeError):
+        p.cache_blocks(list(range(32)), [blocks[0], 3])  # block 3 is not referenced
+
+
+class ModelPool:
+    """The same rules, written plainly: dict index, OrderedDict LRU queue."""
+
+    def __init__(self, n, bs=BS):
+        self.bs, self.ref = bs, [0] * n
+        self.free_q = OrderedDict((b, None) for b in range(n))
+        self.index, self.hash_of, self.evictions = {}, {}, 0
+
+    def match(self, toks, key=0):
+        hs = ref_chain(toks, key, self.bs)[:(len(toks) - 1) // self.bs if toks else 0]
+        hit = []
+        for h in hs:
+            if h not in self.index:
+                break
+            hit.append(self.index[h])
+        for b in hit:
+            if self.ref[b] == 0:
+                del self.free_q[b]
+            self.ref[b] += 1
+        return hit
+
+    def allocate(self, k):
+        out = []
+        for _ in range(k):
+            b, _ = self.free_q.popitem(last=False)
+            if b in self.hash_of:
+                del self.index[self.hash_of.pop(b)]
+                self.evictions += 1
+            self.ref[b] = 1
+            out.append(b)
+        return out
+
+    def cache(self, toks, blocks, key=0):
+        for h, b in zip(ref_chain(toks, key, self.bs), blocks):
+            if b in self.hash_of or h in self.index:
+                continue
+            self.index[h], self.hash_of[b] = b, h
+
+    def free(self, blocks):
+        for b in reversed(blocks):
+            self.ref[b] -= 1
+            if self.ref[b] == 0:
+                self.free_q[b] = None
+
+
+def test_random_requests_match_an_independent_model():
+    """Random requests built from a few shared system prompts and user turns:
+    hits, block ids, evictions and free counts agree step by step."""
+    rng = np.random.default_rng(5)
+    prompts = [rng.integers(0, 500, size=int(rng.integers(20, 300))).tolist() for _ in range(5)]
+    p, m = pool(120), ModelPool(120)
+    live = []
+    for step in range(400):
+        if live and (rng.random() < 0.45 or p.num_free < 40):
+            toks, blocks = live.pop(int(rng.integers(len(live))))
+            p.cache_blocks(toks, blocks)
+            m.cache(toks, blocks)
+            p.free(blocks)
+            m.free(blocks)
+            continue
+        toks = prompts[int(rng.integers(len(prompts)))] + rng.integers(0, 500, size=int(rng.integers(1, 60))).tolist()
+        hit_p = p.match_prefix(toks)
+        hit_m = m.match(toks)
+        assert hit_p == hit_m, step
+        need = -(-len(toks) // BS) - len(hit_p)
+        new_p = p.allocate(need)
+        new_m = m.allocate(need)
+        assert new_p == new_m, step
+        live.append((toks, hit_p + new_p))
+        assert p.evictions == m.evictions and p.num_free == len(m.free_q), step
+    assert p.num_cached == len(m.index)
