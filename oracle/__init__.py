@@ -18,6 +18,7 @@ from .paged_attention import (  # noqa: F401
     gather_slab,
     kv_bytes_per_token,
     oracle_append,
+    oracle_attention_multi,
     oracle_copy_blocks,
     oracle_decode,
     oracle_decode_pairs,

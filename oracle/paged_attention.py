@@ -276,3 +276,47 @@ def oracle_decode(q, q_dtype: str, k_pool, v_pool, kv_dtype: str,
     res = oracle_decode_pairs(q, q_dtype, k_pool, v_pool, kv_dtype, block_tables,
                               context_lens, scale, pairs, k_scale, v_scale)
     return res.reshape(B, Hkv * G, D)
+
+
+# --------------------------------------------------------------------------
+# Several query tokens per sequence
+# --------------------------------------------------------------------------
+def oracle_attention_multi(q, q_dtype: str, k_pool, v_pool, kv_dtype: str,
+                           block_tables, context_lens, scale: float,
+                           k_scale=None, v_scale=None) -> np.ndarray:
+    """Causal attention of the last L tokens of each sequence: ``[B, L, Hq, D]``.
+
+    Habr article §6 "Chunked Prefill": a prompt chunk is processed in one
+    forward pass next to decode tokens, attending to everything cached before
+    it; "Chapter 8 - Next-generation KV cache", closing section: speculative
+    decoding verifies several drafted tokens in one pass.  In both, the L new
+    tokens' K and V are already in the cache (appended first, as for decode),
+    so sequence b holds n = context_lens[b] >= L tokens and query token i
+    (i < L) sits at position n - L + i: it attends to the first n - L + i + 1
+    tokens (itself and everything before it; causal attention, Habr §3).
+    Each output row is the plain softmax(scale * q . K^T) V over those
+    tokens, evaluated in fp64 on the gathered slab; query heads share kv
+    heads in contiguous groups as for decode.
+    """
+    q = np.asarray(q)
+    B, L, Hq, D = q.shape
+    Hkv = k_pool.shape[1]
+    G = Hq // Hkv
+    scale64 = float(np.float32(scale))
+    out = np.zeros((B, L, Hq, D))
+    for b in range(B):
+        n = int(context_lens[b])
+        if n < L:
+            raise ValueError(f"sequence {b} holds {n} tokens, fewer than its {L} query tokens")
+        for g in range(Hkv):
+            K = _widen(gather_slab(k_pool, block_tables[b], n, "k", g), kv_dtype)
+            V = _widen(gather_slab(v_pool, block_tables[b], n, "v", g), kv_dtype)
+            if kv_dtype == "fp8":
+                K = K * float(np.float32(k_scale[g]))
+                V = V * float(np.float32(v_scale[g]))
+            for i in range(L):
+                visible = n - L + i + 1
+                qf = _widen(q[b, i, g * G:(g + 1) * G], q_dtype)
+                out[b, i, g * G:(g + 1) * G] = _attend_pair(qf, K[:visible], V[:visible], scale64)
+    return out
+

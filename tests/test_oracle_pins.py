@@ -387,3 +387,60 @@ def test_copy_on_write_equals_private_history(kv_dtype):
                                       np.array(slots, dtype=np.int64), kv_dtype, ks, vs)
     private = oracle.oracle_decode(q, sc.q_dtype, kq, vq, kv_dtype, t_priv, lens, sc.scale, ks, vs)
     assert np.array_equal(shared, private)
+
+
+def _multi_workload(kv_dtype, L, seed):
+    """A batch whose last L tokens per sequence are the new query tokens."""
+    D = 64 if kv_dtype == "f32" else 32
+    wl = build_workload("multi", [L, L + 1, 37, 64, 100], 8, 2, D, kv_dtype, seed=seed)
+    gen = torch.Generator().manual_seed(seed + 1)
+    qd = torch.float32 if kv_dtype == "f32" else torch.bfloat16
+    q = torch.randn((wl.batch, L, 8, D), generator=gen).to(qd)
+    return wl, storage_numpy(q)
+
+
+@pytest.mark.parametrize("kv_dtype", ["f32", "bf16", "fp8"])
+@pytest.mark.parametrize("L", [1, 2, 4])
+def test_multi_token_equals_sequential_decodes(kv_dtype, L):
+    """Verifying L tokens in one pass gives what L single-token decodes give
+    when each sees the cache only up to its own position (the premise of
+    speculative verification and of chunked prefill); L = 1 is the decode."""
+    wl, q = _multi_workload(kv_dtype, L, 21)
+    args = oracle_args(wl)
+    multi = oracle.oracle_attention_multi(**dict(args, q=q))
+    lens = args["context_lens"]
+    for i in range(L):
+        step = oracle.oracle_decode(**dict(args, q=q[:, i], context_lens=lens - (L - 1 - i)))
+        assert np.array_equal(multi[:, i], step)
+
+
+def test_multi_token_brute_force_causal():
+    """Pure-Python loops over (b, i, h, t) with math.fsum, reading the pool
+    through the table, each query seeing tokens up to its own position."""
+    wl, q = _multi_workload("f32", 3, 22)
+    args = oracle_args(wl)
+    got = oracle.oracle_attention_multi(**dict(args, q=q))
+    kp, vp, tables, lens = args["k_pool"], args["v_pool"], args["block_tables"], args["context_lens"]
+    G = 8 // 2
+    scale = float(np.float32(args["scale"]))
+    for b in range(len(lens)):
+        n = int(lens[b])
+        for i in range(3):
+            vis = n - 3 + i + 1
+            for h in range(8):
+                g = h // G
+                sc = [scale * math.fsum(float(q[b, i, h, d]) * float(kp[int(tables[b][t // BS]), g, t % BS, d])
+                                        for d in range(q.shape[-1])) for t in range(vis)]
+                m = max(sc)
+                e = [math.exp(x - m) for x in sc]
+                z = math.fsum(e)
+                for d in (0, 7, q.shape[-1] - 1):
+                    want = math.fsum(e[t] / z * float(vp[int(tables[b][t // BS]), g, d, t % BS]) for t in range(vis))
+                    assert abs(got[b, i, h, d] - want) < 1e-12
+
+
+def test_multi_token_needs_the_tokens_in_the_cache():
+    wl, q = _multi_workload("f32", 4, 23)
+    args = oracle_args(wl)
+    with pytest.raises(ValueError):
+        oracle.oracle_attention_multi(**dict(args, q=q, context_lens=args["context_lens"] - 1))
