@@ -80,21 +80,30 @@ int32_t resolve_workers(const pkv_cache_desc* d, int32_t num_seqs, int32_t max_c
 // 256-byte boundary.
 size_t align_up(size_t n) { return (n + kWsAlign - 1) / kWsAlign * kWsAlign; }
 
-size_t partial_rows(const pkv_cache_desc* d, int32_t num_seqs, int32_t workers) {
-  return ((size_t)workers + (size_t)num_seqs * d->num_kv_heads) * (d->num_q_heads / d->num_kv_heads);
+// Partial-state rows: (workers + pairs) pieces of q_len * group columns.
+size_t partial_rows(const pkv_cache_desc* d, int32_t num_seqs, int32_t q_len, int32_t workers) {
+  return ((size_t)workers + (size_t)num_seqs * d->num_kv_heads) * (size_t)q_len *
+         (d->num_q_heads / d->num_kv_heads);
 }
 
-size_t acc_bytes(const pkv_cache_desc* d, int32_t num_seqs, int32_t workers) {
-  return align_up(partial_rows(d, num_seqs, workers) * d->head_dim * sizeof(float));
+size_t acc_bytes(const pkv_cache_desc* d, int32_t num_seqs, int32_t q_len, int32_t workers) {
+  return align_up(partial_rows(d, num_seqs, q_len, workers) * d->head_dim * sizeof(float));
 }
 
-size_t ml_bytes(const pkv_cache_desc* d, int32_t num_seqs, int32_t workers) {
-  return align_up(partial_rows(d, num_seqs, workers) * 2 * sizeof(float));
+size_t ml_bytes(const pkv_cache_desc* d, int32_t num_seqs, int32_t q_len, int32_t workers) {
+  return align_up(partial_rows(d, num_seqs, q_len, workers) * 2 * sizeof(float));
 }
 
-size_t workspace_bytes(const pkv_cache_desc* d, int32_t num_seqs, int32_t workers) {
-  return acc_bytes(d, num_seqs, workers) + ml_bytes(d, num_seqs, workers) +
+size_t workspace_bytes(const pkv_cache_desc* d, int32_t num_seqs, int32_t q_len, int32_t workers) {
+  return acc_bytes(d, num_seqs, q_len, workers) + ml_bytes(d, num_seqs, q_len, workers) +
          align_up((size_t)num_seqs * d->num_kv_heads * 2 * sizeof(int32_t));
+}
+
+// q_len query tokens times the group's heads must fit the 16 MFMA columns.
+int check_q_len(const pkv_cache_desc* d, int32_t q_len) {
+  if (q_len < 1) return PKV_EINVAL;
+  if ((int64_t)q_len * (d->num_q_heads / d->num_kv_heads) > pkv::kMaxGroup) return PKV_EUNSUPPORTED;
+  return PKV_OK;
 }
 
 int check_decode_args(const pkv_cache_desc* d, const void* q, const void* k_pool, const void* v_pool,
@@ -110,7 +119,7 @@ int check_decode_args(const pkv_cache_desc* d, const void* q, const void* k_pool
 
 DecodeArgs make_args(const pkv_cache_desc* d, const void* q, const void* k_pool, const void* v_pool,
                      const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens,
-                     int32_t num_seqs, int32_t max_ctx, float scale, int32_t workers, void* out,
+                     int32_t num_seqs, int32_t q_len, int32_t max_ctx, float scale, int32_t workers, void* out,
                      void* workspace) {
   DecodeArgs a{};
   a.q = q;
@@ -125,6 +134,8 @@ DecodeArgs make_args(const pkv_cache_desc* d, const void* q, const void* k_pool,
   a.num_q_heads = d->num_q_heads;
   a.num_kv_heads = d->num_kv_heads;
   a.group = d->num_q_heads / d->num_kv_heads;
+  a.q_len = q_len;
+  a.cols = q_len * a.group;
   a.head_dim = d->head_dim;
   a.max_blocks = max_blocks;
   a.num_blocks = d->num_blocks;
@@ -134,8 +145,9 @@ DecodeArgs make_args(const pkv_cache_desc* d, const void* q, const void* k_pool,
   a.scale = scale;
   char* ws = static_cast<char*>(workspace);
   a.ws_acc = reinterpret_cast<float*>(ws);
-  a.ws_ml = reinterpret_cast<float*>(ws + acc_bytes(d, num_seqs, workers));
-  a.pair_meta = reinterpret_cast<int2*>(ws + acc_bytes(d, num_seqs, workers) + ml_bytes(d, num_seqs, workers));
+  a.ws_ml = reinterpret_cast<float*>(ws + acc_bytes(d, num_seqs, q_len, workers));
+  a.pair_meta = reinterpret_cast<int2*>(ws + acc_bytes(d, num_seqs, q_len, workers) +
+                                        ml_bytes(d, num_seqs, q_len, workers));
   return a;
 }
 
@@ -199,29 +211,45 @@ int32_t pkv_decode_workers(const pkv_cache_desc* desc, int32_t num_seqs, int32_t
   return default_workers(desc, num_seqs, max_context_len);
 }
 
-size_t pkv_decode_workspace_bytes(const pkv_cache_desc* desc, int32_t num_seqs, int32_t max_context_len,
-                                  int32_t num_workers) {
+size_t pkv_attention_workspace_bytes(const pkv_cache_desc* desc, int32_t num_seqs, int32_t q_len,
+                                     int32_t max_context_len, int32_t num_workers) {
   if (check_desc(desc) != PKV_OK || num_seqs < 0 || max_context_len < 0) return 0;
+  if (check_q_len(desc, q_len) != PKV_OK) return 0;
   const int32_t w = resolve_workers(desc, num_seqs, max_context_len, num_workers);
   if (w <= 0) return 0;
-  return workspace_bytes(desc, num_seqs, w);
+  return workspace_bytes(desc, num_seqs, q_len, w);
+}
+
+size_t pkv_decode_workspace_bytes(const pkv_cache_desc* desc, int32_t num_seqs, int32_t max_context_len,
+                                  int32_t num_workers) {
+  return pkv_attention_workspace_bytes(desc, num_seqs, 1, max_context_len, num_workers);
+}
+
+int pkv_paged_attention(const pkv_cache_desc* desc, const void* q, const void* k_pool, const void* v_pool,
+                        const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                        int32_t num_seqs, int32_t q_len, int32_t max_context_len, float scale, int32_t num_workers,
+                        void* out, void* workspace, size_t ws_bytes, void* stream) {
+  int st = check_decode_args(desc, q, k_pool, v_pool, block_tables, max_blocks_per_seq, context_lens,
+                             num_seqs, max_context_len, out);
+  if (st != PKV_OK) return st;
+  st = check_q_len(desc, q_len);
+  if (st != PKV_OK) return st;
+  const int32_t w = resolve_workers(desc, num_seqs, max_context_len, num_workers);
+  if (w <= 0) return w == 0 ? PKV_EINVAL : w;
+  if (num_seqs == 0) return PKV_OK;
+  if (!workspace || ws_bytes < workspace_bytes(desc, num_seqs, q_len, w)) return PKV_EWORKSPACE;
+  if (!aligned16(workspace)) return PKV_EINVAL;
+  DecodeArgs a = make_args(desc, q, k_pool, v_pool, block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                           q_len, max_context_len, scale, w, out, workspace);
+  return launch_status(pkv::launch_decode(a, static_cast<hipStream_t>(stream)));
 }
 
 int pkv_paged_decode_ex(const pkv_cache_desc* desc, const void* q, const void* k_pool, const void* v_pool,
                         const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
                         int32_t num_seqs, int32_t max_context_len, float scale, int32_t num_workers, void* out,
                         void* workspace, size_t ws_bytes, void* stream) {
-  int st = check_decode_args(desc, q, k_pool, v_pool, block_tables, max_blocks_per_seq, context_lens,
-                             num_seqs, max_context_len, out);
-  if (st != PKV_OK) return st;
-  const int32_t w = resolve_workers(desc, num_seqs, max_context_len, num_workers);
-  if (w <= 0) return w == 0 ? PKV_EINVAL : w;
-  if (num_seqs == 0) return PKV_OK;
-  if (!workspace || ws_bytes < workspace_bytes(desc, num_seqs, w)) return PKV_EWORKSPACE;
-  if (!aligned16(workspace)) return PKV_EINVAL;
-  DecodeArgs a = make_args(desc, q, k_pool, v_pool, block_tables, max_blocks_per_seq, context_lens, num_seqs,
-                           max_context_len, scale, w, out, workspace);
-  return launch_status(pkv::launch_decode(a, static_cast<hipStream_t>(stream)));
+  return pkv_paged_attention(desc, q, k_pool, v_pool, block_tables, max_blocks_per_seq, context_lens, num_seqs, 1,
+                             max_context_len, scale, num_workers, out, workspace, ws_bytes, stream);
 }
 
 int pkv_paged_decode(const pkv_cache_desc* desc, const void* q, const void* k_pool, const void* v_pool,

@@ -397,7 +397,14 @@ __device__ __forceinline__ void split_body(const DecodeArgs& a, const int32_t* _
   const int Hkv = a.num_kv_heads;
   const int G = a.group;
   const int Hq = a.num_q_heads;
+  const int L = a.q_len;       // query tokens per sequence (1 for decode)
+  const int NC = a.cols;       // MFMA columns in use: L * G (query token, query head) pairs
   OutT* out = static_cast<OutT*>(a.out);
+  // Column r of this lane: query token qi, head qh of the pair's group
+  // (padding columns r >= NC repeat the last real one and are never stored).
+  const int rc = min(r, NC - 1);
+  const int qi = rc / G;
+  const int qh = rc - qi * G;
 
   // ---- chunk totals over the batch ----
   int64_t total = 0;   // chunks per kv head over the batch
@@ -418,8 +425,8 @@ __device__ __forceinline__ void split_body(const DecodeArgs& a, const int32_t* _
   // and the merge kernel never needs the lengths.
   for (int b = wid; b < B; b += W) {
     if (seq_len(b) != 0) continue;
-    OutT* o = out + (size_t)b * Hq * D;
-    for (int e = lane; e < Hq * D; e += 64) o[e] = (OutT)0.f;
+    OutT* o = out + (size_t)b * L * Hq * D;
+    for (int e = lane; e < L * Hq * D; e += 64) o[e] = (OutT)0.f;
     for (int g = lane; g < Hkv; g += 64) a.pair_meta[b * Hkv + g] = int2{0, 0};
   }
 
@@ -498,8 +505,8 @@ __device__ __forceinline__ void split_body(const DecodeArgs& a, const int32_t* _
   typename T::Q qop, qA, qB;
   auto load_q = [&](typename T::Q& qq, const Pos& q) {
     const uint8_t* row = static_cast<const uint8_t*>(a.q) +
-                         ((size_t)q.b * Hq + q.g * G + min(r, G - 1)) * D * kQBytes;
-    T::load_q(qq, row, r < G, j);
+                         (((size_t)q.b * L + qi) * Hq + q.g * G + qh) * D * kQBytes;
+    T::load_q(qq, row, r < NC, j);
   };
   auto log2_scale = [&](int g) -> float {
     float sl = a.scale * kLog2e;
@@ -539,21 +546,21 @@ __device__ __forceinline__ void split_body(const DecodeArgs& a, const int32_t* _
       if (lane == 0) a.pair_meta[pair] = int2{wid, parts};
     }
     if (seg_c0 == 0 && q.c == q.cb - 1) {   // the whole pair: finish it here
-      if (r < G) {
-        OutT* dst = out + ((size_t)q.b * Hq + q.g * G + r) * D + 4 * j;
-        const float f = mul / l_tot;
+      if (r < NC) {
+        OutT* dst = out + (((size_t)q.b * L + qi) * Hq + q.g * G + qh) * D + 4 * j;
+        const float f = l_tot > 0.f ? mul / l_tot : 0.f;   // a query that sees no token gets zeros
 #pragma unroll
         for (int t = 0; t < kTiles; ++t) store4<OutT>(dst + 16 * t, acc[t] * f);
       }
     } else {
       const size_t slot = (size_t)wid + pair;
-      if (r < G) {
-        float* dst = a.ws_acc + (slot * G + r) * D + 4 * j;
+      if (r < NC) {
+        float* dst = a.ws_acc + (slot * NC + r) * D + 4 * j;
 #pragma unroll
         for (int t = 0; t < kTiles; ++t) *reinterpret_cast<f32x4*>(dst + 16 * t) = acc[t] * mul;
         if (j == 0) {
-          a.ws_ml[(slot * G + r) * 2] = m_run;
-          a.ws_ml[(slot * G + r) * 2 + 1] = l_tot;
+          a.ws_ml[(slot * NC + r) * 2] = m_run;
+          a.ws_ml[(slot * NC + r) * 2 + 1] = l_tot;
         }
       }
     }
@@ -575,19 +582,27 @@ __device__ __forceinline__ void split_body(const DecodeArgs& a, const int32_t* _
     T::scores(kb, qop, sx, sy);
     float t[8] = {sx[0] * sl, sx[1] * sl, sx[2] * sl, sx[3] * sl,
                   sy[0] * sl, sy[1] * sl, sy[2] * sl, sy[3] * sl};
-    if (t0 + kChunkTokens > q.n) {   // tail chunk: mask tokens at or past the end
-      const int nvalid = min(max(q.n - (t0 + 8 * j), 0), 8);
+    // Query token qi sits at position n - L + qi and sees the tokens below
+    // n - L + 1 + qi (causal; for decode, L = 1: every token below n).  V
+    // rows at or past n are zeroed, since they may hold anything (NaN too).
+    if (t0 + kChunkTokens > q.n - L + 1) {
+      const int nvalid = min(max(q.n - L + 1 + qi - (t0 + 8 * j), 0), 8);
 #pragma unroll
       for (int k = 0; k < 8; ++k)
         if (k >= nvalid) t[k] = -INFINITY;
-      T::mask_v(vb, nvalid);
+      T::mask_v(vb, min(max(q.n - (t0 + 8 * j), 0), 8));
     }
     float mloc = fmaxf(fmaxf(fmaxf(t[0], t[1]), fmaxf(t[2], t[3])),
                        fmaxf(fmaxf(t[4], t[5]), fmaxf(t[6], t[7])));
     mloc = row_max4(mloc);
     const float m_new = fmaxf(m_run, mloc);
-    if (__builtin_amdgcn_ballot_w64(m_new != m_run)) {
-      const float corr = exp2_fast(m_run - m_new);
+    // A column that has seen no token yet (several query tokens: a chunk past
+    // an early query's position) keeps max -inf.  It is exponentiated against
+    // 0 instead, so that its weights and its rescale factor are 0, never
+    // exp2(-inf - -inf).
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    if (__builtin_amdgcn_ballot_w64(m_new != m_run)) {   // some column's max grew
+      const float corr = exp2_fast(m_run - m_use);
 #pragma unroll
       for (int u = 0; u < kTiles; ++u) acc[u] *= corr;
       l_run *= corr;
@@ -595,7 +610,7 @@ __device__ __forceinline__ void split_body(const DecodeArgs& a, const int32_t* _
     m_run = m_new;
     float pk[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) pk[k] = exp2_fast(t[k] - m_new);
+    for (int k = 0; k < 8; ++k) pk[k] = exp2_fast(t[k] - m_use);
     l_run += T::pv(acc, vb, pk);
     if (q.c == q.cb - 1 || last_of_range) flush(q);
   };
@@ -670,30 +685,36 @@ template <typename OutT, int D>
 __global__ __launch_bounds__(128) void decode_merge_kernel(const int2* __restrict__ meta,
                                                            const float* __restrict__ ws_acc,
                                                            const float* __restrict__ ws_ml, OutT* __restrict__ out,
-                                                           int num_kv_heads, int group) {
+                                                           int num_kv_heads, int group, int q_len) {
   const int pair = blockIdx.x;
   const int2 m = meta[pair];
   if (m.y <= 1) return;   // one wave covered the pair and wrote its output
   const int G = group;
-  out += ((size_t)(pair / num_kv_heads) * num_kv_heads * G + (size_t)(pair % num_kv_heads) * G) * D;
-  for (int e = threadIdx.x; e < G * (D / 4); e += 128) {
-    const int h = e / (D / 4);
+  const int NC = q_len * G;   // (query token, query head) columns of the pair
+  const int b = pair / num_kv_heads;
+  const int g = pair - b * num_kv_heads;
+  const size_t Hq = (size_t)num_kv_heads * G;
+  for (int e = threadIdx.x; e < NC * (D / 4); e += 128) {
+    const int c = e / (D / 4);
     const int q4 = e % (D / 4);
+    const int qi = c / G;
     float M = -INFINITY, L = 0.f;
     f32x4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
     for (int w = m.x; w < m.x + m.y; ++w) {
-      const size_t slot = ((size_t)w + pair) * G + h;
+      const size_t slot = ((size_t)w + pair) * NC + c;
       const float2 ml = *reinterpret_cast<const float2*>(ws_ml + slot * 2);
       const f32x4 acc_w = *reinterpret_cast<const f32x4*>(ws_acc + slot * D + 4 * q4);
       const float M2 = fmaxf(M, ml.x);
-      const float f_old = exp2_fast(M - M2);
-      const float f_new = exp2_fast(ml.x - M2);
+      const float M2u = M2 == -INFINITY ? 0.f : M2;   // pieces that saw no token weigh 0
+      const float f_old = exp2_fast(M - M2u);
+      const float f_new = exp2_fast(ml.x - M2u);
       L = L * f_old + ml.y * f_new;
       o = o * f_old + acc_w * f_new;
       M = M2;
     }
-    store4<OutT>(out + (size_t)h * D + 4 * q4, o * (1.f / L));
+    OutT* dst = out + (((size_t)b * q_len + qi) * Hq + (size_t)g * G + (c - qi * G)) * D + 4 * q4;
+    store4<OutT>(dst, o * (L > 0.f ? 1.f / L : 0.f));
   }
 }
 
@@ -714,7 +735,8 @@ hipError_t launch_merge_t(const DecodeArgs& a, hipStream_t stream) {
   const unsigned grid = (unsigned)a.num_seqs * (unsigned)a.num_kv_heads;
   hipLaunchKernelGGL((decode_merge_kernel<OutT, D>), dim3(grid), dim3(128), 0, stream,
                      static_cast<const int2*>(a.pair_meta), static_cast<const float*>(a.ws_acc),
-                     static_cast<const float*>(a.ws_ml), static_cast<OutT*>(a.out), a.num_kv_heads, a.group);
+                     static_cast<const float*>(a.ws_ml), static_cast<OutT*>(a.out), a.num_kv_heads, a.group,
+                     a.q_len);
   return hipGetLastError();
 }
 

@@ -24,8 +24,8 @@ struct DecodeArgs {
   const float* k_scale;
   const float* v_scale;
   void* out;
-  float* ws_acc;   // [num_workers + pairs][group][head_dim]  partial accumulators
-  float* ws_ml;    // [num_workers + pairs][group][2]         (max in log2 units, sum)
+  float* ws_acc;   // [num_workers + pairs][cols][head_dim]  partial accumulators
+  float* ws_ml;    // [num_workers + pairs][cols][2]         (max in log2 units, sum)
   int2* pair_meta;      // [pairs] (first wave, parts) of each non-empty pair
   int32_t num_seqs;
   int32_t num_q_heads;
@@ -35,6 +35,8 @@ struct DecodeArgs {
   int32_t max_blocks;
   int32_t num_blocks;
   int32_t max_context_len;
+  int32_t q_len;         // query tokens per sequence (1 for decode)
+  int32_t cols;          // q_len * group: MFMA columns per (sequence, kv head) pair, <= 16
   int32_t num_workers;   // decode worker waves; a multiple of kDecodeWaves
   int32_t kv_dtype;
   float scale;

@@ -61,6 +61,8 @@ def library() -> ctypes.CDLL:
             "pkv_decode_workspace_bytes": (SZ, [D, I32, I32, I32]),
             "pkv_paged_decode": (ctypes.c_int, [D, P, P, P, P, I32, P, I32, I32, F, P, P, SZ, P]),
             "pkv_paged_decode_ex": (ctypes.c_int, [D, P, P, P, P, I32, P, I32, I32, F, I32, P, P, SZ, P]),
+            "pkv_paged_attention": (ctypes.c_int, [D, P, P, P, P, I32, P, I32, I32, I32, F, I32, P, P, SZ, P]),
+            "pkv_attention_workspace_bytes": (SZ, [D, I32, I32, I32, I32]),
             "pkv_strerror": (ctypes.c_char_p, [ctypes.c_int]),
             "pkv_version": (ctypes.c_char_p, []),
         }
@@ -205,6 +207,47 @@ def decode_workspace_bytes(k_pool, v_pool, num_q_heads: int, num_seqs: int, max_
 def new_workspace(nbytes: int, device) -> torch.Tensor:
     """A decode workspace (scratch; reusable by calls ordered on one stream)."""
     return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
+
+
+def attention_workspace_bytes(k_pool, v_pool, num_q_heads: int, num_seqs: int, q_len: int,
+                              max_context_len: int, num_workers: int = 0, k_scale=None, v_scale=None) -> int:
+    desc = cache_desc(k_pool, v_pool, num_q_heads, k_scale, v_scale)
+    return int(library().pkv_attention_workspace_bytes(ctypes.byref(desc), num_seqs, q_len, max_context_len,
+                                                       num_workers))
+
+
+def paged_attention(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                    block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
+                    out: Optional[torch.Tensor] = None, k_scale: Optional[torch.Tensor] = None,
+                    v_scale: Optional[torch.Tensor] = None, max_context_len: Optional[int] = None,
+                    workspace: Optional[torch.Tensor] = None, num_workers: int = 0,
+                    stream=None) -> torch.Tensor:
+    """Causal attention of the last ``L`` tokens of each sequence: q and out ``[B, L, Hq, D]``."""
+    _require(q, "q", (torch.float32, torch.bfloat16), 4)
+    B, L, Hq, D = q.shape
+    desc, _ = _decode_checks(q.view(B, L * Hq, D), k_pool, v_pool, block_tables, context_lens, k_scale, v_scale,
+                             None)
+    desc.num_q_heads = Hq
+    if out is None:
+        out = torch.empty_like(q)
+    _require(out, "out", (q.dtype,), 4)
+    if out.shape != q.shape:
+        raise ValueError("out must have the shape of q")
+    mctx = _max_ctx(block_tables, max_context_len)
+    lib = library()
+    need = lib.pkv_attention_workspace_bytes(ctypes.byref(desc), B, L, mctx, int(num_workers))
+    if need == 0 and B > 0:
+        _check(-2 if L * (Hq // desc.num_kv_heads) > 16 else -1, "pkv_attention_workspace_bytes")
+    if workspace is None:
+        workspace = new_workspace(need, q.device)
+    wbytes = workspace.numel() * workspace.element_size()
+    if workspace.device.type != "cuda" or wbytes < need:
+        raise ValueError(f"workspace must be a device buffer of at least {need} bytes")
+    _check(lib.pkv_paged_attention(ctypes.byref(desc), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
+                                   block_tables.shape[1], _ptr(context_lens), B, L, mctx, float(scale),
+                                   int(num_workers), _ptr(out), _ptr(workspace), wbytes, _stream(stream)),
+           "pkv_paged_attention")
+    return out
 
 
 def paged_decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,

@@ -1,0 +1,90 @@
+"""GPU parity of causal attention for several query tokens per sequence
+(pkv_paged_attention) against the oracle, through the C ABI."""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from paged_kv_cache_23_amd import ops
+from paged_kv_cache_23_amd.workloads import build_workload, storage_numpy
+from tests.gpu_util import Dev, assert_close, out_f64
+from tests.oracle_inputs import oracle_args
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(kv_dtype, D, G, L, lens, seed, Hkv=2):
+    wl = build_workload("multi", lens, G * Hkv, Hkv, D, kv_dtype, seed=seed)
+    gen = torch.Generator().manual_seed(seed + 100)
+    qd = torch.float32 if kv_dtype == "f32" else torch.bfloat16
+    q = torch.randn((wl.batch, L, G * Hkv, D), generator=gen).to(qd)
+    return wl, q
+
+
+def _run(wl, q, workers=0):
+    dev = Dev(wl)
+    return ops.paged_attention(q.to(dev.q.device), dev.k_pool, dev.v_pool, dev.tables, dev.lens, wl.scale,
+                               k_scale=dev.k_scale, v_scale=dev.v_scale,
+                               max_context_len=int(wl.context_lens.max()), num_workers=workers)
+
+
+def _ref(wl, q):
+    return oracle.oracle_attention_multi(**dict(oracle_args(wl), q=storage_numpy(q)))
+
+
+@pytest.mark.parametrize("kv_dtype,D,G,L", [
+    ("f32", 64, 2, 4), ("bf16", 128, 4, 4), ("bf16", 128, 8, 2), ("fp8", 128, 4, 3),
+    ("bf16", 64, 1, 16), ("fp8", 64, 2, 8), ("f32", 128, 4, 2), ("bf16", 128, 16, 1),
+])
+def test_multi_token_parity(kv_dtype, D, G, L):
+    lens = [L, L + 1, 31, 32, 33, 63, 64, 65, 200, 777]
+    wl, q = _case(kv_dtype, D, G, L, lens, seed=50 + L)
+    print(f"multi {kv_dtype} D={D} G={G} L={L}", flush=True)
+    out = _run(wl, q)
+    assert out.shape == q.shape
+    ref = _ref(wl, q)
+    assert_close(out.reshape(wl.batch, L * G * 2, D), ref.reshape(wl.batch, L * G * 2, D), kv_dtype)
+
+
+@pytest.mark.parametrize("workers", [4, 8, 12, 64, 1024])
+def test_multi_token_any_worker_count(workers):
+    """Small ranges cut pairs everywhere, so some pieces hold only a sequence's
+    last chunk, where early query tokens see nothing."""
+    lens = [4, 5, 33, 34, 35, 36, 70, 97, 129, 300]
+    wl, q = _case("bf16", 128, 4, 4, lens, seed=61)
+    print(f"multi workers={workers}", flush=True)
+    out = _run(wl, q, workers)
+    ref = _ref(wl, q)
+    assert_close(out.reshape(wl.batch, 32, 128), ref.reshape(wl.batch, 32, 128), "bf16")
+
+
+def test_one_query_token_is_the_decode():
+    wl, q = _case("bf16", 128, 4, 1, [1, 17, 64, 1000], seed=62)
+    dev = Dev(wl)
+    a = _run(wl, q)[:, 0]
+    b = ops.paged_decode(q[:, 0].contiguous().to(dev.q.device), dev.k_pool, dev.v_pool, dev.tables, dev.lens,
+                         wl.scale, max_context_len=1000)
+    assert torch.equal(a.cpu(), b.cpu())
+
+
+def test_fewer_tokens_than_queries():
+    """n < L: queries that see no token get zeros; the others attend to the
+    tokens before their position."""
+    L = 4
+    wl, q = _case("bf16", 128, 4, L, [2, 3, 40], seed=63)
+    out = out_f64(_run(wl, q))
+    args = oracle_args(wl)
+    qh = storage_numpy(q)
+    for i in range(L):
+        vis = args["context_lens"] - L + 1 + i
+        ref = oracle.oracle_decode(**dict(args, q=qh[:, i], context_lens=np.maximum(vis, 0)))
+        assert_close(torch.from_numpy(out[:, i]), ref, "bf16")
+
+
+def test_too_many_columns_is_unsupported():
+    wl, q = _case("bf16", 128, 4, 5, [40], seed=64)   # 5 * 4 = 20 columns
+    with pytest.raises(RuntimeError, match="unsupported"):
+        _run(wl, q)
