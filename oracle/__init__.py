@@ -13,6 +13,7 @@ source pages (cited in each docstring) and can be checked against them by eye.
 from .paged_attention import (  # noqa: F401
     BLOCK_SIZE,
     bf16_bits_to_f64,
+    block_size_of,
     e4m3_decode,
     e4m3_encode,
     gather_slab,

@@ -26,10 +26,11 @@ Sources (all readings are the plainest the pages support):
 Layout reading (the pages print a third-party API's layout only; this
 library stores tiles so that one (block, kv-head) tile is contiguous):
 
-* K pool: ``[num_blocks, num_kv_heads, 16, head_dim]``  (token-major tile)
-* V pool: ``[num_blocks, num_kv_heads, head_dim, 16]``  (dim-major tile)
-* slot s (int64) names block ``s // 16`` and offset ``s % 16``; a slot
-  outside ``[0, num_blocks * 16)`` is padding and writes nothing.
+* K pool: ``[num_blocks, num_kv_heads, B, head_dim]``  (token-major tile)
+* V pool: ``[num_blocks, num_kv_heads, head_dim, B]``  (dim-major tile)
+* B tokens per block, 16 by default (taken from the pool's shape);
+* slot s (int64) names block ``s // B`` and offset ``s % B``; a slot
+  outside ``[0, num_blocks * B)`` is padding and writes nothing.
 
 Storage dtypes are given by name: ``"f32"`` (float32 arrays), ``"bf16"``
 (uint16 arrays holding the bf16 bit patterns) and ``"fp8"`` (uint8 arrays
@@ -40,7 +41,18 @@ from __future__ import annotations
 
 import numpy as np
 
-BLOCK_SIZE = 16  # tokens per block: Habr article §4, "Blocks and block table"
+BLOCK_SIZE = 16  # default tokens per block: Habr article §4, "Blocks and block table"
+
+
+def block_size_of(k_pool) -> int:
+    """Tokens per block of a K pool ``[num_blocks, Hkv, block_size, D]``.
+
+    Habr article §4, "Choosing the block size": 16 is the default; larger
+    blocks (up to 256 in the page's table) trade internal fragmentation for a
+    smaller block table.  Every function here takes the block size from the
+    pools it is given.
+    """
+    return int(np.shape(k_pool)[2])
 
 
 # --------------------------------------------------------------------------
@@ -146,12 +158,13 @@ def oracle_append(k_pool, v_pool, k_new, v_new, slot_mapping, kv_dtype: str,
     slots = np.asarray(slot_mapping, dtype=np.int64)
     T = slots.shape[0]
     num_kv_heads = k_out.shape[1]
-    num_slots = k_out.shape[0] * BLOCK_SIZE
+    bs = block_size_of(k_out)
+    num_slots = k_out.shape[0] * bs
     for i in range(T):
         s = int(slots[i])
         if s < 0 or s >= num_slots:
             continue  # padding token: nothing to write
-        blk, off = s // BLOCK_SIZE, s % BLOCK_SIZE
+        blk, off = s // bs, s % bs
         for h in range(num_kv_heads):
             if kv_dtype == "fp8":
                 kx = bf16_bits_to_f64(k_new[i, h]).astype(np.float32)
@@ -197,17 +210,18 @@ def gather_slab(pool, table_row, n: int, which: str, head: int) -> np.ndarray:
     """Copy the first n tokens of one sequence and one kv head into a slab.
 
     Logical block j of the sequence lives in physical block
-    ``table_row[j]``; only blocks j < ceil(n / 16) are read, and only the
-    first n - 16 j tokens of the last one.  Returns ``[n, D]`` in the pool's
-    storage dtype.
+    ``table_row[j]``; with B tokens per block, only blocks j < ceil(n / B)
+    are read, and only the first n - B j tokens of the last one.  Returns
+    ``[n, D]`` in the pool's storage dtype.
     """
     head_dim = pool.shape[3] if which == "k" else pool.shape[2]
+    bs = pool.shape[2] if which == "k" else pool.shape[3]
     slab = np.empty((n, head_dim), dtype=pool.dtype)
-    num_blocks = (n + BLOCK_SIZE - 1) // BLOCK_SIZE
+    num_blocks = (n + bs - 1) // bs
     for j in range(num_blocks):
         phys = int(table_row[j])
-        lo = j * BLOCK_SIZE
-        cnt = min(BLOCK_SIZE, n - lo)
+        lo = j * bs
+        cnt = min(bs, n - lo)
         if which == "k":
             slab[lo:lo + cnt] = pool[phys, head, :cnt, :]
         else:

@@ -17,7 +17,7 @@ each new token is written to.  It follows
 * "Why one character breaks the cache", section on PagedAttention as
   virtual memory: each block carries a ref_cnt of the requests holding it.
 
-Slots are flat, 0-based: ``slot = physical_block * 16 + offset``.  The
+Slots are flat, 0-based: ``slot = physical_block * block_size + offset``.  The
 manager is single-threaded by design (the same article, §8, explains why a
 single-threaded scheduler needs no locks around the table).
 """
@@ -48,7 +48,9 @@ class _Sequence:
 
 
 class BlockManager:
-    """Free list + refcounts over ``num_blocks`` physical blocks of 16 tokens.
+    """Free list + refcounts over ``num_blocks`` physical blocks of
+    ``block_size`` tokens (16 by default; Habr article §4, "Choosing the block
+    size": larger blocks shrink the table, smaller ones waste fewer slots).
 
     ``free_order`` fixes the order in which free blocks are handed out (a
     seeded permutation gives the scattered placement the pages describe as
@@ -57,8 +59,8 @@ class BlockManager:
 
     def __init__(self, num_blocks: int, free_order: Optional[Iterable[int]] = None,
                  block_size: int = BLOCK_SIZE):
-        if block_size != BLOCK_SIZE:
-            raise ValueError("only 16-token blocks are supported")
+        if block_size <= 0:
+            raise ValueError("block_size must be positive")
         self.num_blocks = int(num_blocks)
         self.block_size = block_size
         order = list(range(self.num_blocks)) if free_order is None else [int(b) for b in free_order]

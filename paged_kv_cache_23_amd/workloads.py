@@ -101,34 +101,35 @@ def build_workload(name: str, context_lens: Sequence[int], num_q_heads: int, num
                    head_dim: int, kv_dtype: str, seed: int, *, shared_prefix: int = 0,
                    with_append: bool = False, num_blocks: Optional[int] = None,
                    max_blocks: Optional[int] = None,
-                   rng: Optional[np.random.Generator] = None) -> Workload:
+                   rng: Optional[np.random.Generator] = None, block_size: int = BLOCK_SIZE) -> Workload:
     """Seeded workload: pool, tables and queries for one decode step of one layer.
 
-    ``shared_prefix`` tokens (a multiple of 16) are held once, in refcounted
-    blocks that every sequence's table points at.  ``with_append`` also draws
-    one new token per sequence and reserves its slot.
+    ``shared_prefix`` tokens (a multiple of the block size) are held once, in
+    refcounted blocks that every sequence's table points at.  ``with_append``
+    also draws one new token per sequence and reserves its slot.
     """
+    BS = int(block_size)
     rng = np.random.default_rng(seed) if rng is None else rng
     gen = torch.Generator().manual_seed(seed)
     lens = [int(n) for n in context_lens]
     B = len(lens)
-    if shared_prefix % BLOCK_SIZE:
+    if shared_prefix % BS:
         raise ValueError("shared prefix must end on a block boundary")
     if any(n < shared_prefix for n in lens):
         raise ValueError("every sequence must hold the whole shared prefix")
 
     def nblk(n):
-        return (n + BLOCK_SIZE - 1) // BLOCK_SIZE
+        return (n + BS - 1) // BS
 
-    prefix_blocks = shared_prefix // BLOCK_SIZE
+    prefix_blocks = shared_prefix // BS
     needed = prefix_blocks + sum(nblk(n) - prefix_blocks for n in lens)
     if with_append:
-        needed += sum(1 for n in lens if n % BLOCK_SIZE == 0)
+        needed += sum(1 for n in lens if n % BS == 0)
     NB = needed + B if num_blocks is None else int(num_blocks)
     if NB < needed:
         raise ValueError(f"pool of {NB} blocks cannot hold {needed}")
 
-    bm = BlockManager(NB, free_order=rng.permutation(NB))
+    bm = BlockManager(NB, free_order=rng.permutation(NB), block_size=BS)
     if shared_prefix:
         root = bm.new_sequence(shared_prefix)
         ids = []
@@ -150,11 +151,11 @@ def build_workload(name: str, context_lens: Sequence[int], num_q_heads: int, num
     q = _randn((B, Hq, D), gen, _TORCH_DTYPE[q_dtype])
     k_scale = v_scale = None
     if kv_dtype == "fp8":
-        k_pool, k_scale = _fp8_pool((NB, Hkv, BLOCK_SIZE, D), gen)
-        v_pool, v_scale = _fp8_pool((NB, Hkv, D, BLOCK_SIZE), gen)
+        k_pool, k_scale = _fp8_pool((NB, Hkv, BS, D), gen)
+        v_pool, v_scale = _fp8_pool((NB, Hkv, D, BS), gen)
     else:
-        k_pool = _randn((NB, Hkv, BLOCK_SIZE, D), gen, _TORCH_DTYPE[kv_dtype])
-        v_pool = _randn((NB, Hkv, D, BLOCK_SIZE), gen, _TORCH_DTYPE[kv_dtype])
+        k_pool = _randn((NB, Hkv, BS, D), gen, _TORCH_DTYPE[kv_dtype])
+        v_pool = _randn((NB, Hkv, D, BS), gen, _TORCH_DTYPE[kv_dtype])
 
     wl = Workload(name=name, kv_dtype=kv_dtype, q_dtype=q_dtype, num_blocks=NB,
                   num_kv_heads=Hkv, num_q_heads=Hq, head_dim=D, q=q,

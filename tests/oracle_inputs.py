@@ -34,3 +34,48 @@ def oracle_append_args(wl: Workload):
 
 def f32_bits(x) -> np.ndarray:
     return np.asarray(x, dtype=np.float32)
+
+
+def relayout(wl: Workload, block_size: int, seed: int, poison: bool = True):
+    """The same logical cache in pools of another block size (test-side data
+    movement): every sequence's tokens, read through its table, are placed in
+    fresh blocks of ``block_size`` tokens dealt out in a seeded order.  Slots
+    past each sequence's length (and unused blocks) hold NaN (fp8: the NaN
+    code) when ``poison``, so a kernel that reads them shows it.
+    Returns (k_pool, v_pool, block_tables) as host torch tensors."""
+    import torch
+
+    rng = np.random.default_rng(seed)
+    kp, vp = wl.k_pool, wl.v_pool
+    old_bs = kp.shape[2]
+    tables = wl.block_tables.numpy()
+    lens = wl.context_lens.numpy()
+    nblk = [-(-int(n) // block_size) for n in lens]
+    NB = sum(nblk) + 2
+    Hkv, D = kp.shape[1], kp.shape[3]
+    if kp.dtype == torch.uint8:
+        k2 = torch.full((NB, Hkv, block_size, D), 0x7F if poison else 0, dtype=torch.uint8)
+        v2 = torch.full((NB, Hkv, D, block_size), 0x7F if poison else 0, dtype=torch.uint8)
+    else:
+        k2 = torch.full((NB, Hkv, block_size, D), float("nan") if poison else 0.0, dtype=kp.dtype)
+        v2 = torch.full((NB, Hkv, D, block_size), float("nan") if poison else 0.0, dtype=kp.dtype)
+    perm = rng.permutation(NB)
+    t2 = np.full((len(lens), max(max(nblk), 1)), -1, dtype=np.int32)
+    nxt = 0
+    for b, n in enumerate(lens):
+        n = int(n)
+        for j in range(nblk[b]):
+            t2[b, j] = perm[nxt]
+            nxt += 1
+        if n == 0:
+            continue
+        t = np.arange(n)
+        src_blk = torch.from_numpy(tables[b][t // old_bs].astype(np.int64))
+        src_off = torch.from_numpy((t % old_bs).astype(np.int64))
+        dst_blk = torch.from_numpy(t2[b][t // block_size].astype(np.int64))
+        dst_off = torch.from_numpy((t % block_size).astype(np.int64))
+        k_rows = kp[src_blk, :, src_off, :]                 # [n, Hkv, D]
+        v_rows = vp[src_blk, :, :, src_off]                 # [n, Hkv, D]
+        k2[dst_blk, :, dst_off, :] = k_rows
+        v2[dst_blk, :, :, dst_off] = v_rows
+    return k2, v2, torch.from_numpy(t2)

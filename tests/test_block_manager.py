@@ -159,3 +159,17 @@ def test_copy_on_write_gives_a_private_block():
     used = bm.blocks_in_use()
     bm.free_sequence(c2)
     assert bm.blocks_in_use() == used - 1 and bm.ref_count[1] == 1
+
+
+@pytest.mark.parametrize("bs,worst", [(16, 15), (256, 255)])
+def test_block_size_bounds_the_waste(bs, worst):
+    """Habr §4 "Choosing the block size": 16-token blocks waste at most 15
+    slots per request, 256-token blocks up to 255."""
+    bm = BlockManager(4096, block_size=bs)
+    wastes = []
+    for n in range(1, 3 * bs + 2):
+        s = bm.new_sequence(n)
+        wastes.append(bm.wasted_slots(s))
+        assert bm.allocated_slots(s) == -(-n // bs) * bs
+        bm.free_sequence(s)
+    assert max(wastes) == worst and min(wastes) == 0

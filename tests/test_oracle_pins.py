@@ -444,3 +444,42 @@ def test_multi_token_needs_the_tokens_in_the_cache():
     args = oracle_args(wl)
     with pytest.raises(ValueError):
         oracle.oracle_attention_multi(**dict(args, q=q, context_lens=args["context_lens"] - 1))
+
+
+@pytest.mark.parametrize("kv_dtype", ["f32", "bf16", "fp8"])
+def test_block_size_does_not_change_the_result(kv_dtype):
+    """Habr §4 "Choosing the block size": the block size is a memory-layout
+    choice; the same logical cache held in 16-, 32-, 64- or 256-token blocks
+    (tails poisoned with NaN) decodes to the same bits, and a multi-token
+    pass too."""
+    from tests.oracle_inputs import relayout
+    D = 64 if kv_dtype == "f32" else 32
+    wl = build_workload("bs", [1, 16, 17, 63, 100, 300], 8, 2, D, kv_dtype, seed=14)
+    args = oracle_args(wl)
+    base = oracle.oracle_decode(**args)
+    gen = torch.Generator().manual_seed(3)
+    q3 = storage_numpy(torch.randn((wl.batch, 1, 8, D), generator=gen).to(wl.q.dtype))
+    base_multi = oracle.oracle_attention_multi(**dict(args, q=q3))
+    for bs in (16, 32, 64, 256):
+        k2, v2, t2 = relayout(wl, bs, seed=bs)
+        assert oracle.block_size_of(storage_numpy(k2)) == bs
+        a2 = dict(args, k_pool=storage_numpy(k2), v_pool=storage_numpy(v2), block_tables=t2.numpy())
+        assert np.array_equal(oracle.oracle_decode(**a2), base)
+        assert np.array_equal(oracle.oracle_attention_multi(**dict(a2, q=q3)), base_multi)
+
+
+def test_append_at_other_block_sizes():
+    """slot = block * B + offset: the appended token lands at offset
+    slot % B of block slot // B for B = 32 and 256 (K row, V column)."""
+    rng = np.random.default_rng(8)
+    for bs in (32, 256):
+        kp = rng.standard_normal((3, 2, bs, 8)).astype(np.float32)
+        vp = rng.standard_normal((3, 2, 8, bs)).astype(np.float32)
+        kn = rng.standard_normal((2, 2, 8)).astype(np.float32)
+        vn = rng.standard_normal((2, 2, 8)).astype(np.float32)
+        slots = np.array([1 * bs + 5, 2 * bs + bs - 1], dtype=np.int64)
+        k2, v2 = oracle.oracle_append(kp, vp, kn, vn, slots, "f32")
+        assert np.array_equal(k2[1, :, 5, :], kn[0]) and np.array_equal(v2[1, :, :, 5], vn[0])
+        assert np.array_equal(k2[2, :, bs - 1, :], kn[1]) and np.array_equal(v2[2, :, :, bs - 1], vn[1])
+        changed = (k2 != kp).any(axis=(1, 3))
+        assert changed.sum() == 2 and changed[1, 5] and changed[2, bs - 1]
