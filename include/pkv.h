@@ -25,11 +25,12 @@
  * Layout (this library's choice; one (block, kv head) tile is contiguous):
  *   q       [num_seqs][num_q_heads][head_dim]                 q_dtype
  *   out     [num_seqs][num_q_heads][head_dim]                 q_dtype
- *   k_pool  [num_blocks][num_kv_heads][16][head_dim]          kv_dtype (token-major tile)
- *   v_pool  [num_blocks][num_kv_heads][head_dim][16]          kv_dtype (dim-major tile)
+ *   k_pool  [num_blocks][num_kv_heads][B][head_dim]           kv_dtype (token-major tile)
+ *   v_pool  [num_blocks][num_kv_heads][head_dim][B]           kv_dtype (dim-major tile)
  *   block_tables [num_seqs][max_blocks_per_seq] int32 physical block ids
  *   context_lens [num_seqs] int32, tokens held by each sequence
- *   slot_mapping [num_tokens] int64, slot = block * 16 + offset
+ *   slot_mapping [num_tokens] int64, slot = block * B + offset
+ * where B = desc->block_size tokens per block.
  * Query head h reads kv head h / (num_q_heads / num_kv_heads): contiguous
  * query groups share a kv head (grouped-query attention, Habr article
  * section 2, "GQA: 8x reduction").
@@ -56,7 +57,7 @@ extern "C" {
 #define PKV_ELAUNCH (-4)      /* the HIP runtime reported an error (host: out of memory) */
 #define PKV_ENOSPACE (-5)     /* the block pool has too few free blocks */
 
-#define PKV_BLOCK_SIZE 16
+#define PKV_BLOCK_SIZE 16   /* the default; 32, 64, 128 and 256 are supported too */
 
 typedef enum pkv_dtype {
   PKV_F32 = 0,      /* IEEE binary32 */
@@ -65,7 +66,10 @@ typedef enum pkv_dtype {
 } pkv_dtype;
 
 /* Shape and format of one layer's cache.
- * Supported: head_dim 64 or 128; block_size 16; num_q_heads a multiple of
+ * Supported: head_dim 64 or 128; block_size 16, 32, 64, 128 or 256 tokens
+ * (Habr article, section 4, "Choosing the block size": 16 is the default;
+ * larger blocks shrink the table for very long sequences at the cost of up
+ * to block_size - 1 unused slots per sequence); num_q_heads a multiple of
  * num_kv_heads with at most 16 query heads per kv head; (kv, q) dtypes
  * (F32, F32), (BF16, BF16) or (FP8_E4M3, BF16).  For FP8 caches, k_scale and
  * v_scale are device arrays [num_kv_heads] of float32: a stored code c of
@@ -88,7 +92,7 @@ typedef struct pkv_cache_desc {
  * the sequence's last block, the caller opening a fresh block when full.)
  *   k_new, v_new  device [num_tokens][num_kv_heads][head_dim]; q_dtype for an
  *                 FP8 cache (quantised here), else kv_dtype (bit copy)
- *   slot_mapping  device [num_tokens]; a slot outside [0, num_blocks * 16) is
+ *   slot_mapping  device [num_tokens]; a slot outside [0, num_blocks * B) is
  *                 padding and writes nothing
  *   k_pool, v_pool device pools, updated in place
  * FP8: code = E4M3 round-to-nearest-even, saturating to +-448, of the IEEE
@@ -101,7 +105,7 @@ int pkv_kv_append(const pkv_cache_desc* desc, const void* k_new, const void* v_n
 
 /* Copy whole blocks, for copy-on-write.  For every i < num_pairs, block
  * dst[i] of both pools (all kv heads, all 16 token slots) becomes a copy of
- * block src[i].  (Habr article, section 4, "Copy-on-Write for parallel
+ * block src[i] (all B token slots).  (Habr article, section 4, "Copy-on-Write for parallel
  * sampling": a sequence that must modify a block other sequences reference
  * copies it first and the original stays untouched; section 8 applies it to
  * a speculative correction.  The host allocator chooses dst and moves the
@@ -136,11 +140,11 @@ size_t pkv_decode_workspace_bytes(const pkv_cache_desc* desc, int32_t num_seqs,
 /* Decode attention for one query token per sequence over its paged cache:
  *   out[b][h] = softmax_t(scale * q[b][h] . K_b[t]) V_b[t],  t < context_lens[b]
  * where K_b / V_b are sequence b's tokens gathered through its block table,
- * and h reads kv head h / group.  Only table entries j < ceil(n / 16) are
+ * and h reads kv head h / group.  Only table entries j < ceil(n / B) are
  * read; token slots at or past n in the last block are ignored (they may
  * hold anything, NaN included).  A sequence of length 0 gets a zero output.
  * Lengths are taken as min(context_lens[b], max_context_len,
- * 16 * max_blocks_per_seq); block ids are clamped into [0, num_blocks).
+ * B * max_blocks_per_seq); block ids are clamped into [0, num_blocks).
  * Accumulation is float32; out is rounded once to q_dtype (nearest even).
  *
  * Two kernels on `stream`.  The batch's 32-token chunks of every (sequence,

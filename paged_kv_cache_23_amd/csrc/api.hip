@@ -16,11 +16,18 @@ constexpr size_t kWsAlign = 256;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// log2 of a supported block size (16, 32, 64, 128, 256), else -1.
+int block_shift(int32_t bs) {
+  for (int s = 4; s <= 8; ++s)
+    if (bs == (1 << s)) return s;
+  return -1;
+}
+
 int check_desc(const pkv_cache_desc* d) {
   if (!d) return PKV_EINVAL;
   if (d->num_blocks <= 0 || d->num_kv_heads <= 0 || d->num_q_heads <= 0 || d->head_dim <= 0)
     return PKV_EINVAL;
-  if (d->block_size != PKV_BLOCK_SIZE) return PKV_EINVAL;
+  if (block_shift(d->block_size) < 0) return PKV_EINVAL;
   if (d->num_q_heads % d->num_kv_heads != 0) return PKV_EINVAL;
   if (d->num_q_heads / d->num_kv_heads > pkv::kMaxGroup) return PKV_EUNSUPPORTED;
   if (d->head_dim != 64 && d->head_dim != 128) return PKV_EUNSUPPORTED;
@@ -136,6 +143,8 @@ DecodeArgs make_args(const pkv_cache_desc* d, const void* q, const void* k_pool,
   a.group = d->num_q_heads / d->num_kv_heads;
   a.q_len = q_len;
   a.cols = q_len * a.group;
+  a.block_size = d->block_size;
+  a.block_shift = block_shift(d->block_size);
   a.head_dim = d->head_dim;
   a.max_blocks = max_blocks;
   a.num_blocks = d->num_blocks;
@@ -177,6 +186,7 @@ int pkv_kv_append(const pkv_cache_desc* desc, const void* k_new, const void* v_n
   a.num_kv_heads = desc->num_kv_heads;
   a.head_dim = desc->head_dim;
   a.num_blocks = desc->num_blocks;
+  a.block_size = desc->block_size;
   a.kv_dtype = desc->kv_dtype;
   return launch_status(pkv::launch_append(a, static_cast<hipStream_t>(stream)));
 }
@@ -195,7 +205,7 @@ int pkv_copy_blocks(const pkv_cache_desc* desc, void* k_pool, void* v_pool, cons
   a.v_pool = v_pool;
   a.src = src;
   a.dst = dst;
-  a.block_bytes = (size_t)desc->num_kv_heads * PKV_BLOCK_SIZE * desc->head_dim * elt;
+  a.block_bytes = (size_t)desc->num_kv_heads * desc->block_size * desc->head_dim * elt;
   a.num_pairs = num_pairs;
   a.num_blocks = desc->num_blocks;
   const size_t slice = pkv::copy_slice_bytes();

@@ -4,11 +4,12 @@
 // and Decode": each decode step computes K and V for the new token only and
 // appends them to the cache.  Section 4, step-by-step example: the token
 // lands in the next slot of the sequence's last block (the host opened a
-// fresh block when the last one was full).  A slot is block * 16 + offset.
+// fresh block when the last one was full).  A slot is block * B + offset for
+// B tokens per block.
 //
 // One wave per (token, kv head).  K tiles are token-major, so a token's K
 // row is D contiguous elements; V tiles are dim-major, so its V column is D
-// elements 16 apart.  For an fp8 cache the bf16 input is divided by the kv
+// elements B apart.  For an fp8 cache the bf16 input is divided by the kv
 // head's float32 scale (IEEE division) and rounded to E4M3 below.
 
 #include "pkv_internal.h"
@@ -50,11 +51,12 @@ __global__ __launch_bounds__(64) void append_kernel(AppendArgs a) {
   const int i = item / a.num_kv_heads;
   const int h = item % a.num_kv_heads;
   const int64_t slot = a.slot_mapping[i];
-  if (slot < 0 || slot >= (int64_t)a.num_blocks * kBlockTokens) return;  // padding
-  const int64_t blk = slot >> 4;
-  const int off = (int)(slot & 15);
+  const int bs = a.block_size;
+  if (slot < 0 || slot >= (int64_t)a.num_blocks * bs) return;  // padding
+  const int64_t blk = slot / bs;
+  const int off = (int)(slot - blk * bs);
   const size_t src = ((size_t)i * a.num_kv_heads + h) * D;
-  const size_t ktile = ((size_t)blk * a.num_kv_heads + h) * kBlockTokens * D;
+  const size_t ktile = ((size_t)blk * a.num_kv_heads + h) * bs * D;
   const size_t kdst = ktile + (size_t)off * D;     // token-major: row `off`
   const size_t vdst = ktile + off;                 // dim-major: column `off`
   for (int d = threadIdx.x; d < D; d += 64) {
@@ -64,12 +66,12 @@ __global__ __launch_bounds__(64) void append_kernel(AppendArgs a) {
       const float kx = __builtin_bit_cast(float, (uint32_t)kn[src + d] << 16);
       const float vx = __builtin_bit_cast(float, (uint32_t)vn[src + d] << 16);
       static_cast<uint8_t*>(a.k_pool)[kdst + d] = (uint8_t)e4m3_from_f32(__fdiv_rn(kx, a.k_scale[h]));
-      static_cast<uint8_t*>(a.v_pool)[vdst + (size_t)d * kBlockTokens] =
+      static_cast<uint8_t*>(a.v_pool)[vdst + (size_t)d * bs] =
           (uint8_t)e4m3_from_f32(__fdiv_rn(vx, a.v_scale[h]));
     } else {
       using E = typename std::conditional<KV == kF32, uint32_t, uint16_t>::type;
       static_cast<E*>(a.k_pool)[kdst + d] = static_cast<const E*>(a.k_new)[src + d];
-      static_cast<E*>(a.v_pool)[vdst + (size_t)d * kBlockTokens] = static_cast<const E*>(a.v_new)[src + d];
+      static_cast<E*>(a.v_pool)[vdst + (size_t)d * bs] = static_cast<const E*>(a.v_new)[src + d];
     }
   }
 }

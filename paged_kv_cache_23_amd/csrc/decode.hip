@@ -108,7 +108,8 @@ struct TileBF16 {
       q.op[s] = __builtin_bit_cast(bf16x8, v);
     }
   }
-  // tile: K tile [16][D] of block r / 8 for this lane.
+  // tile: the first of the 16 token rows of this lane's half-chunk (half
+  // r / 8) inside its block's token-major K tile.
   __device__ static void load_k(K& k, const Elem* tile, int r, int j) {
     const Elem* rx = tile + row_token(r, 0) * D + 8 * j;
     const Elem* ry = tile + row_token(r, 1) * D + 8 * j;
@@ -118,11 +119,12 @@ struct TileBF16 {
       k.y[s] = *reinterpret_cast<const u32x4*>(ry + 32 * s);
     }
   }
-  // tile: V^T tile [D][16] of block j / 2 for this lane.
-  __device__ static void load_v(V& v, const Elem* tile, int r, int j) {
-    const Elem* base = tile + r * 16 + 8 * (j & 1);
+  // tile: this lane's half-chunk inside the V^T tile [D][bs] (dim rows of
+  // bs tokens); the lane reads dims 16 t + r, tokens 8 (j % 2) .. +7.
+  __device__ static void load_v(V& v, const Elem* tile, int r, int j, int bs) {
+    const Elem* base = tile + r * bs + 8 * (j & 1);
 #pragma unroll
-    for (int t = 0; t < kTiles; ++t) v.t[t] = *reinterpret_cast<const u32x4*>(base + t * 256);
+    for (int t = 0; t < kTiles; ++t) v.t[t] = *reinterpret_cast<const u32x4*>(base + (size_t)t * 16 * bs);
   }
   __device__ static void scores(const K& k, const Q& q, f32x4& sx, f32x4& sy) {
     sx = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -195,10 +197,10 @@ struct TileFP8 {
       k.y[s] = *reinterpret_cast<const u32x4*>(ry + 16 * s);
     }
   }
-  __device__ static void load_v(V& v, const Elem* tile, int r, int j) {
-    const Elem* base = tile + r * 16 + 8 * (j & 1);
+  __device__ static void load_v(V& v, const Elem* tile, int r, int j, int bs) {
+    const Elem* base = tile + r * bs + 8 * (j & 1);
 #pragma unroll
-    for (int t = 0; t < kTiles; ++t) v.t[t] = *reinterpret_cast<const u32x2*>(base + t * 256);
+    for (int t = 0; t < kTiles; ++t) v.t[t] = *reinterpret_cast<const u32x2*>(base + (size_t)t * 16 * bs);
   }
   __device__ static void scores(const K& k, const Q& q, f32x4& sx, f32x4& sy) {
     sx = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -270,12 +272,12 @@ struct TileF32 {
       k.y[a] = *reinterpret_cast<const f32x4*>(ry + 16 * a);
     }
   }
-  __device__ static void load_v(V& v, const Elem* tile, int r, int j) {
-    const float* base = tile + r * 16 + 8 * (j & 1);
+  __device__ static void load_v(V& v, const Elem* tile, int r, int j, int bs) {
+    const float* base = tile + r * bs + 8 * (j & 1);
 #pragma unroll
     for (int t = 0; t < kTiles; ++t) {
-      v.t[t][0] = *reinterpret_cast<const f32x4*>(base + t * 256);
-      v.t[t][1] = *reinterpret_cast<const f32x4*>(base + t * 256 + 4);
+      v.t[t][0] = *reinterpret_cast<const f32x4*>(base + (size_t)t * 16 * bs);
+      v.t[t][1] = *reinterpret_cast<const f32x4*>(base + (size_t)t * 16 * bs + 4);
     }
   }
   __device__ static void scores(const K& k, const Q& q, f32x4& sx, f32x4& sy) {
@@ -330,7 +332,7 @@ __device__ __forceinline__ void store4<__bf16>(__bf16* dst, f32x4 v) {
 
 __device__ __forceinline__ int clamp_len(int n, const DecodeArgs& a) {
   n = min(n, a.max_context_len);
-  n = min(n, a.max_blocks * kBlockTokens);
+  n = (int)min((int64_t)n, (int64_t)a.max_blocks * a.block_size);
   return max(n, 0);
 }
 
@@ -484,16 +486,21 @@ __device__ __forceinline__ void split_body(const DecodeArgs& a, const int32_t* _
     return q;
   };
 
-  const size_t blk_stride = (size_t)Hkv * kBlockTokens * D;   // elements per block
-  // Physical ids of a chunk's two blocks (scalar loads).  They are fetched one
+  const int bsz = a.block_size;         // tokens per block: 16 or a multiple of 32
+  const int bshift = a.block_shift;     // log2(bsz)
+  const size_t blk_stride = (size_t)Hkv * bsz * D;   // elements per block
+  // Physical ids of the blocks holding a chunk's two 16-token halves, tokens
+  // 32 c + 16 h of the sequence: logical block (32 c + 16 h) / bsz (two
+  // blocks at bsz = 16, one block otherwise).  Scalar loads, fetched one
   // chunk ahead of their use, so the table lookup never delays a prefetch.
   struct Ids {
     int id0, id1;
   };
   auto block_ids = [&](const Pos& q) -> Ids {
     const int32_t* table = tables + (size_t)q.b * a.max_blocks;
-    const int last = (q.n + kBlockTokens - 1) / kBlockTokens - 1;
-    return Ids{table[uni(min(2 * q.c, last))], table[uni(min(2 * q.c + 1, last))]};
+    const int last = ((q.n + bsz - 1) >> bshift) - 1;
+    const int t0 = q.c * kChunkTokens;
+    return Ids{table[uni(min(t0 >> bshift, last))], table[uni(min((t0 + 16) >> bshift, last))]};
   };
 
   // Query operand (and fp8 scales) of a pair.  Lane (r, j) holds head g*G + r;
@@ -521,10 +528,15 @@ __device__ __forceinline__ void split_body(const DecodeArgs& a, const int32_t* _
   auto issue = [&](typename T::K& kb, typename T::V& vb, typename T::Q& qn, const Pos& q, const Ids& ids) {
     const int id0 = uni(min(max(ids.id0, 0), a.num_blocks - 1));
     const int id1 = uni(min(max(ids.id1, 0), a.num_blocks - 1));
-    const Elem* kp = static_cast<const Elem*>(a.k_pool) + (size_t)q.g * kBlockTokens * D;
-    const Elem* vp = static_cast<const Elem*>(a.v_pool) + (size_t)q.g * kBlockTokens * D;
-    T::load_k(kb, kp + (size_t)((r >> 3) ? id1 : id0) * blk_stride, r, j);
-    T::load_v(vb, vp + (size_t)((j >> 1) ? id1 : id0) * blk_stride, r, j);
+    const int t0 = q.c * kChunkTokens;
+    const int off0 = t0 & (bsz - 1);          // the halves' offsets inside their blocks
+    const int off1 = (t0 + 16) & (bsz - 1);
+    const Elem* kp = static_cast<const Elem*>(a.k_pool) + (size_t)q.g * bsz * D;
+    const Elem* vp = static_cast<const Elem*>(a.v_pool) + (size_t)q.g * bsz * D;
+    const bool hk = (r >> 3) != 0;            // K rows: half by score row
+    const bool hv = (j >> 1) != 0;            // V rows: half by lane group
+    T::load_k(kb, kp + (size_t)(hk ? id1 : id0) * blk_stride + (size_t)(hk ? off1 : off0) * D, r, j);
+    T::load_v(vb, vp + (size_t)(hv ? id1 : id0) * blk_stride + (hv ? off1 : off0), r, j, bsz);
     if (q.c == 0) load_q(qn, q);   // first chunk of a pair: its query rides along
   };
 

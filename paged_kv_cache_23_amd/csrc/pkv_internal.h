@@ -7,7 +7,7 @@
 
 namespace pkv {
 
-constexpr int kBlockTokens = 16;    // tokens per cache block
+constexpr int kBlockTokens = 16;    // default tokens per cache block (also 32 ... 256)
 constexpr int kChunkTokens = 32;    // tokens one wave consumes per step: two blocks
 constexpr int kDecodeWaves = 4;     // worker waves per decode workgroup
 constexpr int kMaxGroup = 16;       // query heads per kv head that one MFMA column tile holds
@@ -35,6 +35,8 @@ struct DecodeArgs {
   int32_t max_blocks;
   int32_t num_blocks;
   int32_t max_context_len;
+  int32_t block_size;    // tokens per block: 16, 32, 64, 128 or 256
+  int32_t block_shift;   // log2(block_size)
   int32_t q_len;         // query tokens per sequence (1 for decode)
   int32_t cols;          // q_len * group: MFMA columns per (sequence, kv head) pair, <= 16
   int32_t num_workers;   // decode worker waves; a multiple of kDecodeWaves
@@ -54,6 +56,7 @@ struct AppendArgs {
   int32_t num_kv_heads;
   int32_t head_dim;
   int32_t num_blocks;
+  int32_t block_size;
   int32_t kv_dtype;
 };
 

@@ -7,8 +7,8 @@ computation runs in the library's HIP kernels; there is no fallback path.
 Shapes and the cache layout are documented in ``include/pkv.h``:
 
 * q, out   ``[B, Hq, D]``            float32 or bfloat16
-* k_pool   ``[NB, Hkv, 16, D]``      float32, bfloat16 or uint8 (E4M3 codes)
-* v_pool   ``[NB, Hkv, D, 16]``
+* k_pool   ``[NB, Hkv, B, D]``       float32, bfloat16 or uint8 (E4M3 codes)
+* v_pool   ``[NB, Hkv, D, B]``       B tokens per block: 16, 32, 64, 128 or 256
 * block_tables ``[B, max_blocks]`` int32, context_lens ``[B]`` int32
 * slot_mapping ``[T]`` int64; k_new / v_new ``[T, Hkv, D]``
 * copy src / dst ``[P]`` int32 block ids
@@ -114,14 +114,14 @@ def _kv_code(pool: torch.Tensor) -> int:
 def cache_desc(k_pool: torch.Tensor, v_pool: torch.Tensor, num_q_heads: int,
                k_scale: Optional[torch.Tensor] = None,
                v_scale: Optional[torch.Tensor] = None) -> CacheDesc:
-    """Descriptor for pools ``k_pool [NB, Hkv, 16, D]`` / ``v_pool [NB, Hkv, D, 16]``."""
+    """Descriptor for pools ``k_pool [NB, Hkv, B, D]`` / ``v_pool [NB, Hkv, D, B]``."""
     kv = _kv_code(k_pool)
     _require(k_pool, "k_pool", (k_pool.dtype,), 4)
     _require(v_pool, "v_pool", (k_pool.dtype,), 4)
     NB, Hkv, bs, D = k_pool.shape
-    if bs != BLOCK_SIZE or tuple(v_pool.shape) != (NB, Hkv, D, BLOCK_SIZE):
+    if tuple(v_pool.shape) != (NB, Hkv, D, bs):
         raise ValueError(f"pool shapes {tuple(k_pool.shape)} / {tuple(v_pool.shape)} do not match "
-                         "[NB, Hkv, 16, D] / [NB, Hkv, D, 16]")
+                         "[NB, Hkv, B, D] / [NB, Hkv, D, B]")
     if kv == FP8_E4M3:
         if k_scale is None or v_scale is None:
             raise ValueError("an fp8 cache needs k_scale and v_scale")
@@ -131,7 +131,7 @@ def cache_desc(k_pool: torch.Tensor, v_pool: torch.Tensor, num_q_heads: int,
                 raise ValueError(f"{name} must have {Hkv} entries")
     elif k_scale is not None or v_scale is not None:
         raise ValueError("scales are only used with an fp8 cache")
-    return CacheDesc(NB, BLOCK_SIZE, Hkv, int(num_q_heads), D, kv,
+    return CacheDesc(NB, bs, Hkv, int(num_q_heads), D, kv,
                      F32 if kv == F32 else BF16, _ptr(k_scale), _ptr(v_scale))
 
 
@@ -184,9 +184,9 @@ def _decode_checks(q, k_pool, v_pool, block_tables, context_lens, k_scale, v_sca
     return desc, out
 
 
-def _max_ctx(block_tables: torch.Tensor, max_context_len: Optional[int]) -> int:
+def _max_ctx(block_tables: torch.Tensor, max_context_len: Optional[int], block_size: int = BLOCK_SIZE) -> int:
     # without a host-side value, the table width bounds every length (no device sync)
-    return int(max_context_len) if max_context_len is not None else BLOCK_SIZE * block_tables.shape[1]
+    return int(max_context_len) if max_context_len is not None else block_size * block_tables.shape[1]
 
 
 def decode_workers(k_pool, v_pool, num_q_heads: int, num_seqs: int, max_context_len: int,
@@ -233,7 +233,7 @@ def paged_attention(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
     _require(out, "out", (q.dtype,), 4)
     if out.shape != q.shape:
         raise ValueError("out must have the shape of q")
-    mctx = _max_ctx(block_tables, max_context_len)
+    mctx = _max_ctx(block_tables, max_context_len, k_pool.shape[2])
     lib = library()
     need = lib.pkv_attention_workspace_bytes(ctypes.byref(desc), B, L, mctx, int(num_workers))
     if need == 0 and B > 0:
@@ -262,7 +262,7 @@ def paged_decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
     same shape and ``num_workers``; calls sharing it must run on one stream.
     """
     desc, out = _decode_checks(q, k_pool, v_pool, block_tables, context_lens, k_scale, v_scale, out)
-    mctx = _max_ctx(block_tables, max_context_len)
+    mctx = _max_ctx(block_tables, max_context_len, k_pool.shape[2])
     lib = library()
     need = lib.pkv_decode_workspace_bytes(ctypes.byref(desc), q.shape[0], mctx, int(num_workers))
     if need == 0 and q.shape[0] > 0:

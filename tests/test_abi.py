@@ -53,7 +53,9 @@ FAKE = 0x10000  # a non-null, 16-byte aligned address that is never dereferenced
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(block_size=32), EINVAL),
+    (dict(block_size=48), EINVAL),           # block sizes: 16, 32, 64, 128, 256
+    (dict(block_size=8), EINVAL),
+    (dict(block_size=512), EINVAL),
     (dict(num_blocks=0), EINVAL),
     (dict(num_q_heads=7), EINVAL),
     (dict(num_q_heads=64), EUNSUPPORTED),   # 32 query heads per kv head
