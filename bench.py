@@ -177,11 +177,12 @@ def unique_kv_bytes(wl, after_append: bool) -> int:
 
     tables = (wl.block_tables_after if after_append else wl.block_tables).numpy()
     lens = (wl.context_lens_after if after_append else wl.context_lens).numpy()
+    bs = wl.k_pool.shape[2]
     used = {}
     for row, n in zip(tables, lens):
-        nb = -(-int(n) // 16)
+        nb = -(-int(n) // bs)
         for j in range(nb):
-            t = min(16, int(n) - 16 * j)
+            t = min(bs, int(n) - bs * j)
             blk = int(row[j])
             if used.get(blk, 0) < t:
                 used[blk] = t
@@ -261,7 +262,7 @@ def run_bench(args) -> dict:
 
     from paged_kv_cache_23_amd import workloads as W
 
-    wl = W.WORKLOADS[args.workload]()
+    wl = W.WORKLOADS[args.workload](block_size=args.block_size)
     log(f"workload {wl.name}: B={wl.batch} Hq={wl.num_q_heads} Hkv={wl.num_kv_heads} D={wl.head_dim} "
         f"kv={wl.kv_dtype} blocks={wl.num_blocks} KV={wl.kv_bytes() / 1e6:.1f} MB")
     runner = Runner(wl, args.layers, args.workers, args.identity_tables, args.q_len)
@@ -330,7 +331,7 @@ def run_bench(args) -> dict:
         "data": "synthetic",
         "config": {
             "workload": f"{wl.name}: single-layer paged decode, batch {wl.batch}, {wl.num_q_heads} q / "
-                        f"{wl.num_kv_heads} kv heads, head_dim {wl.head_dim}, 16-token blocks, "
+                        f"{wl.num_kv_heads} kv heads, head_dim {wl.head_dim}, {args.block_size}-token blocks, "
                         f"shuffled pool, {args.layers}-layer pool rotation",
             "batch": wl.batch,
             "context_tokens": int((wl.context_lens_after if runner.append else wl.context_lens).sum()),
@@ -477,6 +478,7 @@ def main() -> int:
     p.add_argument("--profile-one", action="store_true")
     p.add_argument("--copy-probe", action="store_true")
     p.add_argument("--cow", action="store_true", help="time the copy-on-write block copy instead")
+    p.add_argument("--block-size", type=int, default=16, help="tokens per cache block (16, 32, 64, 128, 256)")
     p.add_argument("--q-len", type=int, default=1,
                    help="query tokens per sequence (speculative verification); 1 is the decode")
     args = p.parse_args()

@@ -178,54 +178,56 @@ def build_workload(name: str, context_lens: Sequence[int], num_q_heads: int, num
 # ---------------------------------------------------------------------------
 # The five workload shapes
 # ---------------------------------------------------------------------------
-def tiny_fp32(seed: int = 1) -> Workload:
+def tiny_fp32(seed: int = 1, block_size: int = BLOCK_SIZE) -> Workload:
     """4 sequences of 17/33/50/64 tokens, 4 q / 2 kv heads, D 64, fp32, 32-block
     pool in seeded random order, plus one appended token per sequence."""
     return build_workload("tiny-fp32", [17, 33, 50, 64], 4, 2, 64, "f32", seed,
-                          with_append=True, num_blocks=32)
+                          with_append=True, num_blocks=32 if block_size == BLOCK_SIZE else None,
+                          block_size=block_size)
 
 
-def llama8b_b64(seed: int = 2) -> Workload:
+def llama8b_b64(seed: int = 2, block_size: int = BLOCK_SIZE) -> Workload:
     """Llama-3-8B-shaped layer: batch 64, 32 q / 8 kv heads, D 128, bf16,
     context lengths uniform in [512, 4096], shuffled pool."""
     rng = np.random.default_rng(seed)
     lens = rng.integers(512, 4097, size=64)
-    return build_workload("llama3-8b-b64", lens, 32, 8, 128, "bf16", seed, rng=rng)
+    return build_workload("llama3-8b-b64", lens, 32, 8, 128, "bf16", seed, rng=rng, block_size=block_size)
 
 
-def llama70b_long(seed: int = 3) -> Workload:
+def llama70b_long(seed: int = 3, block_size: int = BLOCK_SIZE) -> Workload:
     """Llama-3-70B-shaped layer, long context: batch 8, 64 q / 8 kv heads, D 128,
     bf16, context lengths uniform in [32768, 131072]."""
     rng = np.random.default_rng(seed)
     lens = rng.integers(32768, 131073, size=8)
-    return build_workload("llama3-70b-long", lens, 64, 8, 128, "bf16", seed, rng=rng)
+    return build_workload("llama3-70b-long", lens, 64, 8, 128, "bf16", seed, rng=rng, block_size=block_size)
 
 
-def shared_prefix_256(seed: int = 4) -> Workload:
+def shared_prefix_256(seed: int = 4, block_size: int = BLOCK_SIZE) -> Workload:
     """256 sequences sharing one 4096-token prefix (256 refcounted blocks) plus
     private tails of 64..512 tokens; 32 q / 8 kv heads, D 128, bf16."""
     rng = np.random.default_rng(seed)
     lens = 4096 + rng.integers(64, 513, size=256)
     return build_workload("shared-prefix-256", lens, 32, 8, 128, "bf16", seed,
-                          shared_prefix=4096, rng=rng)
+                          shared_prefix=4096, rng=rng, block_size=block_size)
 
 
-def best_of_8(seed: int = 40) -> Workload:
+def best_of_8(seed: int = 40, block_size: int = BLOCK_SIZE) -> Workload:
     """Best-of-8 over a 2000-token prompt (125 shared blocks) with divergent
     1..200-token tails; 32 q / 8 kv heads, D 128, bf16."""
     rng = np.random.default_rng(seed)
     lens = 2000 + rng.integers(1, 201, size=8)
     return build_workload("best-of-8", lens, 32, 8, 128, "bf16", seed,
-                          shared_prefix=2000, rng=rng)
+                          shared_prefix=2000, rng=rng, block_size=block_size)
 
 
-def fp8_b256(seed: int = 5) -> Workload:
+def fp8_b256(seed: int = 5, block_size: int = BLOCK_SIZE) -> Workload:
     """fp8 (E4M3) cache with per-head scales: batch 256, context lengths
     log-uniform in [128, 8192], 32 q / 8 kv heads, D 128, bf16 queries, plus
     one appended bf16 token per sequence."""
     rng = np.random.default_rng(seed)
     lens = np.rint(np.exp(rng.uniform(math.log(128), math.log(8192), size=256))).astype(np.int64)
-    return build_workload("fp8-b256", lens, 32, 8, 128, "fp8", seed, with_append=True, rng=rng)
+    return build_workload("fp8-b256", lens, 32, 8, 128, "fp8", seed, with_append=True, rng=rng,
+                          block_size=block_size)
 
 
 @dataclass
