@@ -41,10 +41,11 @@ __global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(CopyArgs a, c
   const size_t n = min(kSliceBytes, a.block_bytes - lo) / 16;   // vectors in this slice
   const unsigned i0 = threadIdx.x, i1 = threadIdx.x + kCopyThreads;
   u32x4 v0 = {0, 0, 0, 0}, v1 = {0, 0, 0, 0};
-  if (i0 < n) v0 = from[i0];
-  if (i1 < n) v1 = from[i1];
-  if (i0 < n) to[i0] = v0;
-  if (i1 < n) to[i1] = v1;
+  // bytes pass through once: non-temporal loads and stores keep them out of the caches
+  if (i0 < n) v0 = __builtin_nontemporal_load(from + i0);
+  if (i1 < n) v1 = __builtin_nontemporal_load(from + i1);
+  if (i0 < n) __builtin_nontemporal_store(v0, to + i0);
+  if (i1 < n) __builtin_nontemporal_store(v1, to + i1);
 }
 
 }  // namespace
