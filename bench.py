@@ -71,7 +71,8 @@ def committed_traffic(workload: str):
 class Runner:
     """Pre-marshalled C-ABI calls for one workload on the current stream."""
 
-    def __init__(self, wl, layers: int, workers: int = 0, identity_tables: bool = False, q_len: int = 1):
+    def __init__(self, wl, layers: int, workers: int = 0, identity_tables: bool = False, q_len: int = 1,
+                 reread: bool = False):
         import torch
         from paged_kv_cache_23_amd import ops
 
@@ -116,7 +117,7 @@ class Runner:
         self.B = wl.batch
         self.max_ctx = int(lens.max())
         self.out = torch.empty_like(self.q)
-        self.desc = ops.cache_desc(k0, v0, wl.num_q_heads, self.k_scale, self.v_scale)
+        self.desc = ops.cache_desc(k0, v0, wl.num_q_heads, self.k_scale, self.v_scale, reread)
         lib = ops.library()
         self.lib = lib
         self.explicit_workers = bool(workers)
@@ -265,8 +266,15 @@ def run_bench(args) -> dict:
     wl = W.WORKLOADS[args.workload](block_size=args.block_size)
     log(f"workload {wl.name}: B={wl.batch} Hq={wl.num_q_heads} Hkv={wl.num_kv_heads} D={wl.head_dim} "
         f"kv={wl.kv_dtype} blocks={wl.num_blocks} KV={wl.kv_bytes() / 1e6:.1f} MB")
-    runner = Runner(wl, args.layers, args.workers, args.identity_tables, args.q_len)
-    log(f"workers={runner.workers} waves, workspace={runner.ws_bytes} B, layers={args.layers}")
+    # a scheduler knows from its reference counts whether the batch shares
+    # blocks; here: when the distinct token slots are fewer than 90% of those read
+    shares = unique_kv_bytes(wl, wl.k_new is not None) < 0.9 * wl.kv_bytes(after_append=wl.k_new is not None)
+    reread = shares if args.reread == "auto" else args.reread == "on"
+    runner = Runner(wl, args.layers, args.workers, args.identity_tables, args.q_len, reread)
+    streamed = not reread and args.block_size <= 32
+    loads = "streamed (non-temporal)" if streamed else (
+        "cached (PKV_KV_REREAD: blocks shared)" if reread else "cached (blocks above 32 tokens)")
+    log(f"workers={runner.workers} waves, workspace={runner.ws_bytes} B, layers={args.layers}, K/V loads {loads}")
     torch.cuda.synchronize()
 
     # one checked step on layer 0 (the output is compared with the oracle below)
@@ -337,6 +345,7 @@ def run_bench(args) -> dict:
             "context_tokens": int((wl.context_lens_after if runner.append else wl.context_lens).sum()),
             "kv_bytes_per_step": step_bytes,
             "worker_waves": runner.workers,
+            "kv_loads": loads,
         },
         "hbm_peak_frac": round(gbs / HBM_PEAK_GBS, 4),
         "unique_kv_bytes_per_step": unique,
@@ -479,6 +488,8 @@ def main() -> int:
     p.add_argument("--copy-probe", action="store_true")
     p.add_argument("--cow", action="store_true", help="time the copy-on-write block copy instead")
     p.add_argument("--block-size", type=int, default=16, help="tokens per cache block (16, 32, 64, 128, 256)")
+    p.add_argument("--reread", choices=["auto", "on", "off"], default="auto",
+                   help="PKV_KV_REREAD hint: auto = on when the tables share blocks")
     p.add_argument("--q-len", type=int, default=1,
                    help="query tokens per sequence (speculative verification); 1 is the decode")
     args = p.parse_args()

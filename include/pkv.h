@@ -84,7 +84,17 @@ typedef struct pkv_cache_desc {
   int32_t q_dtype;
   const float* k_scale;
   const float* v_scale;
+  uint32_t flags;         /* PKV_KV_* hints below; 0 by default */
 } pkv_cache_desc;
+
+/* flags: the decode reads blocks that several sequences of the batch share
+ * (prefix sharing, parallel sampling; "Why one character breaks the cache",
+ * section on a block serving many requests).  K/V are then loaded with
+ * ordinary cached loads, so a shared block read again later in the call is
+ * served from the caches.  Without it every K/V byte is assumed to be read
+ * once and is streamed with non-temporal loads, which are faster on MI355X
+ * for data read once.  A hint only: the result is the same bits either way. */
+#define PKV_KV_REREAD 1u
 
 /* Write the K and V of num_tokens new tokens into their slots.
  * (Habr article, section 1: one new token per sequence is appended each

@@ -28,6 +28,7 @@ int check_desc(const pkv_cache_desc* d) {
   if (d->num_blocks <= 0 || d->num_kv_heads <= 0 || d->num_q_heads <= 0 || d->head_dim <= 0)
     return PKV_EINVAL;
   if (block_shift(d->block_size) < 0) return PKV_EINVAL;
+  if (d->flags & ~PKV_KV_REREAD) return PKV_EINVAL;
   if (d->num_q_heads % d->num_kv_heads != 0) return PKV_EINVAL;
   if (d->num_q_heads / d->num_kv_heads > pkv::kMaxGroup) return PKV_EUNSUPPORTED;
   if (d->head_dim != 64 && d->head_dim != 128) return PKV_EUNSUPPORTED;
@@ -145,6 +146,7 @@ DecodeArgs make_args(const pkv_cache_desc* d, const void* q, const void* k_pool,
   a.cols = q_len * a.group;
   a.block_size = d->block_size;
   a.block_shift = block_shift(d->block_size);
+  a.kv_reread = (d->flags & PKV_KV_REREAD) ? 1 : 0;
   a.head_dim = d->head_dim;
   a.max_blocks = max_blocks;
   a.num_blocks = d->num_blocks;

@@ -53,12 +53,15 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// K and V are read once per call: non-temporal loads stream them without
-// keeping them in the caches (measured on MI355X: random 4 KiB tiles at
-// 6.7 TB/s instead of 6.0 with ordinary loads).
-template <typename V>
-__device__ __forceinline__ V stream_load(const void* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const V*>(p));
+// Operand loads.  With NT the load is non-temporal: bytes read once per call
+// stream past the caches (measured on MI355X: random 4 KiB tiles at 6.7 TB/s
+// instead of 6.0 with ordinary loads).  Ordinary loads keep lines cached for
+// bytes that are read again within the call (blocks shared by several
+// sequences; the other half of a V line at block sizes of 64 and more).
+template <bool NT, typename V>
+__device__ __forceinline__ V op_load(const void* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(reinterpret_cast<const V*>(p));
+  return *reinterpret_cast<const V*>(p);
 }
 
 // Combine a per-head value across the four 16-lane rows (lanes l, l^16,
@@ -118,21 +121,23 @@ struct TileBF16 {
   }
   // tile: the first of the 16 token rows of this lane's half-chunk (half
   // r / 8) inside its block's token-major K tile.
+  template <bool NT>
   __device__ static void load_k(K& k, const Elem* tile, int r, int j) {
     const Elem* rx = tile + row_token(r, 0) * D + 8 * j;
     const Elem* ry = tile + row_token(r, 1) * D + 8 * j;
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) {
-      k.x[s] = stream_load<u32x4>(rx + 32 * s);
-      k.y[s] = stream_load<u32x4>(ry + 32 * s);
+      k.x[s] = op_load<NT, u32x4>(rx + 32 * s);
+      k.y[s] = op_load<NT, u32x4>(ry + 32 * s);
     }
   }
   // tile: this lane's half-chunk inside the V^T tile [D][bs] (dim rows of
   // bs tokens); the lane reads dims 16 t + r, tokens 8 (j % 2) .. +7.
+  template <bool NT>
   __device__ static void load_v(V& v, const Elem* tile, int r, int j, int bs) {
     const Elem* base = tile + r * bs + 8 * (j & 1);
 #pragma unroll
-    for (int t = 0; t < kTiles; ++t) v.t[t] = stream_load<u32x4>(base + (size_t)t * 16 * bs);
+    for (int t = 0; t < kTiles; ++t) v.t[t] = op_load<NT, u32x4>(base + (size_t)t * 16 * bs);
   }
   __device__ static void scores(const K& k, const Q& q, f32x4& sx, f32x4& sy) {
     sx = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -196,19 +201,21 @@ struct TileFP8 {
       q.op[s] = __builtin_bit_cast(bf16x8, v);
     }
   }
+  template <bool NT>
   __device__ static void load_k(K& k, const Elem* tile, int r, int j) {
     const Elem* rx = tile + row_token(r, 0) * D + j * (D / 4);
     const Elem* ry = tile + row_token(r, 1) * D + j * (D / 4);
 #pragma unroll
     for (int s = 0; s < kLoads; ++s) {
-      k.x[s] = stream_load<u32x4>(rx + 16 * s);
-      k.y[s] = stream_load<u32x4>(ry + 16 * s);
+      k.x[s] = op_load<NT, u32x4>(rx + 16 * s);
+      k.y[s] = op_load<NT, u32x4>(ry + 16 * s);
     }
   }
+  template <bool NT>
   __device__ static void load_v(V& v, const Elem* tile, int r, int j, int bs) {
     const Elem* base = tile + r * bs + 8 * (j & 1);
 #pragma unroll
-    for (int t = 0; t < kTiles; ++t) v.t[t] = stream_load<u32x2>(base + (size_t)t * 16 * bs);
+    for (int t = 0; t < kTiles; ++t) v.t[t] = op_load<NT, u32x2>(base + (size_t)t * 16 * bs);
   }
   __device__ static void scores(const K& k, const Q& q, f32x4& sx, f32x4& sy) {
     sx = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -271,21 +278,23 @@ struct TileF32 {
     for (int a = 0; a < kQuads; ++a)
       q.op[a] = valid ? *reinterpret_cast<const f32x4*>(p + 16 * a) : f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  template <bool NT>
   __device__ static void load_k(K& k, const Elem* tile, int r, int j) {
     const float* rx = tile + row_token(r, 0) * D + 4 * j;
     const float* ry = tile + row_token(r, 1) * D + 4 * j;
 #pragma unroll
     for (int a = 0; a < kQuads; ++a) {
-      k.x[a] = stream_load<f32x4>(rx + 16 * a);
-      k.y[a] = stream_load<f32x4>(ry + 16 * a);
+      k.x[a] = op_load<NT, f32x4>(rx + 16 * a);
+      k.y[a] = op_load<NT, f32x4>(ry + 16 * a);
     }
   }
+  template <bool NT>
   __device__ static void load_v(V& v, const Elem* tile, int r, int j, int bs) {
     const float* base = tile + r * bs + 8 * (j & 1);
 #pragma unroll
     for (int t = 0; t < kTiles; ++t) {
-      v.t[t][0] = stream_load<f32x4>(base + (size_t)t * 16 * bs);
-      v.t[t][1] = stream_load<f32x4>(base + (size_t)t * 16 * bs + 4);
+      v.t[t][0] = op_load<NT, f32x4>(base + (size_t)t * 16 * bs);
+      v.t[t][1] = op_load<NT, f32x4>(base + (size_t)t * 16 * bs + 4);
     }
   }
   __device__ static void scores(const K& k, const Q& q, f32x4& sx, f32x4& sy) {
@@ -388,7 +397,7 @@ struct Pos {
 // and ordered.  The wave that holds a pair's first chunk records the pair's
 // first wave and number of parts for the merge kernel.
 // ---------------------------------------------------------------------------
-template <int KV, int D>
+template <int KV, int D, bool KNT, bool VNT>
 __device__ __forceinline__ void split_body(const DecodeArgs& a, const int32_t* __restrict__ tables,
                                             const int32_t* __restrict__ lens, const float* __restrict__ k_scale,
                                             const float* __restrict__ v_scale) {
@@ -543,8 +552,8 @@ __device__ __forceinline__ void split_body(const DecodeArgs& a, const int32_t* _
     const Elem* vp = static_cast<const Elem*>(a.v_pool) + (size_t)q.g * bsz * D;
     const bool hk = (r >> 3) != 0;            // K rows: half by score row
     const bool hv = (j >> 1) != 0;            // V rows: half by lane group
-    T::load_k(kb, kp + (size_t)(hk ? id1 : id0) * blk_stride + (size_t)(hk ? off1 : off0) * D, r, j);
-    T::load_v(vb, vp + (size_t)(hv ? id1 : id0) * blk_stride + (hv ? off1 : off0), r, j, bsz);
+    T::template load_k<KNT>(kb, kp + (size_t)(hk ? id1 : id0) * blk_stride + (size_t)(hk ? off1 : off0) * D, r, j);
+    T::template load_v<VNT>(vb, vp + (size_t)(hv ? id1 : id0) * blk_stride + (hv ? off1 : off0), r, j, bsz);
     if (q.c == 0) load_q(qn, q);   // first chunk of a pair: its query rides along
   };
 
@@ -680,18 +689,18 @@ __device__ __forceinline__ void split_body(const DecodeArgs& a, const int32_t* _
 // per SIMD (at most 256 VGPRs each) are resident together; the float32 path at
 // head_dim 128 needs more registers for its double buffer and runs one wave
 // per SIMD instead of spilling.
-template <int KV, int D>
+template <int KV, int D, bool KNT, bool VNT>
 __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void decode_split_kernel(DecodeArgs a, const int32_t* __restrict__ tables, const int32_t* __restrict__ lens,
                          const float* __restrict__ k_scale, const float* __restrict__ v_scale) {
-  split_body<KV, D>(a, tables, lens, k_scale, v_scale);
+  split_body<KV, D, KNT, VNT>(a, tables, lens, k_scale, v_scale);
 }
 
-template <int KV, int D>
-__global__ __launch_bounds__(64 * kDecodeWaves) void decode_split_kernel_wide(
-    DecodeArgs a, const int32_t* __restrict__ tables, const int32_t* __restrict__ lens,
-    const float* __restrict__ k_scale, const float* __restrict__ v_scale) {
-  split_body<KV, D>(a, tables, lens, k_scale, v_scale);
+template <int KV, int D, bool KNT, bool VNT>
+__global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void decode_split_kernel_wide(DecodeArgs a, const int32_t* __restrict__ tables, const int32_t* __restrict__ lens,
+                              const float* __restrict__ k_scale, const float* __restrict__ v_scale) {
+  split_body<KV, D, KNT, VNT>(a, tables, lens, k_scale, v_scale);
 }
 
 // ---------------------------------------------------------------------------
@@ -738,16 +747,27 @@ __global__ __launch_bounds__(128) void decode_merge_kernel(const int2* __restric
   }
 }
 
-template <int KV, int D>
-hipError_t launch_split_t(const DecodeArgs& a, hipStream_t stream) {
+template <int KV, int D, bool KNT, bool VNT>
+hipError_t launch_split_p(const DecodeArgs& a, hipStream_t stream) {
   const unsigned grid = (unsigned)(a.num_workers / kDecodeWaves);
   if constexpr (KV == kF32 && D == 128)
-    hipLaunchKernelGGL((decode_split_kernel_wide<KV, D>), dim3(grid), dim3(64 * kDecodeWaves), 0, stream, a,
-                       a.block_tables, a.context_lens, a.k_scale, a.v_scale);
+    hipLaunchKernelGGL((decode_split_kernel_wide<KV, D, KNT, VNT>), dim3(grid), dim3(64 * kDecodeWaves), 0, stream,
+                       a, a.block_tables, a.context_lens, a.k_scale, a.v_scale);
   else
-    hipLaunchKernelGGL((decode_split_kernel<KV, D>), dim3(grid), dim3(64 * kDecodeWaves), 0, stream, a,
+    hipLaunchKernelGGL((decode_split_kernel<KV, D, KNT, VNT>), dim3(grid), dim3(64 * kDecodeWaves), 0, stream, a,
                        a.block_tables, a.context_lens, a.k_scale, a.v_scale);
   return hipGetLastError();
+}
+
+// Load policy: K and V streamed when every byte is read once.  Cached loads
+// for both when blocks are shared (re-read within the call) and at block
+// sizes of 64 and more, where a 32-token chunk uses half of each V line and
+// the next chunk reads the other half (measured on MI355X: streaming only K,
+// or both, is slower there than caching both).
+template <int KV, int D>
+hipError_t launch_split_t(const DecodeArgs& a, hipStream_t stream) {
+  if (a.kv_reread || a.block_size > 32) return launch_split_p<KV, D, false, false>(a, stream);
+  return launch_split_p<KV, D, true, true>(a, stream);
 }
 
 template <typename OutT, int D>

@@ -37,6 +37,7 @@ struct DecodeArgs {
   int32_t max_context_len;
   int32_t block_size;    // tokens per block: 16, 32, 64, 128 or 256
   int32_t block_shift;   // log2(block_size)
+  int32_t kv_reread;     // blocks are read more than once per call: keep K/V cached
   int32_t q_len;         // query tokens per sequence (1 for decode)
   int32_t cols;          // q_len * group: MFMA columns per (sequence, kv head) pair, <= 16
   int32_t num_workers;   // decode worker waves; a multiple of kDecodeWaves

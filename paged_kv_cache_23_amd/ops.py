@@ -41,7 +41,11 @@ class CacheDesc(ctypes.Structure):
         ("q_dtype", ctypes.c_int32),
         ("k_scale", ctypes.c_void_p),
         ("v_scale", ctypes.c_void_p),
+        ("flags", ctypes.c_uint32),
     ]
+
+
+KV_REREAD = 1   # blocks shared within the batch: keep K/V cached (a hint; same result)
 
 
 def library() -> ctypes.CDLL:
@@ -113,7 +117,7 @@ def _kv_code(pool: torch.Tensor) -> int:
 
 def cache_desc(k_pool: torch.Tensor, v_pool: torch.Tensor, num_q_heads: int,
                k_scale: Optional[torch.Tensor] = None,
-               v_scale: Optional[torch.Tensor] = None) -> CacheDesc:
+               v_scale: Optional[torch.Tensor] = None, reread: bool = False) -> CacheDesc:
     """Descriptor for pools ``k_pool [NB, Hkv, B, D]`` / ``v_pool [NB, Hkv, D, B]``."""
     kv = _kv_code(k_pool)
     _require(k_pool, "k_pool", (k_pool.dtype,), 4)
@@ -132,7 +136,7 @@ def cache_desc(k_pool: torch.Tensor, v_pool: torch.Tensor, num_q_heads: int,
     elif k_scale is not None or v_scale is not None:
         raise ValueError("scales are only used with an fp8 cache")
     return CacheDesc(NB, bs, Hkv, int(num_q_heads), D, kv,
-                     F32 if kv == F32 else BF16, _ptr(k_scale), _ptr(v_scale))
+                     F32 if kv == F32 else BF16, _ptr(k_scale), _ptr(v_scale), KV_REREAD if reread else 0)
 
 
 def kv_append(k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: torch.Tensor,
@@ -165,8 +169,8 @@ def copy_blocks(k_pool: torch.Tensor, v_pool: torch.Tensor, src: torch.Tensor, d
                                      src.shape[0], _stream(stream)), "pkv_copy_blocks")
 
 
-def _decode_checks(q, k_pool, v_pool, block_tables, context_lens, k_scale, v_scale, out):
-    desc = cache_desc(k_pool, v_pool, q.shape[1] if q.dim() == 3 else 0, k_scale, v_scale)
+def _decode_checks(q, k_pool, v_pool, block_tables, context_lens, k_scale, v_scale, out, reread=False):
+    desc = cache_desc(k_pool, v_pool, q.shape[1] if q.dim() == 3 else 0, k_scale, v_scale, reread)
     q_dtype = torch.float32 if desc.q_dtype == F32 else torch.bfloat16
     _require(q, "q", (q_dtype,), 3)
     B = q.shape[0]
@@ -221,12 +225,13 @@ def paged_attention(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
                     out: Optional[torch.Tensor] = None, k_scale: Optional[torch.Tensor] = None,
                     v_scale: Optional[torch.Tensor] = None, max_context_len: Optional[int] = None,
                     workspace: Optional[torch.Tensor] = None, num_workers: int = 0,
-                    stream=None) -> torch.Tensor:
-    """Causal attention of the last ``L`` tokens of each sequence: q and out ``[B, L, Hq, D]``."""
+                    stream=None, reread: bool = False) -> torch.Tensor:
+    """Causal attention of the last ``L`` tokens of each sequence: q and out ``[B, L, Hq, D]``.
+    ``reread``: the tables share blocks (see ``paged_decode``)."""
     _require(q, "q", (torch.float32, torch.bfloat16), 4)
     B, L, Hq, D = q.shape
     desc, _ = _decode_checks(q.view(B, L * Hq, D), k_pool, v_pool, block_tables, context_lens, k_scale, v_scale,
-                             None)
+                             None, reread)
     desc.num_q_heads = Hq
     if out is None:
         out = torch.empty_like(q)
@@ -255,13 +260,17 @@ def paged_decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
                  out: Optional[torch.Tensor] = None, k_scale: Optional[torch.Tensor] = None,
                  v_scale: Optional[torch.Tensor] = None, max_context_len: Optional[int] = None,
                  workspace: Optional[torch.Tensor] = None, num_workers: int = 0,
-                 stream=None) -> torch.Tensor:
+                 stream=None, reread: bool = False) -> torch.Tensor:
     """Decode attention of one query per sequence over its paged K/V; returns ``out``.
+
+    ``reread``: the tables share blocks between sequences (prefix sharing,
+    parallel sampling), so K/V are loaded cached instead of streamed; a speed
+    hint only, the result is the same.
 
     ``workspace`` (optional) must hold ``decode_workspace_bytes`` bytes for the
     same shape and ``num_workers``; calls sharing it must run on one stream.
     """
-    desc, out = _decode_checks(q, k_pool, v_pool, block_tables, context_lens, k_scale, v_scale, out)
+    desc, out = _decode_checks(q, k_pool, v_pool, block_tables, context_lens, k_scale, v_scale, out, reread)
     mctx = _max_ctx(block_tables, max_context_len, k_pool.shape[2])
     lib = library()
     need = lib.pkv_decode_workspace_bytes(ctypes.byref(desc), q.shape[0], mctx, int(num_workers))

@@ -64,6 +64,7 @@ FAKE = 0x10000  # a non-null, 16-byte aligned address that is never dereferenced
     (dict(kv_dtype=ops.FP8_E4M3), EINVAL),   # fp8 without scales
     (dict(kv_dtype=7), EINVAL),
     (dict(k_scale=FAKE), EINVAL),            # scales on a bf16 cache
+    (dict(flags=2), EINVAL),                 # unknown flag bit
 ])
 def test_bad_descriptors_are_rejected(kw, code):
     lib = ops.library()

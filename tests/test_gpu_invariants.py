@@ -170,3 +170,18 @@ def test_reused_workspace_stays_valid():
         assert np.array_equal(_bits(out), first)
         assert_close(out, ref_big, "bf16")
         assert_close(dev_small.decode(workers=8, workspace=ws), ref_small, "bf16")
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+def test_load_policy_hint_changes_nothing(kv_dtype):
+    """PKV_KV_REREAD only switches K/V loads between streamed and cached: the
+    output is the same bits, for a shared-prefix batch and a private one."""
+    for shared in (0, 64):
+        wl = build_workload("hint", [70, 100, 130, 400], 8, 2, 128, kv_dtype, seed=91, shared_prefix=shared)
+        dev = Dev(wl)
+        a = ops.paged_decode(dev.q, dev.k_pool, dev.v_pool, dev.tables, dev.lens, wl.scale, k_scale=dev.k_scale,
+                             v_scale=dev.v_scale, max_context_len=400)
+        b = ops.paged_decode(dev.q, dev.k_pool, dev.v_pool, dev.tables, dev.lens, wl.scale, k_scale=dev.k_scale,
+                             v_scale=dev.v_scale, max_context_len=400, reread=True)
+        assert np.array_equal(_bits(a), _bits(b))
+        assert_close(a, oracle_full(wl), kv_dtype)
