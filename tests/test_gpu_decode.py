@@ -148,3 +148,19 @@ def test_fp8_append_then_decode():
     ref = oracle_full(wl, ref_k, ref_v, after_append=True)
     err = assert_close(out, ref, "fp8")
     print(f"fp8-b256 max|err| = {err:.3g}")
+
+
+@pytest.mark.parametrize("workers", [0, 4096])
+def test_large_ragged_batch(workers):
+    """2,000 sequences of 0..300 tokens (a tenth of them empty): the length
+    scans and start searches run over many 64-sequence groups, empty
+    sequences get zeros, and every output matches the oracle."""
+    rng = np.random.default_rng(81)
+    lens = rng.integers(1, 301, size=2000)
+    lens[rng.random(2000) < 0.1] = 0
+    wl = build_workload("ragged-2000", lens, 8, 2, 64, "bf16", seed=81)
+    print(f"ragged 2000 workers={workers}", flush=True)
+    out = Dev(wl).decode(workers=workers)
+    ref = oracle_full(wl)
+    assert_close(out, ref, "bf16")
+    assert np.all(out_f64(out)[lens == 0] == 0)
