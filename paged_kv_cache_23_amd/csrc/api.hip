@@ -107,10 +107,20 @@ size_t workspace_bytes(const pkv_cache_desc* d, int32_t num_seqs, int32_t q_len,
          align_up((size_t)num_seqs * d->num_kv_heads * 2 * sizeof(int32_t));
 }
 
-// q_len query tokens times the group's heads must fit the 16 MFMA columns.
+// Query columns (query token, head) per (sequence, kv head) pair.
+int64_t query_cols(const pkv_cache_desc* d, int32_t q_len) {
+  return (int64_t)q_len * (d->num_q_heads / d->num_kv_heads);
+}
+
+// Up to 16 columns share one MFMA column tile and run on the split decode
+// kernels; more run on the many-query (prefill) kernel.
+bool many_queries(const pkv_cache_desc* d, int32_t q_len) { return query_cols(d, q_len) > pkv::kMaxGroup; }
+
+constexpr int64_t kMaxCols = int64_t(1) << 24;
+
 int check_q_len(const pkv_cache_desc* d, int32_t q_len) {
   if (q_len < 1) return PKV_EINVAL;
-  if ((int64_t)q_len * (d->num_q_heads / d->num_kv_heads) > pkv::kMaxGroup) return PKV_EUNSUPPORTED;
+  if (query_cols(d, q_len) > kMaxCols) return PKV_EUNSUPPORTED;
   return PKV_OK;
 }
 
@@ -154,6 +164,7 @@ DecodeArgs make_args(const pkv_cache_desc* d, const void* q, const void* k_pool,
   a.num_workers = workers;
   a.kv_dtype = d->kv_dtype;
   a.scale = scale;
+  if (!workspace) return a;   // the prefill kernel takes none
   char* ws = static_cast<char*>(workspace);
   a.ws_acc = reinterpret_cast<float*>(ws);
   a.ws_ml = reinterpret_cast<float*>(ws + acc_bytes(d, num_seqs, q_len, workers));
@@ -229,6 +240,7 @@ size_t pkv_attention_workspace_bytes(const pkv_cache_desc* desc, int32_t num_seq
   if (check_q_len(desc, q_len) != PKV_OK) return 0;
   const int32_t w = resolve_workers(desc, num_seqs, max_context_len, num_workers);
   if (w <= 0) return 0;
+  if (many_queries(desc, q_len)) return kWsAlign;   // nominal: the prefill kernel needs none
   return workspace_bytes(desc, num_seqs, q_len, w);
 }
 
@@ -249,6 +261,12 @@ int pkv_paged_attention(const pkv_cache_desc* desc, const void* q, const void* k
   const int32_t w = resolve_workers(desc, num_seqs, max_context_len, num_workers);
   if (w <= 0) return w == 0 ? PKV_EINVAL : w;
   if (num_seqs == 0) return PKV_OK;
+  if (many_queries(desc, q_len)) {
+    DecodeArgs a = make_args(desc, q, k_pool, v_pool, block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                             q_len, max_context_len, scale, w, out, nullptr);
+    if (pkv::prefill_groups(a) > 0x7FFFFFFF) return PKV_EUNSUPPORTED;
+    return launch_status(pkv::launch_prefill(a, static_cast<hipStream_t>(stream)));
+  }
   if (!workspace || ws_bytes < workspace_bytes(desc, num_seqs, q_len, w)) return PKV_EWORKSPACE;
   if (!aligned16(workspace)) return PKV_EINVAL;
   DecodeArgs a = make_args(desc, q, k_pool, v_pool, block_tables, max_blocks_per_seq, context_lens, num_seqs,

@@ -39,7 +39,7 @@ struct DecodeArgs {
   int32_t block_shift;   // log2(block_size)
   int32_t kv_reread;     // blocks are read more than once per call: keep K/V cached
   int32_t q_len;         // query tokens per sequence (1 for decode)
-  int32_t cols;          // q_len * group: MFMA columns per (sequence, kv head) pair, <= 16
+  int32_t cols;          // q_len * group: query columns per (sequence, kv head) pair
   int32_t num_workers;   // decode worker waves; a multiple of kDecodeWaves
   int32_t kv_dtype;
   float scale;
@@ -72,8 +72,13 @@ struct CopyArgs {
   uint32_t slices_per_block;   // 8 KiB slices per block and pool
 };
 
-// Split kernel then merge kernel, on `stream`.
+// Split kernel then merge kernel, on `stream` (cols <= kMaxGroup).
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+// Many-query kernel (cols > kMaxGroup): one workgroup per tile of columns
+// of a (sequence, kv head) pair; uses no workspace.
+hipError_t launch_prefill(const DecodeArgs& a, hipStream_t stream);
+// Workgroups launch_prefill starts for these arguments.
+int64_t prefill_groups(const DecodeArgs& a);
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
 hipError_t launch_copy(const CopyArgs& a, hipStream_t stream);
 size_t copy_slice_bytes();

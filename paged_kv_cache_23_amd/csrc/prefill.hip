@@ -1,0 +1,379 @@
+// Paged attention for many query tokens per sequence (chunked prefill) on
+// gfx950.
+//
+// What is computed (Habr KV-Cache article, habr.com/ru/articles/1021832):
+//  - section 6 "Chunked Prefill": a chunk of a prompt's new tokens is
+//    processed as its own step and attends to everything cached before it;
+//    the chunk's keys and values are already in the paged cache (appended
+//    first), so query token i of a chunk of L tokens in a sequence of n
+//    cached tokens sits at position n - L + i and sees tokens 0 .. n - L + i;
+//  - section 3 "Recalling FlashAttention": exact softmax(q K^T * scale) V
+//    reached tile by tile with a running max and sum;
+//  - section 4 "Recalling PagedAttention": K and V live in blocks scattered
+//    over a pool, found through the block table;
+//  - section 2 "GQA": the group's query heads share one kv head.
+//
+// With many query columns (query token, head) per kv head this is a dense
+// contraction, bound by the matrix cores, not by HBM: each K/V chunk is
+// loaded once into LDS and used by every column of a workgroup.
+//
+// Work decomposition.  Columns c = i * G + h of a (sequence, kv head) pair
+// are cut into workgroup tiles of 4 * 16 * kT columns; one workgroup of four
+// waves owns one tile and walks every 32-token key chunk up to the tile's
+// last visible token, so no partial results leave the workgroup.  Wave w owns
+// kT MFMA column tiles of 16 columns; the four waves stage each chunk's K
+// (token-major) and V (dimension-major) from the pool into double-buffered
+// LDS together, one barrier per chunk.  Workgroups are issued largest first
+// (the last column tiles see the most keys), and workgroups of the same pair
+// are spaced by the pair count, so with a pair count divisible by 8 they land
+// on the same XCD and share its L2.
+//
+// Tile math: the transposed-score layout of the decode kernel (tile_math.h):
+// per chunk and column tile, 2 * D/32 score MFMAs and D/16 P.V MFMAs (bf16),
+// all operands read from LDS with 16-byte reads.
+
+#include "pkv_internal.h"
+#include "tile_math.h"
+
+namespace pkv {
+namespace {
+
+constexpr int kPrefillWaves = 4;
+
+// LDS row of chunk token t in the K tile.  The 16 lanes of a lane group read
+// the rows of tokens 8 (r / 4) + 4 x + (r % 4), r < 16: row stride an odd
+// multiple of 16 bytes plus this row permutation puts them in distinct banks.
+__device__ __forceinline__ int k_row(int t) { return t ^ ((t >> 1) & 12); }
+
+template <int KV, int D>
+struct PrefillCfg {
+  using Tile = typename TileOf<KV, D>::type;
+  using Elem = typename Tile::Elem;
+  using Out = typename TileOf<KV, D>::Out;
+  static constexpr int kEs = (int)sizeof(Elem);
+  static constexpr int kPerPiece = 16 / kEs;                     // elements per 16-byte piece
+  static constexpr int kT = KV == kF32 ? 2 : 4;                  // column tiles per wave
+  static constexpr int kWaveCols = 16 * kT;
+  static constexpr int kGroupCols = kPrefillWaves * kWaveCols;   // columns per workgroup
+  static constexpr int kSK = D + kPerPiece;                      // K tile row stride (elements)
+  static constexpr int kSV = kChunkTokens + kPerPiece;           // V tile row stride (elements)
+  static constexpr int kKRowPieces = D / kPerPiece;
+  static constexpr int kVRowPieces = kChunkTokens / kPerPiece;
+  static constexpr int kKPieces = kChunkTokens * kKRowPieces;
+  static constexpr int kVPieces = D * kVRowPieces;
+  static constexpr int kThreads = 64 * kPrefillWaves;
+  static constexpr int kKPerThread = (kKPieces + kThreads - 1) / kThreads;
+  static constexpr int kVPerThread = (kVPieces + kThreads - 1) / kThreads;
+  static constexpr int kKTileElems = kChunkTokens * kSK;
+  static constexpr int kVTileElems = D * kSV;
+};
+
+// Zero every byte of a 16-byte piece from byte `keep` on.
+__device__ __forceinline__ u32x4 keep_bytes(u32x4 v, int keep) {
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const int nb = keep - 4 * w;
+    const uint32_t m = nb >= 4 ? 0xFFFFFFFFu : nb <= 0 ? 0u : ((1u << (8 * nb)) - 1u);
+    v[w] &= m;
+  }
+  return v;
+}
+
+// K operand of one chunk from the LDS tile: rows x and y of lane (r, j) are
+// chunk tokens 8 (r / 4) + (r % 4) and that + 4 (the decode kernel's chunk
+// layout), columns as each dtype's score tile expects.
+template <int KV, int D>
+__device__ __forceinline__ void lds_k(typename PrefillCfg<KV, D>::Tile::K& k,
+                                      const typename PrefillCfg<KV, D>::Elem* ks, int r, int j) {
+  using C = PrefillCfg<KV, D>;
+  const int tx = 8 * (r >> 2) + (r & 3);
+  const typename C::Elem* rx = ks + k_row(tx) * C::kSK;
+  const typename C::Elem* ry = ks + k_row(tx + 4) * C::kSK;
+  if constexpr (KV == kBF16) {
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s) {
+      k.x[s] = *reinterpret_cast<const u32x4*>(rx + 32 * s + 8 * j);
+      k.y[s] = *reinterpret_cast<const u32x4*>(ry + 32 * s + 8 * j);
+    }
+  } else if constexpr (KV == kFP8) {
+#pragma unroll
+    for (int s = 0; s < D / 64; ++s) {
+      k.x[s] = *reinterpret_cast<const u32x4*>(rx + j * (D / 4) + 16 * s);
+      k.y[s] = *reinterpret_cast<const u32x4*>(ry + j * (D / 4) + 16 * s);
+    }
+  } else {
+#pragma unroll
+    for (int a = 0; a < D / 16; ++a) {
+      k.x[a] = *reinterpret_cast<const f32x4*>(rx + 4 * j + 16 * a);
+      k.y[a] = *reinterpret_cast<const f32x4*>(ry + 4 * j + 16 * a);
+    }
+  }
+}
+
+// V operand: lane (r, j) reads dimension 16 u + r, chunk tokens 8 j .. 8 j + 7.
+template <int KV, int D>
+__device__ __forceinline__ void lds_v(typename PrefillCfg<KV, D>::Tile::V& v,
+                                      const typename PrefillCfg<KV, D>::Elem* vs, int r, int j) {
+  using C = PrefillCfg<KV, D>;
+  const typename C::Elem* base = vs + r * C::kSV + 8 * j;
+#pragma unroll
+  for (int u = 0; u < D / 16; ++u) {
+    const typename C::Elem* p = base + 16 * u * C::kSV;
+    if constexpr (KV == kBF16) {
+      v.t[u] = *reinterpret_cast<const u32x4*>(p);
+    } else if constexpr (KV == kFP8) {
+      v.t[u] = *reinterpret_cast<const u32x2*>(p);
+    } else {
+      v.t[u][0] = *reinterpret_cast<const f32x4*>(p);
+      v.t[u][1] = *reinterpret_cast<const f32x4*>(p + 4);
+    }
+  }
+}
+
+template <int KV, int D>
+__global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void prefill_kernel(DecodeArgs a, const int32_t* __restrict__ tables, const int32_t* __restrict__ lens,
+                    const float* __restrict__ k_scale, const float* __restrict__ v_scale) {
+  using C = PrefillCfg<KV, D>;
+  using T = typename C::Tile;
+  using Elem = typename C::Elem;
+  using OutT = typename C::Out;
+  constexpr int kT = C::kT;
+  constexpr int kTiles = D / 16;
+  constexpr size_t kQBytes = (KV == kF32) ? 4 : 2;
+
+  __shared__ __attribute__((aligned(16))) Elem lds_kt[2][C::kKTileElems];
+  __shared__ __attribute__((aligned(16))) Elem lds_vt[2][C::kVTileElems];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int r = lane & 15;
+  const int j = lane >> 4;
+  const int Hkv = a.num_kv_heads;
+  const int Hq = a.num_q_heads;
+  const int G = a.group;
+  const int L = a.q_len;
+  const int NC = a.cols;
+  const int pairs = a.num_seqs * Hkv;
+  const int ncb = (NC + C::kGroupCols - 1) / C::kGroupCols;
+  const int bid = blockIdx.x;
+  const int cb = ncb - 1 - bid / pairs;   // last column tiles (most keys) first
+  const int pair = bid - (bid / pairs) * pairs;
+  const int b = pair / Hkv;
+  const int g = pair - b * Hkv;
+
+  int n = min(lens[b], a.max_context_len);
+  n = (int)min((int64_t)n, (int64_t)a.max_blocks * a.block_size);
+  n = max(n, 0);
+  const int base = n - L + 1;   // query token i sees tokens < base + i
+
+  // Columns of this lane: tile t holds column col0 + 16 t + r.
+  const int col0 = cb * C::kGroupCols + wave * C::kWaveCols;
+  int lim[kT];
+  int qi[kT], qh[kT];
+#pragma unroll
+  for (int t = 0; t < kT; ++t) {
+    const int cc = min(col0 + 16 * t + r, NC - 1);
+    qi[t] = cc / G;
+    qh[t] = cc - qi[t] * G;
+    lim[t] = base + qi[t];
+  }
+  // Keys this wave and this workgroup need: up to their last column's limit.
+  const int wave_last = min(col0 + C::kWaveCols, NC) - 1;
+  const int kend_w = col0 < NC ? max(0, base + wave_last / G) : 0;
+  const int lim_lo = base + min(col0, NC - 1) / G;   // smallest limit of the wave
+  const int group_last = min(cb * C::kGroupCols + C::kGroupCols, NC) - 1;
+  const int kend = max(0, base + group_last / G);
+  const int nck = (kend + kChunkTokens - 1) / kChunkTokens;
+
+  float sl = a.scale * kLog2e;
+  float mul = 1.f;
+  if constexpr (KV == kFP8) {
+    sl *= k_scale[g];
+    mul = v_scale[g];
+  }
+
+  typename T::Q qop[kT];
+#pragma unroll
+  for (int t = 0; t < kT; ++t) {
+    const uint8_t* row = static_cast<const uint8_t*>(a.q) +
+                         (((size_t)b * L + qi[t]) * Hq + (size_t)g * G + qh[t]) * D * kQBytes;
+    T::load_q(qop[t], row, col0 + 16 * t + r < NC, j);
+  }
+
+  // ---- chunk staging: pool -> registers -> LDS ----
+  const int bs = a.block_size;
+  const int bshift = a.block_shift;
+  const int32_t* table = tables + (size_t)b * a.max_blocks;
+  const int last_blk = ((n + bs - 1) >> bshift) - 1;
+  const Elem* kpool = static_cast<const Elem*>(a.k_pool);
+  const Elem* vpool = static_cast<const Elem*>(a.v_pool);
+  struct Stage {
+    u32x4 k[C::kKPerThread];
+    u32x4 v[C::kVPerThread];
+  } st;
+
+  auto stage_load = [&](int c) {
+    const int t0 = c * kChunkTokens;
+    // Blocks holding the chunk's two 16-token halves.
+    const int i0 = min(max(table[min(t0 >> bshift, last_blk)], 0), a.num_blocks - 1);
+    const int i1 = min(max(table[min((t0 + 16) >> bshift, last_blk)], 0), a.num_blocks - 1);
+    const int off0 = t0 & (bs - 1);
+    const int off1 = (t0 + 16) & (bs - 1);
+#pragma unroll
+    for (int i = 0; i < C::kKPerThread; ++i) {
+      const int p = tid + C::kThreads * i;
+      if (C::kKPieces % C::kThreads == 0 || p < C::kKPieces) {
+        const int t = p / C::kKRowPieces;
+        const int e = p - t * C::kKRowPieces;
+        const int h = t >> 4;
+        const size_t blk = (size_t)(h ? i1 : i0) * Hkv + g;
+        const Elem* src = kpool + (blk * bs + (h ? off1 : off0) + (t & 15)) * D + e * C::kPerPiece;
+        st.k[i] = *reinterpret_cast<const u32x4*>(src);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < C::kVPerThread; ++i) {
+      const int p = tid + C::kThreads * i;
+      if (C::kVPieces % C::kThreads == 0 || p < C::kVPieces) {
+        const int d = p / C::kVRowPieces;
+        const int tk = (p - d * C::kVRowPieces) * C::kPerPiece;
+        const int h = tk >> 4;
+        const size_t blk = (size_t)(h ? i1 : i0) * Hkv + g;
+        const Elem* src = vpool + blk * bs * D + (size_t)d * bs + (h ? off1 : off0) + (tk & 15);
+        u32x4 x = *reinterpret_cast<const u32x4*>(src);
+        // V rows at or past n may hold anything (NaN too): zero them, since
+        // their zero weights would not cancel a NaN.
+        const int valid = n - (t0 + tk);
+        if (valid < C::kPerPiece) x = keep_bytes(x, max(valid, 0) * C::kEs);
+        st.v[i] = x;
+      }
+    }
+  };
+  auto stage_store = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < C::kKPerThread; ++i) {
+      const int p = tid + C::kThreads * i;
+      if (C::kKPieces % C::kThreads == 0 || p < C::kKPieces) {
+        const int t = p / C::kKRowPieces;
+        const int e = p - t * C::kKRowPieces;
+        *reinterpret_cast<u32x4*>(&lds_kt[buf][k_row(t) * C::kSK + e * C::kPerPiece]) = st.k[i];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < C::kVPerThread; ++i) {
+      const int p = tid + C::kThreads * i;
+      if (C::kVPieces % C::kThreads == 0 || p < C::kVPieces) {
+        const int d = p / C::kVRowPieces;
+        const int tk = (p - d * C::kVRowPieces) * C::kPerPiece;
+        *reinterpret_cast<u32x4*>(&lds_vt[buf][d * C::kSV + tk]) = st.v[i];
+      }
+    }
+  };
+
+  f32x4 acc[kT][kTiles];
+  float m_run[kT], l_run[kT];
+#pragma unroll
+  for (int t = 0; t < kT; ++t) {
+#pragma unroll
+    for (int u = 0; u < kTiles; ++u) acc[t][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_run[t] = -INFINITY;
+    l_run[t] = 0.f;
+  }
+
+  auto compute = [&](int buf, int t0) {
+    typename T::K kf;
+    typename T::V vf;
+    lds_k<KV, D>(kf, lds_kt[buf], r, j);
+    lds_v<KV, D>(vf, lds_vt[buf], r, j);
+    const bool diag = t0 + kChunkTokens > lim_lo;   // some column's causal limit falls in this chunk
+#pragma unroll
+    for (int t = 0; t < kT; ++t) {
+      f32x4 sx, sy;
+      T::scores(kf, qop[t], sx, sy);
+      float s[8] = {sx[0] * sl, sx[1] * sl, sx[2] * sl, sx[3] * sl,
+                    sy[0] * sl, sy[1] * sl, sy[2] * sl, sy[3] * sl};
+      if (diag) {
+        const int nvalid = min(max(lim[t] - (t0 + 8 * j), 0), 8);
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+          if (k >= nvalid) s[k] = -INFINITY;
+      }
+      float mloc = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])),
+                         fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
+      mloc = row_max4(mloc);
+      const float m_new = fmaxf(m_run[t], mloc);
+      // A column that has seen no token keeps max -inf and is exponentiated
+      // against 0, so its weights and rescale factor are 0, never NaN.
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      if (__builtin_amdgcn_ballot_w64(m_new != m_run[t])) {
+        const float corr = exp2_fast(m_run[t] - m_use);
+#pragma unroll
+        for (int u = 0; u < kTiles; ++u) acc[t][u] *= corr;
+        l_run[t] *= corr;
+      }
+      m_run[t] = m_new;
+      float pk[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) pk[k] = exp2_fast(s[k] - m_use);
+      l_run[t] += T::pv(acc[t], vf, pk);
+    }
+  };
+
+  if (nck > 0) {
+    stage_load(0);
+    stage_store(0);
+  }
+  __syncthreads();
+  for (int c = 0; c < nck; ++c) {
+    if (c + 1 < nck) stage_load(c + 1);   // next chunk's loads fly while this one is computed
+    const int t0 = c * kChunkTokens;
+    if (t0 < kend_w) compute(c & 1, t0);
+    if (c + 1 < nck) stage_store((c + 1) & 1);
+    __syncthreads();
+  }
+
+  OutT* out = static_cast<OutT*>(a.out);
+#pragma unroll
+  for (int t = 0; t < kT; ++t) {
+    const float l_tot = row_sum4(l_run[t]);
+    if (col0 + 16 * t + r < NC) {
+      const float f = l_tot > 0.f ? mul / l_tot : 0.f;   // a query that sees no token gets zeros
+      OutT* dst = out + (((size_t)b * L + qi[t]) * Hq + (size_t)g * G + qh[t]) * D + 4 * j;
+#pragma unroll
+      for (int u = 0; u < kTiles; ++u) store4<OutT>(dst + 16 * u, acc[t][u] * f);
+    }
+  }
+}
+
+template <int KV, int D>
+hipError_t launch_prefill_t(const DecodeArgs& a, hipStream_t stream) {
+  using C = PrefillCfg<KV, D>;
+  const int64_t ncb = (a.cols + C::kGroupCols - 1) / C::kGroupCols;
+  const int64_t grid = ncb * a.num_seqs * a.num_kv_heads;
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL((prefill_kernel<KV, D>), dim3((unsigned)grid), dim3(C::kThreads), 0, stream, a,
+                     a.block_tables, a.context_lens, a.k_scale, a.v_scale);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int64_t prefill_groups(const DecodeArgs& a) {
+  const int cols = a.kv_dtype == kF32 ? PrefillCfg<kF32, 64>::kGroupCols : PrefillCfg<kBF16, 64>::kGroupCols;
+  return ((int64_t)a.cols + cols - 1) / cols * a.num_seqs * a.num_kv_heads;
+}
+
+hipError_t launch_prefill(const DecodeArgs& a, hipStream_t stream) {
+  if (a.head_dim == 64) {
+    if (a.kv_dtype == kF32) return launch_prefill_t<kF32, 64>(a, stream);
+    if (a.kv_dtype == kBF16) return launch_prefill_t<kBF16, 64>(a, stream);
+    return launch_prefill_t<kFP8, 64>(a, stream);
+  }
+  if (a.kv_dtype == kF32) return launch_prefill_t<kF32, 128>(a, stream);
+  if (a.kv_dtype == kBF16) return launch_prefill_t<kBF16, 128>(a, stream);
+  return launch_prefill_t<kFP8, 128>(a, stream);
+}
+
+}  // namespace pkv

@@ -227,7 +227,11 @@ def paged_attention(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
                     workspace: Optional[torch.Tensor] = None, num_workers: int = 0,
                     stream=None, reread: bool = False) -> torch.Tensor:
     """Causal attention of the last ``L`` tokens of each sequence: q and out ``[B, L, Hq, D]``.
-    ``reread``: the tables share blocks (see ``paged_decode``)."""
+
+    Up to 16 (query token, head) columns per kv head run on the split decode
+    kernels (speculative verification); more run on the prefill kernel
+    (chunked prefill), which needs no workspace.  ``reread``: the tables
+    share blocks (see ``paged_decode``)."""
     _require(q, "q", (torch.float32, torch.bfloat16), 4)
     B, L, Hq, D = q.shape
     desc, _ = _decode_checks(q.view(B, L * Hq, D), k_pool, v_pool, block_tables, context_lens, k_scale, v_scale,
@@ -242,7 +246,7 @@ def paged_attention(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
     lib = library()
     need = lib.pkv_attention_workspace_bytes(ctypes.byref(desc), B, L, mctx, int(num_workers))
     if need == 0 and B > 0:
-        _check(-2 if L * (Hq // desc.num_kv_heads) > 16 else -1, "pkv_attention_workspace_bytes")
+        _check(-2 if L * (Hq // desc.num_kv_heads) > 1 << 24 else -1, "pkv_attention_workspace_bytes")
     if workspace is None:
         workspace = new_workspace(need, q.device)
     wbytes = workspace.numel() * workspace.element_size()

@@ -231,6 +231,43 @@ def fp8_b256(seed: int = 5, block_size: int = BLOCK_SIZE) -> Workload:
 
 
 @dataclass
+class PrefillStep:
+    """One chunk of a chunked prefill: the cache after the chunk's tokens were
+    appended (``wl``, one sequence of n tokens) and the chunk's queries
+    ``q`` ``[1, L, Hq, D]``; query token i sits at position n - L + i."""
+    wl: Workload
+    q: torch.Tensor
+
+    def flops(self) -> int:
+        """Multiply-adds of QK^T and PV, counted as 2 flops each, over the
+        tokens every query token sees (causal): 4 * Hq * D per (query, key)."""
+        n, L = int(self.wl.context_lens[0]), int(self.q.shape[1])
+        seen = sum(max(0, n - L + 1 + i) for i in range(L))
+        return 4 * self.wl.num_q_heads * self.wl.head_dim * seen
+
+
+def prefill_chunks(seed: int = 6, prompt_tokens: int = 10000, chunk: int = 2048, num_q_heads: int = 64,
+                   num_kv_heads: int = 8, head_dim: int = 128, kv_dtype: str = "bf16",
+                   block_size: int = BLOCK_SIZE) -> List[PrefillStep]:
+    """Habr article section 6, "Chunked Prefill": a 10,000-token prompt under a
+    2048-token step budget is prefilled in chunks of 2048, 2048, 2048, 2048 and
+    1808 tokens, each attending to every chunk before it.  Layer shape of the
+    section's model (Llama-3-70B: 64 q / 8 kv heads, D 128), bf16.  One pool
+    holds the whole prompt in shuffled 16-token blocks; step k's cache is its
+    first n_k tokens (the chunks appended so far)."""
+    wl = build_workload("prefill-70b-10k", [prompt_tokens], num_q_heads, num_kv_heads, head_dim, kv_dtype, seed,
+                        block_size=block_size)
+    gen = torch.Generator().manual_seed(seed + 1000)
+    qd = _TORCH_DTYPE["f32" if kv_dtype == "f32" else "bf16"]
+    steps = []
+    for lo in range(0, prompt_tokens, chunk):
+        hi = min(prompt_tokens, lo + chunk)
+        part = Workload(**{**wl.__dict__, "context_lens": torch.tensor([hi], dtype=torch.int32)})
+        steps.append(PrefillStep(part, _randn((1, hi - lo, num_q_heads, head_dim), gen, qd)))
+    return steps
+
+
+@dataclass
 class CowStep:
     """One decode step of a parallel-sampling batch: block copies to make
     first, then one new token per sample written to its slot."""

@@ -125,6 +125,33 @@ def test_workspace_sizing_and_check():
                                    64, FAKE, None, 0, None) == 0
 
 
+def test_many_query_sizing():
+    """Up to 16 (query token, head) columns per kv head use the split kernels'
+    workspace; more run on the prefill kernel, which takes none (a nominal 256
+    bytes is reported so that 0 still means bad arguments); beyond 2^24
+    columns the call is unsupported."""
+    lib = ops.library()
+    d = _desc()                                 # group 4
+    up = lambda n: -(-n // 256) * 256
+    rows = (64 + 4 * 2) * 4 * 4                 # q_len 4: 16 columns
+    assert lib.pkv_attention_workspace_bytes(ctypes.byref(d), 4, 4, 150, 64) == \
+        up(rows * 128 * 4) + up(rows * 2 * 4) + up(4 * 2 * 4)
+    assert lib.pkv_attention_workspace_bytes(ctypes.byref(d), 4, 5, 150, 64) == 256
+    assert lib.pkv_attention_workspace_bytes(ctypes.byref(d), 4, 2048, 10000, 0) in (0, 256)  # 0 without a GPU
+    assert lib.pkv_attention_workspace_bytes(ctypes.byref(d), 4, 1 << 22, 150, 64) == 256
+    assert lib.pkv_attention_workspace_bytes(ctypes.byref(d), 4, (1 << 22) + 1, 150, 64) == 0
+    assert lib.pkv_attention_workspace_bytes(ctypes.byref(d), 4, 0, 150, 64) == 0
+    st = lib.pkv_paged_attention(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 16, FAKE, 4, (1 << 22) + 1, 150, 0.1,
+                                 64, FAKE, None, 0, None)
+    assert st == EUNSUPPORTED
+    st = lib.pkv_paged_attention(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 16, FAKE, 4, 0, 150, 0.1,
+                                 64, FAKE, None, 0, None)
+    assert st == EINVAL
+    # the prefill route needs no workspace: with zero sequences nothing is launched
+    assert lib.pkv_paged_attention(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 16, FAKE, 0, 64, 150, 0.1,
+                                   64, FAKE, None, 0, None) == 0
+
+
 def test_strerror_and_version():
     lib = ops.library()
     assert lib.pkv_strerror(0) == b"ok"

@@ -82,9 +82,3 @@ def test_fewer_tokens_than_queries():
         vis = args["context_lens"] - L + 1 + i
         ref = oracle.oracle_decode(**dict(args, q=qh[:, i], context_lens=np.maximum(vis, 0)))
         assert_close(torch.from_numpy(out[:, i]), ref, "bf16")
-
-
-def test_too_many_columns_is_unsupported():
-    wl, q = _case("bf16", 128, 4, 5, [40], seed=64)   # 5 * 4 = 20 columns
-    with pytest.raises(RuntimeError, match="unsupported"):
-        _run(wl, q)

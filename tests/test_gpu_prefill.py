@@ -1,0 +1,137 @@
+"""GPU parity of the many-query path of pkv_paged_attention (more than 16
+(query token, head) columns per kv head: chunked prefill) against the oracle,
+through the C ABI."""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from paged_kv_cache_23_amd import ops
+from paged_kv_cache_23_amd.workloads import build_workload, storage_numpy
+from tests.gpu_util import Dev, assert_close, out_f64
+from tests.oracle_inputs import oracle_args, relayout
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(kv_dtype, D, G, L, lens, seed, Hkv=2, block_size=16):
+    wl = build_workload("prefill", lens, G * Hkv, Hkv, D, kv_dtype, seed=seed, block_size=block_size)
+    gen = torch.Generator().manual_seed(seed + 100)
+    qd = torch.float32 if kv_dtype == "f32" else torch.bfloat16
+    q = torch.randn((wl.batch, L, G * Hkv, D), generator=gen).to(qd)
+    return wl, q
+
+
+def _run(wl, q, k_pool=None, v_pool=None, tables=None):
+    dev = Dev(wl)
+    return ops.paged_attention(q.to(dev.q.device), dev.k_pool if k_pool is None else k_pool.cuda(),
+                               dev.v_pool if v_pool is None else v_pool.cuda(),
+                               dev.tables if tables is None else tables.cuda(), dev.lens, wl.scale,
+                               k_scale=dev.k_scale, v_scale=dev.v_scale,
+                               max_context_len=int(wl.context_lens.max()))
+
+
+def _ref(wl, q):
+    return oracle.oracle_attention_multi(**dict(oracle_args(wl), q=storage_numpy(q)))
+
+
+# Column counts L * G: just past one MFMA tile (20), one wave's tiles (64),
+# one workgroup (256), several workgroups with a ragged last one (600, 800).
+@pytest.mark.parametrize("kv_dtype,D,G,L", [
+    ("bf16", 128, 4, 5), ("bf16", 128, 4, 64), ("bf16", 128, 8, 100), ("bf16", 64, 1, 300),
+    ("bf16", 128, 16, 2), ("fp8", 128, 4, 33), ("fp8", 64, 16, 9), ("fp8", 128, 8, 75),
+    ("f32", 64, 2, 40), ("f32", 128, 4, 17), ("f32", 128, 1, 150),
+])
+def test_prefill_parity(kv_dtype, D, G, L):
+    # lengths: n == L (a whole prompt), n a multiple of 32 and not, long tails
+    lens = [L, L + 1, L + 31, L + 32, L + 100, 2 * L + 7, L + 519]
+    wl, q = _case(kv_dtype, D, G, L, lens, seed=70 + L)
+    print(f"prefill {kv_dtype} D={D} G={G} L={L}", flush=True)
+    out = _run(wl, q)
+    assert out.shape == q.shape
+    ref = _ref(wl, q)
+    Hq = G * 2
+    assert_close(out.reshape(wl.batch, L * Hq, D), ref.reshape(wl.batch, L * Hq, D), kv_dtype)
+
+
+def test_boundary_between_the_two_kernels():
+    """16 columns run on the split kernels, 17 and more on the prefill kernel;
+    both agree with the oracle."""
+    for L, G in ((4, 4), (17, 1), (2, 8), (3, 8)):
+        wl, q = _case("bf16", 128, G, L, [L, 50, 333], seed=80 + L * G)
+        out = _run(wl, q)
+        ref = _ref(wl, q)
+        assert_close(out.reshape(wl.batch, -1, 128), ref.reshape(wl.batch, -1, 128), "bf16")
+
+
+def test_fewer_tokens_than_queries():
+    """n < L: queries that see no token get zeros, the others attend to the
+    tokens before their position; an empty sequence is all zeros."""
+    L = 40
+    wl, q = _case("bf16", 128, 4, L, [0, 3, 39, 40, 41], seed=90)
+    out = out_f64(_run(wl, q))
+    args = oracle_args(wl)
+    qh = storage_numpy(q)
+    for i in range(L):
+        vis = args["context_lens"] - L + 1 + i
+        ref = oracle.oracle_decode(**dict(args, q=qh[:, i], context_lens=np.maximum(vis, 0)))
+        assert_close(torch.from_numpy(out[:, i]), ref, "bf16")
+    assert not out[0].any()
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+def test_layout_invariance_is_bit_exact(kv_dtype):
+    """The arithmetic order depends on logical positions only: another block
+    size (with NaN in every slot past a sequence's end) or another placement
+    of the blocks gives the same bits."""
+    L = 70
+    wl, q = _case(kv_dtype, 128, 4, L, [L, 100, 257, 640], seed=91)
+    base = _run(wl, q).cpu()
+    for bs, seed in ((16, 5), (32, 6), (64, 7), (256, 8)):
+        kp, vp, tab = relayout(wl, bs, seed)
+        got = _run(wl, q, kp, vp, tab).cpu()
+        assert torch.equal(got, base), f"block size {bs}"
+
+
+def test_each_query_equals_a_decode_over_its_prefix():
+    """Query token i of the chunk attends exactly like a decode over the first
+    n - L + 1 + i tokens (the multi-token reading of the pages), checked
+    against the split decode kernel within tolerance."""
+    L = 48
+    wl, q = _case("bf16", 128, 4, L, [L, 300, 1000], seed=92)
+    out = _run(wl, q)
+    dev = Dev(wl)
+    for i in (0, 1, 17, 31, 32, 47):
+        lens = (wl.context_lens - L + 1 + i).clamp(min=0).to(torch.int32)
+        dec = ops.paged_decode(q[:, i].contiguous().cuda(), dev.k_pool, dev.v_pool, dev.tables, lens.cuda(),
+                               wl.scale, max_context_len=int(lens.max()))
+        np.testing.assert_allclose(out_f64(out[:, i]), out_f64(dec), atol=1.5e-2, rtol=0)
+
+
+def test_ten_thousand_token_prompt_in_chunks_sampled():
+    """Habr section 6's worked example at full size: a 10,000-token prompt
+    prefilled in chunks of 2048, 2048, 2048, 2048 and 1808 tokens, on one
+    Llama-3-70B layer (64 query heads, 8 kv heads, head_dim 128, bf16).
+    Every chunk runs over the blocks of the chunks before it; sampled query
+    rows are checked against the oracle, the whole output for finiteness."""
+    from paged_kv_cache_23_amd.workloads import prefill_chunks
+
+    steps = prefill_chunks(seed=6)
+    assert [s.q.shape[1] for s in steps] == [2048, 2048, 2048, 2048, 1808]
+    rng = np.random.default_rng(7)
+    for s in steps:
+        wl, q = s.wl, s.q
+        L = q.shape[1]
+        print(f"chunk n={int(wl.context_lens[0])} L={L}", flush=True)
+        out = _run(wl, q)
+        got = out_f64(out)
+        assert np.all(np.isfinite(got))
+        args = oracle_args(wl)
+        qh = storage_numpy(q)
+        for i in sorted(set(rng.integers(0, L, size=6).tolist()) | {0, L - 1}):
+            lens = np.array([int(wl.context_lens[0]) - L + 1 + i], dtype=np.int32)
+            ref = oracle.oracle_decode(**dict(args, q=qh[:, i], context_lens=lens))
+            assert_close(torch.from_numpy(got[:, i]), ref, "bf16")
