@@ -18,6 +18,9 @@ Extra modes:
   --copy-probe    run a plain device-to-device copy of known size (calibrates
                   the FETCH_SIZE / WRITE_SIZE counters)
   --cow           time the copy-on-write block copy and a parallel-sampling step
+  --prefill       time chunked prefill: a 10,000-token prompt in chunks of at
+                  most 2048 tokens on one Llama-3-70B-shaped layer (TFLOP/s
+                  against the bf16 MFMA peak)
 """
 
 from __future__ import annotations
@@ -472,6 +475,199 @@ def cow_bench(args) -> dict:
     }
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+class PrefillRunner:
+    """The chunk steps of one prompt's chunked prefill, pre-marshalled."""
+
+    def __init__(self, block_size: int = 16):
+        import torch
+        from paged_kv_cache_23_amd import ops
+        from paged_kv_cache_23_amd.workloads import prefill_chunks
+
+        self.torch, self.ops = torch, ops
+        dev = torch.device("cuda:0")
+        self.steps = prefill_chunks(block_size=block_size)
+        wl = self.steps[0].wl
+        self.wl = wl
+        self.k_pool, self.v_pool = wl.k_pool.to(dev), wl.v_pool.to(dev)
+        self.tables = wl.block_tables.to(dev)
+        self.q = [s.q.to(dev) for s in self.steps]
+        self.out = [torch.empty_like(q) for q in self.q]
+        self.lens = [s.wl.context_lens.to(dev) for s in self.steps]
+        self.n = [int(s.wl.context_lens[0]) for s in self.steps]
+        self.flops = [s.flops() for s in self.steps]
+        self.desc = ops.cache_desc(self.k_pool, self.v_pool, wl.num_q_heads)
+        self.lib = ops.library()
+        self.ws = ops.new_workspace(256, dev)
+
+    def chunk(self, k: int, stream):
+        q = self.q[k]
+        st = self.lib.pkv_paged_attention(
+            ctypes.byref(self.desc), q.data_ptr(), self.k_pool.data_ptr(), self.v_pool.data_ptr(),
+            self.tables.data_ptr(), self.tables.shape[1], self.lens[k].data_ptr(), 1, q.shape[1], self.n[k],
+            self.wl.scale, 0, self.out[k].data_ptr(), self.ws.data_ptr(), 256, stream)
+        if st:
+            raise RuntimeError(f"pkv_paged_attention failed: {st}")
+
+    def step(self, stream):
+        for k in range(len(self.steps)):
+            self.chunk(k, stream)
+
+
+def prefill_parity(runner, rows: int = 4) -> float:
+    """Max |error| of a few sampled query rows of every chunk against the oracle."""
+    import numpy as np
+
+    import oracle
+    from paged_kv_cache_23_amd.workloads import storage_numpy
+
+    runner.torch.cuda.synchronize()
+    wl = runner.wl
+    kp, vp = storage_numpy(wl.k_pool), storage_numpy(wl.v_pool)
+    worst = 0.0
+    for k, s in enumerate(runner.steps):
+        L = s.q.shape[1]
+        got = runner.out[k].float().cpu().numpy().astype(np.float64)
+        for i in np.linspace(0, L - 1, rows).astype(int):
+            lens = np.array([runner.n[k] - L + 1 + int(i)], dtype=np.int32)
+            ref = oracle.oracle_decode(storage_numpy(s.q[:, i]), wl.q_dtype, kp, vp, wl.kv_dtype,
+                                       wl.block_tables.numpy(), lens, wl.scale)
+            worst = max(worst, float(np.max(np.abs(got[:, i] - ref))))
+    return worst
+
+
+def prefill_cpu_baseline(runner, min_seconds: float):
+    """The oracle on this host over a bounded sample: the first query rows of
+    the last chunk (each sees about 8,200 tokens), rows added until
+    min_seconds; reported as TFLOP/s of the same causal flop count."""
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    from paged_kv_cache_23_amd.workloads import storage_numpy
+
+    wl, s = runner.wl, runner.steps[-1]
+    kp, vp = storage_numpy(wl.k_pool), storage_numpy(wl.v_pool)
+    q = storage_numpy(s.q)
+    L, n = s.q.shape[1], runner.n[-1]
+    done, flops, t0 = 0, 0, time.perf_counter()
+    with threadpool_limits(1):
+        while done < L and time.perf_counter() - t0 < min_seconds:
+            rows = min(8, L - done)
+            lens = [n - L + done + rows]
+            oracle.oracle_attention_multi(q[:, done:done + rows], wl.q_dtype, kp, vp, wl.kv_dtype,
+                                          wl.block_tables.numpy(), lens, wl.scale)
+            flops += sum(4 * wl.num_q_heads * wl.head_dim * (n - L + 1 + i) for i in range(done, done + rows))
+            done += rows
+    sec = time.perf_counter() - t0
+    return {
+        "value": round(flops / sec / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"first {done} query rows of the last chunk (n = {n}, {wl.num_q_heads} q heads) through "
+                  f"oracle_attention_multi in fp64 NumPy on one host thread, {sec:.1f} s",
+    }
+
+
+def prefill_bench(args) -> dict:
+    """Chunked prefill: the 10,000-token prompt of the pages' worked example,
+    five chunk calls per step, each over every chunk before it."""
+    import numpy as np
+    import torch
+
+    runner = PrefillRunner(args.block_size)
+    wl = runner.wl
+    flops = sum(runner.flops)
+    log(f"prefill {wl.name}: chunks {[int(q.shape[1]) for q in runner.q]} over n = {runner.n}, "
+        f"Hq={wl.num_q_heads} Hkv={wl.num_kv_heads} D={wl.head_dim}, {flops / 1e9:.1f} GFLOP per step")
+    s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    runner.step(s)
+    err = prefill_parity(runner)
+    log(f"parity on sampled rows: max|err| = {err:.3g}")
+    for _ in range(args.warmup):
+        runner.step(s)
+    torch.cuda.synchronize()
+    K = args.steps
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(K):
+        runner.step(s)
+    b.record()
+    torch.cuda.synchronize()
+    ms_per_step = a.elapsed_time(b) / K
+    # per-call durations, HIP events around each chunk call on its stream
+    nck = len(runner.steps)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K * nck)]
+    for i in range(K):
+        for k in range(nck):
+            ev[i * nck + k][0].record()
+            runner.chunk(k, s)
+            ev[i * nck + k][1].record()
+    torch.cuda.synchronize()
+    call_ms = np.array([e[0].elapsed_time(e[1]) for e in ev]).reshape(K, nck)
+    mean_call = call_ms.mean(axis=0)
+    per_chunk = [round(f / (m * 1e-3) / 1e12, 1) for f, m in zip(runner.flops, mean_call)]
+    kern_tflops = flops / (mean_call.sum() * 1e-3) / 1e12
+    tflops = flops / (ms_per_step * 1e-3) / 1e12
+    log(f"{K} steps: {ms_per_step * 1e3:.1f} us/step, {tflops:.1f} TFLOP/s; per chunk call (us) "
+        f"{[round(m * 1e3, 1) for m in mean_call]}, TFLOP/s {per_chunk}")
+    result = {
+        "metric": "chunked-prefill paged attention TFLOP/s (bf16 MFMA)",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{wl.name}: one layer (64 q / 8 kv heads, head_dim 128, bf16, {args.block_size}-token "
+                        f"blocks, shuffled pool) prefilling a 10,000-token prompt in chunks of "
+                        f"{[int(q.shape[1]) for q in runner.q]}, each attending causally to all chunks before it",
+            "flops_per_step": flops,
+            "prefill_tokens_per_step": int(sum(q.shape[1] for q in runner.q)),
+        },
+        "prefill_tokens_per_s": round(sum(q.shape[1] for q in runner.q) / (ms_per_step * 1e-3), 1),
+        "max_abs_err_sampled": err,
+        "per_chunk_call_us": [round(m * 1e3, 2) for m in mean_call],
+        "per_chunk_tflops": per_chunk,
+        "roofline": {
+            "kernel": "prefill_kernel<bf16, 128>",
+            "bound": "mfma",
+            "achieved": round(kern_tflops, 2),
+            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(kern_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic": None,
+            "algorithmic_flops_per_step": flops,
+            "mean_step_kernel_us": round(float(mean_call.sum()) * 1e3, 2),
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on the host ...")
+        result["cpu_baseline"] = prefill_cpu_baseline(runner, args.cpu_seconds)
+    else:
+        result["cpu_baseline"] = None
+    return result
+
+
+def prefill_profile(args) -> None:
+    import torch
+
+    runner = PrefillRunner(args.block_size)
+    s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    for _ in range(args.warmup + args.steps):
+        runner.step(s)
+    torch.cuda.synchronize()
+    log(f"profiled {args.warmup + args.steps} prefill steps")
+
+
 def main() -> int:
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
@@ -490,6 +686,8 @@ def main() -> int:
     p.add_argument("--block-size", type=int, default=16, help="tokens per cache block (16, 32, 64, 128, 256)")
     p.add_argument("--reread", choices=["auto", "on", "off"], default="auto",
                    help="PKV_KV_REREAD hint: auto = on when the tables share blocks")
+    p.add_argument("--prefill", action="store_true",
+                   help="time chunked prefill (a 10,000-token prompt in 2048-token chunks) instead")
     p.add_argument("--q-len", type=int, default=1,
                    help="query tokens per sequence (speculative verification); 1 is the decode")
     args = p.parse_args()
@@ -500,8 +698,14 @@ def main() -> int:
     if args.copy_probe:
         copy_probe(args)
         return 0
+    if args.prefill and args.profile_one:
+        prefill_profile(args)
+        return 0
     if args.profile_one:
         profile_one(args)
+        return 0
+    if args.prefill:
+        print(json.dumps(prefill_bench(args)), flush=True)
         return 0
     if args.cow:
         print(json.dumps(cow_bench(args)), flush=True)

@@ -38,7 +38,10 @@
 namespace pkv {
 namespace {
 
-constexpr int kPrefillWaves = 4;
+// Rescale threshold (log2 units): the running max used in the exponentials
+// is only raised when a column's max exceeds it by more than this, so
+// weights stay below 2^8 and most chunks skip the accumulator rescale.
+constexpr float kRescaleSlack = 8.f;
 
 // LDS row of chunk token t in the K tile.  The 16 lanes of a lane group read
 // the rows of tokens 8 (r / 4) + 4 x + (r % 4), r < 16: row stride an odd
@@ -52,16 +55,20 @@ struct PrefillCfg {
   using Out = typename TileOf<KV, D>::Out;
   static constexpr int kEs = (int)sizeof(Elem);
   static constexpr int kPerPiece = 16 / kEs;                     // elements per 16-byte piece
-  static constexpr int kT = KV == kF32 ? 2 : 4;                  // column tiles per wave
+  // Eight waves of two column tiles (two waves per SIMD, at most 256
+  // registers each) for bf16 / fp8; the float32 tiles need more registers
+  // and run four waves, one per SIMD.
+  static constexpr int kT = 2;                                   // column tiles per wave
+  static constexpr int kWaves = KV == kF32 ? 4 : 8;              // waves per workgroup
   static constexpr int kWaveCols = 16 * kT;
-  static constexpr int kGroupCols = kPrefillWaves * kWaveCols;   // columns per workgroup
+  static constexpr int kGroupCols = kWaves * kWaveCols;          // columns per workgroup
   static constexpr int kSK = D + kPerPiece;                      // K tile row stride (elements)
   static constexpr int kSV = kChunkTokens + kPerPiece;           // V tile row stride (elements)
   static constexpr int kKRowPieces = D / kPerPiece;
   static constexpr int kVRowPieces = kChunkTokens / kPerPiece;
   static constexpr int kKPieces = kChunkTokens * kKRowPieces;
   static constexpr int kVPieces = D * kVRowPieces;
-  static constexpr int kThreads = 64 * kPrefillWaves;
+  static constexpr int kThreads = 64 * kWaves;
   static constexpr int kKPerThread = (kKPieces + kThreads - 1) / kThreads;
   static constexpr int kVPerThread = (kVPieces + kThreads - 1) / kThreads;
   static constexpr int kKTileElems = kChunkTokens * kSK;
@@ -130,10 +137,31 @@ __device__ __forceinline__ void lds_v(typename PrefillCfg<KV, D>::Tile::V& v,
   }
 }
 
+// Row sums of the weights by the matrix cores: an all-ones A operand times
+// P^T gives, in every row of its output, each column's sum over the chunk's
+// 32 tokens (of the bf16-rounded weights the P.V product uses).
+__device__ __forceinline__ void pv_ones(f32x4& lsum, const bf16x8& pb) {
+  const bf16x8 ones = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f,
+                       (__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f};
+  lsum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb, lsum, 0, 0, 0);
+}
+
+// acc^T += V^T P^T with the weights already rounded to bf16.
 template <int KV, int D>
-__global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void prefill_kernel(DecodeArgs a, const int32_t* __restrict__ tables, const int32_t* __restrict__ lens,
-                    const float* __restrict__ k_scale, const float* __restrict__ v_scale) {
+__device__ __forceinline__ void pv_bf16(f32x4* acc, const typename PrefillCfg<KV, D>::Tile::V& v, const bf16x8& pb) {
+#pragma unroll
+  for (int u = 0; u < D / 16; ++u) {
+    u32x4 op;
+    if constexpr (KV == kFP8) op = fp8x8_to_bf16x8(v.t[u][0], v.t[u][1]);
+    else op = v.t[u];
+    acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, op), pb, acc[u], 0, 0, 0);
+  }
+}
+
+template <int KV, int D>
+__device__ __forceinline__ void prefill_body(const DecodeArgs& a, const int32_t* __restrict__ tables,
+                                             const int32_t* __restrict__ lens, const float* __restrict__ k_scale,
+                                             const float* __restrict__ v_scale) {
   using C = PrefillCfg<KV, D>;
   using T = typename C::Tile;
   using Elem = typename C::Elem;
@@ -272,13 +300,20 @@ void prefill_kernel(DecodeArgs a, const int32_t* __restrict__ tables, const int3
     }
   };
 
+  // Per column tile: accumulator, the reference max m_ref of its
+  // exponentials (log2 units; always within kRescaleSlack of the running max
+  // from below) and the running sum: a register for float32, an MFMA
+  // accumulator (four equal copies) for bf16 weights.
+  constexpr bool kMfmaSum = KV != kF32;
   f32x4 acc[kT][kTiles];
-  float m_run[kT], l_run[kT];
+  f32x4 lsum[kT];
+  float m_ref[kT], l_run[kT];
 #pragma unroll
   for (int t = 0; t < kT; ++t) {
 #pragma unroll
     for (int u = 0; u < kTiles; ++u) acc[t][u] = f32x4{0.f, 0.f, 0.f, 0.f};
-    m_run[t] = -INFINITY;
+    lsum[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_ref[t] = -INFINITY;
     l_run[t] = 0.f;
   }
 
@@ -303,21 +338,35 @@ void prefill_kernel(DecodeArgs a, const int32_t* __restrict__ tables, const int3
       float mloc = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])),
                          fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
       mloc = row_max4(mloc);
-      const float m_new = fmaxf(m_run[t], mloc);
-      // A column that has seen no token keeps max -inf and is exponentiated
-      // against 0, so its weights and rescale factor are 0, never NaN.
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      if (__builtin_amdgcn_ballot_w64(m_new != m_run[t])) {
-        const float corr = exp2_fast(m_run[t] - m_use);
+      // Raise the reference only when this chunk's max passes it by more
+      // than the slack (the first chunk with a visible token always does).
+      const bool raise = mloc > m_ref[t] + kRescaleSlack;
+      if (__builtin_amdgcn_ballot_w64(raise)) {
+        // Lanes that keep their reference use factor 1 (never exp2(-inf - -inf)
+        // for a column that has seen nothing); a first raise gives exp2(-inf) = 0.
+        const float m_new = raise ? mloc : m_ref[t];
+        const float corr = raise ? exp2_fast(m_ref[t] - m_new) : 1.f;
 #pragma unroll
         for (int u = 0; u < kTiles; ++u) acc[t][u] *= corr;
-        l_run[t] *= corr;
+        if constexpr (kMfmaSum) lsum[t] *= corr;
+        else l_run[t] *= corr;
+        m_ref[t] = m_new;
       }
-      m_run[t] = m_new;
+      // A column that has seen no token keeps -inf and is exponentiated
+      // against 0, so its weights are 0, never NaN.
+      const float m_use = m_ref[t] == -INFINITY ? 0.f : m_ref[t];
       float pk[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) pk[k] = exp2_fast(s[k] - m_use);
-      l_run[t] += T::pv(acc[t], vf, pk);
+      if constexpr (kMfmaSum) {
+        bf16x8 pb;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) pb[k] = (__bf16)pk[k];
+        pv_bf16<KV, D>(acc[t], vf, pb);
+        pv_ones(lsum[t], pb);
+      } else {
+        l_run[t] += T::pv(acc[t], vf, pk);
+      }
     }
   };
 
@@ -337,7 +386,9 @@ void prefill_kernel(DecodeArgs a, const int32_t* __restrict__ tables, const int3
   OutT* out = static_cast<OutT*>(a.out);
 #pragma unroll
   for (int t = 0; t < kT; ++t) {
-    const float l_tot = row_sum4(l_run[t]);
+    float l_tot;
+    if constexpr (kMfmaSum) l_tot = lsum[t][0];
+    else l_tot = row_sum4(l_run[t]);
     if (col0 + 16 * t + r < NC) {
       const float f = l_tot > 0.f ? mul / l_tot : 0.f;   // a query that sees no token gets zeros
       OutT* dst = out + (((size_t)b * L + qi[t]) * Hq + (size_t)g * G + qh[t]) * D + 4 * j;
@@ -347,14 +398,34 @@ void prefill_kernel(DecodeArgs a, const int32_t* __restrict__ tables, const int3
   }
 }
 
+// Tables, lengths and scales as restrict parameters: nothing the kernel
+// writes aliases them, so their wave-uniform reads use the scalar cache.
+template <int KV, int D>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void prefill_kernel(DecodeArgs a, const int32_t* __restrict__ tables, const int32_t* __restrict__ lens,
+                    const float* __restrict__ k_scale, const float* __restrict__ v_scale) {
+  prefill_body<KV, D>(a, tables, lens, k_scale, v_scale);
+}
+
+template <int KV, int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void prefill_kernel_wide(DecodeArgs a, const int32_t* __restrict__ tables, const int32_t* __restrict__ lens,
+                         const float* __restrict__ k_scale, const float* __restrict__ v_scale) {
+  prefill_body<KV, D>(a, tables, lens, k_scale, v_scale);
+}
+
 template <int KV, int D>
 hipError_t launch_prefill_t(const DecodeArgs& a, hipStream_t stream) {
   using C = PrefillCfg<KV, D>;
   const int64_t ncb = (a.cols + C::kGroupCols - 1) / C::kGroupCols;
   const int64_t grid = ncb * a.num_seqs * a.num_kv_heads;
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL((prefill_kernel<KV, D>), dim3((unsigned)grid), dim3(C::kThreads), 0, stream, a,
-                     a.block_tables, a.context_lens, a.k_scale, a.v_scale);
+  if constexpr (KV == kF32)
+    hipLaunchKernelGGL((prefill_kernel_wide<KV, D>), dim3((unsigned)grid), dim3(C::kThreads), 0, stream, a,
+                       a.block_tables, a.context_lens, a.k_scale, a.v_scale);
+  else
+    hipLaunchKernelGGL((prefill_kernel<KV, D>), dim3((unsigned)grid), dim3(C::kThreads), 0, stream, a,
+                       a.block_tables, a.context_lens, a.k_scale, a.v_scale);
   return hipGetLastError();
 }
 
