@@ -41,7 +41,8 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0
 METRIC = "paged decode KV GB/s read (% of HBM peak) + decode tokens/s, 8B-shape b64"
 PROFILE_DIR = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = ["paged_kv_cache_23_amd/csrc/decode.hip", "paged_kv_cache_23_amd/csrc/pkv_internal.h"]
+KERNEL_SOURCES = ["paged_kv_cache_23_amd/csrc/decode.hip", "paged_kv_cache_23_amd/csrc/tile_math.h",
+                  "paged_kv_cache_23_amd/csrc/pkv_internal.h"]
 
 
 def log(msg: str) -> None:
@@ -608,11 +609,11 @@ def prefill_bench(args) -> dict:
     torch.cuda.synchronize()
     call_ms = np.array([e[0].elapsed_time(e[1]) for e in ev]).reshape(K, nck)
     mean_call = call_ms.mean(axis=0)
-    per_chunk = [round(f / (m * 1e-3) / 1e12, 1) for f, m in zip(runner.flops, mean_call)]
+    per_chunk = [round(float(f / (m * 1e-3) / 1e12), 1) for f, m in zip(runner.flops, mean_call)]
     kern_tflops = flops / (mean_call.sum() * 1e-3) / 1e12
     tflops = flops / (ms_per_step * 1e-3) / 1e12
     log(f"{K} steps: {ms_per_step * 1e3:.1f} us/step, {tflops:.1f} TFLOP/s; per chunk call (us) "
-        f"{[round(m * 1e3, 1) for m in mean_call]}, TFLOP/s {per_chunk}")
+        f"{[round(float(m) * 1e3, 1) for m in mean_call]}, TFLOP/s {per_chunk}")
     result = {
         "metric": "chunked-prefill paged attention TFLOP/s (bf16 MFMA)",
         "value": round(tflops, 2),
@@ -635,7 +636,7 @@ def prefill_bench(args) -> dict:
         },
         "prefill_tokens_per_s": round(sum(q.shape[1] for q in runner.q) / (ms_per_step * 1e-3), 1),
         "max_abs_err_sampled": err,
-        "per_chunk_call_us": [round(m * 1e3, 2) for m in mean_call],
+        "per_chunk_call_us": [round(float(m) * 1e3, 2) for m in mean_call],
         "per_chunk_tflops": per_chunk,
         "roofline": {
             "kernel": "prefill_kernel<bf16, 128>",

@@ -251,7 +251,7 @@ int32_t pkv_pool_ref_count(const pkv_block_pool* pool, int32_t block);
 int64_t pkv_pool_evictions(const pkv_block_pool* pool);
 
 /* Attention of several query tokens per sequence over its paged cache, for
- * speculative verification and small prefill chunks.  (Habr article,
+ * speculative verification and chunked prefill.  (Habr article,
  * section 6 "Chunked Prefill": a chunk of new tokens runs next to decode
  * tokens and attends to everything cached before it; "Chapter 8 -
  * Next-generation KV cache", closing section: speculative decoding verifies
@@ -261,12 +261,17 @@ int64_t pkv_pool_evictions(const pkv_block_pool* pool);
  * n - q_len + i:
  *   out[b][i][h] = softmax_t(scale * q[b][i][h] . K_b[t]) V_b[t],  t <= n - q_len + i
  *   q, out   [num_seqs][q_len][num_q_heads][head_dim], q_dtype
- * All other arguments, the lengths' clamping, the kernels and the result for
- * q_len == 1 are those of pkv_paged_decode_ex (which is this call with
- * q_len == 1).  A query that sees no token (n < q_len) gets zeros.
- * q_len * (num_q_heads / num_kv_heads) must be at most 16 (the query tokens
- * of a group share one 16-column matrix tile): PKV_EUNSUPPORTED otherwise;
- * q_len < 1 is PKV_EINVAL.
+ * All other arguments, the lengths' clamping and the result for q_len == 1
+ * are those of pkv_paged_decode_ex (which is this call with q_len == 1).  A
+ * query that sees no token (n < q_len) gets zeros.
+ * Kernels: with at most 16 query columns (q_len * (num_q_heads /
+ * num_kv_heads) (query token, head) pairs per kv head) the call runs the
+ * decode's split and merge kernels, all of a group's columns sharing one
+ * 16-column matrix tile; with more (chunked prefill) it runs one many-query
+ * kernel in which every workgroup owns up to 256 columns of one (sequence,
+ * kv head) pair and walks all its keys, and num_workers and the workspace
+ * are not used (workspace may be NULL).  More than 2^24 columns is
+ * PKV_EUNSUPPORTED; q_len < 1 is PKV_EINVAL.
  *   workspace  pkv_attention_workspace_bytes(...) bytes, as for decode. */
 int pkv_paged_attention(const pkv_cache_desc* desc, const void* q, const void* k_pool,
                         const void* v_pool, const int32_t* block_tables,
@@ -276,7 +281,8 @@ int pkv_paged_attention(const pkv_cache_desc* desc, const void* q, const void* k
                         size_t workspace_bytes, void* stream);
 
 /* Workspace bytes of pkv_paged_attention: as pkv_decode_workspace_bytes with
- * q_len * group columns per partial state.  0 on bad arguments. */
+ * q_len * group columns per partial state; a nominal 256 for more than 16
+ * columns (the many-query kernel uses none).  0 on bad arguments. */
 size_t pkv_attention_workspace_bytes(const pkv_cache_desc* desc, int32_t num_seqs, int32_t q_len,
                                      int32_t max_context_len, int32_t num_workers);
 

@@ -52,9 +52,6 @@ __device__ __forceinline__ int clamp_len(int n, const DecodeArgs& a) {
 // Chunks of one sequence: 32-token steps covering its n tokens.
 __device__ __forceinline__ int chunks_of(int n) { return (n + kChunkTokens - 1) / kChunkTokens; }
 
-// A value every lane holds: keep it in a scalar register.
-__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
-
 __device__ __forceinline__ int wave_sum(int v) {
 #pragma unroll
   for (int s = 32; s >= 1; s >>= 1) v += __shfl_xor(v, s);

@@ -35,6 +35,8 @@
 #include "pkv_internal.h"
 #include "tile_math.h"
 
+#include <type_traits>
+
 namespace pkv {
 namespace {
 
@@ -43,9 +45,19 @@ namespace {
 // weights stay below 2^8 and most chunks skip the accumulator rescale.
 constexpr float kRescaleSlack = 8.f;
 
+// s_waitcnt immediate for "vector memory counter 0, others unchanged"
+// (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+constexpr int kVmcntZero = 0x0F70;
+
+// LDS bank rule for 16-byte reads (measured on MI355X with the LDS bank
+// conflict counter): the 16 lanes of each quarter-wave are served together,
+// and lanes reading rows r = 0..15 of a tile at a row stride S are
+// conflict-free when S is 32 bytes plus a multiple of 64 (S = 80, 144 or 272
+// bytes conflict two-way).  Both tiles use such strides.
+//
 // LDS row of chunk token t in the K tile.  The 16 lanes of a lane group read
-// the rows of tokens 8 (r / 4) + 4 x + (r % 4), r < 16: row stride an odd
-// multiple of 16 bytes plus this row permutation puts them in distinct banks.
+// the rows of tokens 8 (r / 4) + 4 x + (r % 4), r < 16; without this row
+// permutation those rows conflict at every stride.
 __device__ __forceinline__ int k_row(int t) { return t ^ ((t >> 1) & 12); }
 
 template <int KV, int D>
@@ -62,8 +74,8 @@ struct PrefillCfg {
   static constexpr int kWaves = KV == kF32 ? 4 : 8;              // waves per workgroup
   static constexpr int kWaveCols = 16 * kT;
   static constexpr int kGroupCols = kWaves * kWaveCols;          // columns per workgroup
-  static constexpr int kSK = D + kPerPiece;                      // K tile row stride (elements)
-  static constexpr int kSV = kChunkTokens + kPerPiece;           // V tile row stride (elements)
+  static constexpr int kSK = D + 32 / kEs;                       // K tile row stride: +32 bytes
+  static constexpr int kSV = kChunkTokens + (KV == kFP8 ? 64 : 32) / kEs;   // V row: 96 / 96 / 160 bytes
   static constexpr int kKRowPieces = D / kPerPiece;
   static constexpr int kVRowPieces = kChunkTokens / kPerPiece;
   static constexpr int kKPieces = kChunkTokens * kKRowPieces;
@@ -137,6 +149,18 @@ __device__ __forceinline__ void lds_v(typename PrefillCfg<KV, D>::Tile::V& v,
   }
 }
 
+// Flip the sign of every element of a query operand (sign bits only: exact).
+template <typename Q>
+__device__ __forceinline__ void negate_q(Q& q) {
+  for (auto& v : q.op) {
+    using V = std::remove_reference_t<decltype(v)>;
+    constexpr uint32_t kSign = std::is_same_v<V, f32x4> ? 0x80000000u : 0x80008000u;
+    u32x4 w = __builtin_bit_cast(u32x4, v);
+    w ^= u32x4{kSign, kSign, kSign, kSign};
+    v = __builtin_bit_cast(V, w);
+  }
+}
+
 // Row sums of the weights by the matrix cores: an all-ones A operand times
 // P^T gives, in every row of its output, each column's sum over the chunk's
 // 32 tokens (of the bf16-rounded weights the P.V product uses).
@@ -170,8 +194,10 @@ __device__ __forceinline__ void prefill_body(const DecodeArgs& a, const int32_t*
   constexpr int kTiles = D / 16;
   constexpr size_t kQBytes = (KV == kF32) ? 4 : 2;
 
-  __shared__ __attribute__((aligned(16))) Elem lds_kt[2][C::kKTileElems];
-  __shared__ __attribute__((aligned(16))) Elem lds_vt[2][C::kVTileElems];
+  // Three chunk buffers: chunk c + 2 is staged while chunk c is computed and
+  // chunk c + 1's operands are read.
+  __shared__ __attribute__((aligned(16))) Elem lds_kt[3][C::kKTileElems];
+  __shared__ __attribute__((aligned(16))) Elem lds_vt[3][C::kVTileElems];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -215,12 +241,17 @@ __device__ __forceinline__ void prefill_body(const DecodeArgs& a, const int32_t*
   const int kend = max(0, base + group_last / G);
   const int nck = (kend + kChunkTokens - 1) / kChunkTokens;
 
+  // Score scale in log2 units, kept non-negative: a negative scale flips the
+  // sign of the queries instead (exact), so the max of the raw scores times
+  // sl is the max of the scaled ones and the scale folds into one fma.
   float sl = a.scale * kLog2e;
   float mul = 1.f;
   if constexpr (KV == kFP8) {
     sl *= k_scale[g];
     mul = v_scale[g];
   }
+  const bool neg = sl < 0.f;
+  sl = fabsf(sl);
 
   typename T::Q qop[kT];
 #pragma unroll
@@ -228,15 +259,45 @@ __device__ __forceinline__ void prefill_body(const DecodeArgs& a, const int32_t*
     const uint8_t* row = static_cast<const uint8_t*>(a.q) +
                          (((size_t)b * L + qi[t]) * Hq + (size_t)g * G + qh[t]) * D * kQBytes;
     T::load_q(qop[t], row, col0 + 16 * t + r < NC, j);
+    if (neg) negate_q(qop[t]);
   }
 
   // ---- chunk staging: pool -> registers -> LDS ----
+  // Pieces are ordered half-major (tokens 0-15 of the chunk, then 16-31), so
+  // every wave's pieces come from one 16-token half: the half's address in
+  // the pool is a per-chunk scalar and each thread adds fixed 32-bit offsets.
+  //   K piece p: half p / (16 KR), token (p / KR) % 16, dims (p % KR) * kPerPiece
+  //   V piece p: half p / (D VH), dim (p / VH) % D, tokens (p % VH) * kPerPiece
+  // (KR = pieces per K row, VH = pieces per 16 tokens of a V row).
   const int bs = a.block_size;
   const int bshift = a.block_shift;
   const int32_t* table = tables + (size_t)b * a.max_blocks;
   const int last_blk = ((n + bs - 1) >> bshift) - 1;
-  const Elem* kpool = static_cast<const Elem*>(a.k_pool);
-  const Elem* vpool = static_cast<const Elem*>(a.v_pool);
+  const char* kpool = static_cast<const char*>(a.k_pool);
+  const char* vpool = static_cast<const char*>(a.v_pool);
+  constexpr int KR = C::kKRowPieces;
+  constexpr int VH = C::kVRowPieces / 2;
+  constexpr int kEs = C::kEs;
+  uint32_t k_src[C::kKPerThread], v_src[C::kVPerThread];   // byte offsets inside a half
+  int k_dst[C::kKPerThread], v_dst[C::kVPerThread];        // LDS element offsets
+  int k_half[C::kKPerThread], v_half[C::kVPerThread], v_tok[C::kVPerThread];
+#pragma unroll
+  for (int i = 0; i < C::kKPerThread; ++i) {
+    const int p = tid + C::kThreads * i;
+    const int u = (p / KR) % 16, e = p % KR;
+    k_half[i] = uni(p / (16 * KR));
+    k_src[i] = (uint32_t)((u * D + e * C::kPerPiece) * kEs);
+    k_dst[i] = k_row(16 * k_half[i] + u) * C::kSK + e * C::kPerPiece;
+  }
+#pragma unroll
+  for (int i = 0; i < C::kVPerThread; ++i) {
+    const int p = tid + C::kThreads * i;
+    const int d = (p / VH) % D, q = p % VH;
+    v_half[i] = uni(p / (D * VH));
+    v_tok[i] = 16 * v_half[i] + q * C::kPerPiece;
+    v_src[i] = (uint32_t)((d * bs + q * C::kPerPiece) * kEs);
+    v_dst[i] = d * C::kSV + v_tok[i];
+  }
   struct Stage {
     u32x4 k[C::kKPerThread];
     u32x4 v[C::kVPerThread];
@@ -244,60 +305,45 @@ __device__ __forceinline__ void prefill_body(const DecodeArgs& a, const int32_t*
 
   auto stage_load = [&](int c) {
     const int t0 = c * kChunkTokens;
-    // Blocks holding the chunk's two 16-token halves.
+    // Blocks holding the chunk's two 16-token halves, and where each half
+    // starts in its block's K tile and V tile (wave-uniform).
     const int i0 = min(max(table[min(t0 >> bshift, last_blk)], 0), a.num_blocks - 1);
     const int i1 = min(max(table[min((t0 + 16) >> bshift, last_blk)], 0), a.num_blocks - 1);
     const int off0 = t0 & (bs - 1);
     const int off1 = (t0 + 16) & (bs - 1);
+    const size_t tile0 = ((size_t)i0 * Hkv + g) * bs * D, tile1 = ((size_t)i1 * Hkv + g) * bs * D;
+    const char* kb0 = kpool + (tile0 + (size_t)off0 * D) * kEs;
+    const char* kb1 = kpool + (tile1 + (size_t)off1 * D) * kEs;
+    const char* vb0 = vpool + (tile0 + off0) * kEs;
+    const char* vb1 = vpool + (tile1 + off1) * kEs;
 #pragma unroll
-    for (int i = 0; i < C::kKPerThread; ++i) {
-      const int p = tid + C::kThreads * i;
-      if (C::kKPieces % C::kThreads == 0 || p < C::kKPieces) {
-        const int t = p / C::kKRowPieces;
-        const int e = p - t * C::kKRowPieces;
-        const int h = t >> 4;
-        const size_t blk = (size_t)(h ? i1 : i0) * Hkv + g;
-        const Elem* src = kpool + (blk * bs + (h ? off1 : off0) + (t & 15)) * D + e * C::kPerPiece;
-        st.k[i] = *reinterpret_cast<const u32x4*>(src);
-      }
-    }
+    for (int i = 0; i < C::kKPerThread; ++i)
+      if (C::kKPieces % C::kThreads == 0 || tid + C::kThreads * i < C::kKPieces)
+        st.k[i] = *reinterpret_cast<const u32x4*>((k_half[i] ? kb1 : kb0) + k_src[i]);
 #pragma unroll
-    for (int i = 0; i < C::kVPerThread; ++i) {
-      const int p = tid + C::kThreads * i;
-      if (C::kVPieces % C::kThreads == 0 || p < C::kVPieces) {
-        const int d = p / C::kVRowPieces;
-        const int tk = (p - d * C::kVRowPieces) * C::kPerPiece;
-        const int h = tk >> 4;
-        const size_t blk = (size_t)(h ? i1 : i0) * Hkv + g;
-        const Elem* src = vpool + blk * bs * D + (size_t)d * bs + (h ? off1 : off0) + (tk & 15);
-        u32x4 x = *reinterpret_cast<const u32x4*>(src);
-        // V rows at or past n may hold anything (NaN too): zero them, since
-        // their zero weights would not cancel a NaN.
-        const int valid = n - (t0 + tk);
-        if (valid < C::kPerPiece) x = keep_bytes(x, max(valid, 0) * C::kEs);
-        st.v[i] = x;
+    for (int i = 0; i < C::kVPerThread; ++i)
+      if (C::kVPieces % C::kThreads == 0 || tid + C::kThreads * i < C::kVPieces)
+        st.v[i] = *reinterpret_cast<const u32x4*>((v_half[i] ? vb1 : vb0) + v_src[i]);
+    // V rows at or past n may hold anything (NaN too): zero them, since
+    // their zero weights would not cancel a NaN.  Only a sequence's last
+    // chunk has such rows.
+    if (t0 + kChunkTokens > n) {
+#pragma unroll
+      for (int i = 0; i < C::kVPerThread; ++i) {
+        const int valid = n - (t0 + v_tok[i]);
+        if (valid < C::kPerPiece) st.v[i] = keep_bytes(st.v[i], max(valid, 0) * kEs);
       }
     }
   };
   auto stage_store = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < C::kKPerThread; ++i) {
-      const int p = tid + C::kThreads * i;
-      if (C::kKPieces % C::kThreads == 0 || p < C::kKPieces) {
-        const int t = p / C::kKRowPieces;
-        const int e = p - t * C::kKRowPieces;
-        *reinterpret_cast<u32x4*>(&lds_kt[buf][k_row(t) * C::kSK + e * C::kPerPiece]) = st.k[i];
-      }
-    }
+    for (int i = 0; i < C::kKPerThread; ++i)
+      if (C::kKPieces % C::kThreads == 0 || tid + C::kThreads * i < C::kKPieces)
+        *reinterpret_cast<u32x4*>(&lds_kt[buf][k_dst[i]]) = st.k[i];
 #pragma unroll
-    for (int i = 0; i < C::kVPerThread; ++i) {
-      const int p = tid + C::kThreads * i;
-      if (C::kVPieces % C::kThreads == 0 || p < C::kVPieces) {
-        const int d = p / C::kVRowPieces;
-        const int tk = (p - d * C::kVRowPieces) * C::kPerPiece;
-        *reinterpret_cast<u32x4*>(&lds_vt[buf][d * C::kSV + tk]) = st.v[i];
-      }
-    }
+    for (int i = 0; i < C::kVPerThread; ++i)
+      if (C::kVPieces % C::kThreads == 0 || tid + C::kThreads * i < C::kVPieces)
+        *reinterpret_cast<u32x4*>(&lds_vt[buf][v_dst[i]]) = st.v[i];
   };
 
   // Per column tile: accumulator, the reference max m_ref of its
@@ -307,57 +353,86 @@ __device__ __forceinline__ void prefill_body(const DecodeArgs& a, const int32_t*
   constexpr bool kMfmaSum = KV != kF32;
   f32x4 acc[kT][kTiles];
   f32x4 lsum[kT];
-  float m_ref[kT], l_run[kT];
+  float m_ref[kT], m_ref_next[kT], l_run[kT];
 #pragma unroll
   for (int t = 0; t < kT; ++t) {
 #pragma unroll
     for (int u = 0; u < kTiles; ++u) acc[t][u] = f32x4{0.f, 0.f, 0.f, 0.f};
     lsum[t] = f32x4{0.f, 0.f, 0.f, 0.f};
     m_ref[t] = -INFINITY;
+    m_ref_next[t] = -INFINITY;
     l_run[t] = 0.f;
   }
 
-  auto compute = [&](int buf, int t0) {
-    typename T::K kf;
-    typename T::V vf;
-    lds_k<KV, D>(kf, lds_kt[buf], r, j);
-    lds_v<KV, D>(vf, lds_vt[buf], r, j);
-    const bool diag = t0 + kChunkTokens > lim_lo;   // some column's causal limit falls in this chunk
+  // One chunk for this wave's column tiles, in two straight-line phases so
+  // that one tile's MFMAs overlap the other's vector work: (A) scores of all
+  // tiles, their scaled maxima; a rarely taken rescale; (B) weights and P.V
+  // of all tiles.  `kMask`: some column's causal limit falls in the chunk.
+  // The chunk's K and V operands (kf, vf) were read from LDS before; once
+  // the score MFMAs have taken kf, the next chunk's K operand is read into
+  // it (buffer `nbuf`, when `more`), and vf likewise after the P.V MFMAs, so
+  // LDS latency hides behind this chunk's work.
+  typename T::K kf;
+  typename T::V vf;
+  auto compute = [&](int t0, int nbuf, bool more, auto mask_tag) {
+    constexpr bool kMask = decltype(mask_tag)::value;
+    f32x4 sx[kT], sy[kT];
+#pragma unroll
+    for (int t = 0; t < kT; ++t) T::scores(kf, qop[t], sx[t], sy[t]);
+    if (more) lds_k<KV, D>(kf, lds_kt[nbuf], r, j);
+    float s[kT][8];   // raw scores q . k; scaled inside the exponent
+    int nvalid[kT];
+    bool raise[kT];
+    bool any = false;
 #pragma unroll
     for (int t = 0; t < kT; ++t) {
-      f32x4 sx, sy;
-      T::scores(kf, qop[t], sx, sy);
-      float s[8] = {sx[0] * sl, sx[1] * sl, sx[2] * sl, sx[3] * sl,
-                    sy[0] * sl, sy[1] * sl, sy[2] * sl, sy[3] * sl};
-      if (diag) {
-        const int nvalid = min(max(lim[t] - (t0 + 8 * j), 0), 8);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        s[t][k] = sx[t][k];
+        s[t][k + 4] = sy[t][k];
+      }
+      if constexpr (kMask) {
+        nvalid[t] = min(max(lim[t] - (t0 + 8 * j), 0), 8);
 #pragma unroll
         for (int k = 0; k < 8; ++k)
-          if (k >= nvalid) s[k] = -INFINITY;
+          if (k >= nvalid[t]) s[t][k] = -INFINITY;
       }
-      float mloc = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])),
-                         fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
-      mloc = row_max4(mloc);
+      // Scores here are finite or -inf: rows past a sequence's end (which
+      // may hold NaN) only occur in masked chunks, where they are -inf.
+      float mraw = fmax_nq(fmax_nq(fmax_nq(s[t][0], s[t][1]), fmax_nq(s[t][2], s[t][3])),
+                           fmax_nq(fmax_nq(s[t][4], s[t][5]), fmax_nq(s[t][6], s[t][7])));
+      mraw = row_max4_nq(mraw);
+      const float mloc = mraw == -INFINITY ? -INFINITY : mraw * sl;   // sl >= 0
       // Raise the reference only when this chunk's max passes it by more
       // than the slack (the first chunk with a visible token always does).
-      const bool raise = mloc > m_ref[t] + kRescaleSlack;
-      if (__builtin_amdgcn_ballot_w64(raise)) {
+      raise[t] = mloc > m_ref[t] + kRescaleSlack;
+      any |= raise[t];
+      if (raise[t]) m_ref_next[t] = mloc;
+    }
+    if (__builtin_amdgcn_ballot_w64(any)) {
+#pragma unroll
+      for (int t = 0; t < kT; ++t) {
         // Lanes that keep their reference use factor 1 (never exp2(-inf - -inf)
         // for a column that has seen nothing); a first raise gives exp2(-inf) = 0.
-        const float m_new = raise ? mloc : m_ref[t];
-        const float corr = raise ? exp2_fast(m_ref[t] - m_new) : 1.f;
+        const float corr = raise[t] ? exp2_fast(m_ref[t] - m_ref_next[t]) : 1.f;
 #pragma unroll
         for (int u = 0; u < kTiles; ++u) acc[t][u] *= corr;
         if constexpr (kMfmaSum) lsum[t] *= corr;
         else l_run[t] *= corr;
-        m_ref[t] = m_new;
+        m_ref[t] = m_ref_next[t];
       }
+    }
+#pragma unroll
+    for (int t = 0; t < kT; ++t) {
       // A column that has seen no token keeps -inf and is exponentiated
       // against 0, so its weights are 0, never NaN.
       const float m_use = m_ref[t] == -INFINITY ? 0.f : m_ref[t];
       float pk[8];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) pk[k] = exp2_fast(s[k] - m_use);
+      for (int k = 0; k < 8; ++k) {
+        pk[k] = exp2_fast(fmaf(s[t][k], sl, -m_use));
+        if constexpr (kMask) pk[k] = k < nvalid[t] ? pk[k] : 0.f;   // also when sl == 0
+      }
       if constexpr (kMfmaSum) {
         bf16x8 pb;
 #pragma unroll
@@ -368,19 +443,44 @@ __device__ __forceinline__ void prefill_body(const DecodeArgs& a, const int32_t*
         l_run[t] += T::pv(acc[t], vf, pk);
       }
     }
+    if (more) lds_v<KV, D>(vf, lds_vt[nbuf], r, j);
   };
 
+  // Pipeline: before iteration c, chunks c and c + 1 are in LDS (c's operands
+  // already in registers); iteration c stages chunk c + 2 into the buffer
+  // chunk c - 1 used, whose operands every wave read during iteration c - 2
+  // (before the barrier that ended it).
   if (nck > 0) {
     stage_load(0);
     stage_store(0);
   }
+  if (nck > 1) {
+    stage_load(1);
+    stage_store(1);
+  }
+  // Every load issued so far (queries included) has landed: without this
+  // wait the compiler's counters would treat the query operands as pending
+  // inside the loop and make each iteration wait for its own staging loads.
+  __builtin_amdgcn_s_waitcnt(kVmcntZero);
   __syncthreads();
+  if (nck > 0 && kend_w > 0) {
+    lds_k<KV, D>(kf, lds_kt[0], r, j);
+    lds_v<KV, D>(vf, lds_vt[0], r, j);
+  }
+  int buf = 0;   // buffer of chunk c
   for (int c = 0; c < nck; ++c) {
-    if (c + 1 < nck) stage_load(c + 1);   // next chunk's loads fly while this one is computed
+    const int nbuf = buf == 2 ? 0 : buf + 1;
+    const int sbuf = nbuf == 2 ? 0 : nbuf + 1;
+    if (c + 2 < nck) stage_load(c + 2);   // its loads fly while chunk c is computed
     const int t0 = c * kChunkTokens;
-    if (t0 < kend_w) compute(c & 1, t0);
-    if (c + 1 < nck) stage_store((c + 1) & 1);
+    if (t0 < kend_w) {
+      const bool more = t0 + kChunkTokens < kend_w;   // this wave computes chunk c + 1 too
+      if (t0 + kChunkTokens > lim_lo) compute(t0, nbuf, more, std::true_type{});
+      else compute(t0, nbuf, more, std::false_type{});
+    }
+    if (c + 2 < nck) stage_store(sbuf);
     __syncthreads();
+    buf = nbuf;
   }
 
   OutT* out = static_cast<OutT*>(a.out);

@@ -24,6 +24,9 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// A value every lane holds: keep it in a scalar register.
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Operand loads.  With NT the load is non-temporal: bytes read once per call
@@ -46,6 +49,21 @@ __device__ __forceinline__ float row_max4(float v) {
   u = __builtin_bit_cast(uint32_t, v);
   auto s32 = __builtin_amdgcn_permlane32_swap(u, u, false, false);
   return fmaxf(__builtin_bit_cast(float, (uint32_t)s32[0]), __builtin_bit_cast(float, (uint32_t)s32[1]));
+}
+
+// IEEE 754-2019 maximum (v_maximum3_f32 on gfx950): propagates NaN, so the
+// compiler needs no quieting step before it; for scores that are finite or
+// -inf it is the ordinary max.
+__device__ __forceinline__ float fmax_nq(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
+// row_max4 for values that are never NaN, without quieting steps.
+__device__ __forceinline__ float row_max4_nq(float v) {
+  uint32_t u = __builtin_bit_cast(uint32_t, v);
+  auto s16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  v = fmax_nq(__builtin_bit_cast(float, (uint32_t)s16[0]), __builtin_bit_cast(float, (uint32_t)s16[1]));
+  u = __builtin_bit_cast(uint32_t, v);
+  auto s32 = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmax_nq(__builtin_bit_cast(float, (uint32_t)s32[0]), __builtin_bit_cast(float, (uint32_t)s32[1]));
 }
 
 __device__ __forceinline__ float row_sum4(float v) {
