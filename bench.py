@@ -49,25 +49,29 @@ def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
+PREFILL_SOURCES = ["paged_kv_cache_23_amd/csrc/prefill.hip", "paged_kv_cache_23_amd/csrc/tile_math.h",
+                   "paged_kv_cache_23_amd/csrc/pkv_internal.h"]
+
+
+def kernel_source_hash(sources=None) -> str:
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in (KERNEL_SOURCES if sources is None else sources):
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def committed_traffic(workload: str):
-    """HBM bytes per pkv_paged_decode call (both kernels) from the committed
-    rocprofv3 counter summary, if it was taken on the current kernel source;
-    else None."""
-    path = os.path.join(PROFILE_DIR, f"paged_decode_{workload}_hbm_traffic.txt")
+def committed_traffic(workload: str, kind: str = "paged_decode", sources=None):
+    """HBM bytes per launch unit (one pkv_paged_decode call, or one prefill
+    step) from the committed rocprofv3 counter summary, if it was taken on
+    the current kernel source; else None."""
+    path = os.path.join(PROFILE_DIR, f"{kind}_{workload}_hbm_traffic.txt")
     if not os.path.exists(path):
         return None
     text = open(path).read()
     m_hash = re.search(r"^source_hash:\s*(\w+)", text, re.M)
     m_bytes = re.search(r"^hbm_bytes_per_launch:\s*([0-9.eE+]+)", text, re.M)
-    if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash():
+    if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash(sources):
         return None
     return float(m_bytes.group(1))
 
@@ -645,7 +649,8 @@ def prefill_bench(args) -> dict:
             "peak": MFMA_BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(kern_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-            "traffic": None,
+            "traffic": committed_traffic(wl.name, "prefill_kernel", PREFILL_SOURCES),
+            "traffic_unit": "HBM bytes per step (five calls)",
             "algorithmic_flops_per_step": flops,
             "mean_step_kernel_us": round(float(mean_call.sum()) * 1e3, 2),
         },
