@@ -18,19 +18,20 @@
 // loaded once into LDS and used by every column of a workgroup.
 //
 // Work decomposition.  Columns c = i * G + h of a (sequence, kv head) pair
-// are cut into workgroup tiles of 4 * 16 * kT columns; one workgroup of four
-// waves owns one tile and walks every 32-token key chunk up to the tile's
-// last visible token, so no partial results leave the workgroup.  Wave w owns
-// kT MFMA column tiles of 16 columns; the four waves stage each chunk's K
-// (token-major) and V (dimension-major) from the pool into double-buffered
-// LDS together, one barrier per chunk.  Workgroups are issued largest first
-// (the last column tiles see the most keys), and workgroups of the same pair
-// are spaced by the pair count, so with a pair count divisible by 8 they land
-// on the same XCD and share its L2.
+// are cut into workgroup tiles of kWaves * 16 * kT columns (256: eight waves
+// of two 16-column MFMA tiles, two waves per SIMD; float32: four waves, one
+// per SIMD); a workgroup owns one tile and walks every 32-token key chunk up
+// to the tile's last visible token, so no partial results leave the
+// workgroup.  The waves stage each chunk's K (token-major) and V
+// (dimension-major) from the pool into LDS together (three chunk buffers, one
+// barrier per chunk) and each reads its operands from there.  Workgroups are
+// issued largest first (the last column tiles see the most keys), and
+// workgroups of the same pair are spaced by the pair count, so with a pair
+// count divisible by 8 they land on the same XCD and share its L2.
 //
 // Tile math: the transposed-score layout of the decode kernel (tile_math.h):
-// per chunk and column tile, 2 * D/32 score MFMAs and D/16 P.V MFMAs (bf16),
-// all operands read from LDS with 16-byte reads.
+// per chunk and column tile, 2 * D/32 score MFMAs, D/16 P.V MFMAs and one
+// row-sum MFMA (bf16), all operands read from LDS with 16-byte reads.
 
 #include "pkv_internal.h"
 #include "tile_math.h"
