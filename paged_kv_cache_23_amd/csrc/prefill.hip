@@ -82,6 +82,9 @@ struct PrefillCfg {
   static constexpr int kKPieces = kChunkTokens * kKRowPieces;
   static constexpr int kVPieces = D * kVRowPieces;
   static constexpr int kThreads = 64 * kWaves;
+  // Chunks per barrier: two (64 keys) where three pairs of chunk tiles fit
+  // in LDS, one for the float32 tiles.
+  static constexpr int kPair = KV == kF32 ? 1 : 2;
   static constexpr int kKPerThread = (kKPieces + kThreads - 1) / kThreads;
   static constexpr int kVPerThread = (kVPieces + kThreads - 1) / kThreads;
   static constexpr int kKTileElems = kChunkTokens * kSK;
@@ -197,8 +200,8 @@ __device__ __forceinline__ void prefill_body(const DecodeArgs& a, const int32_t*
 
   // Three chunk buffers: chunk c + 2 is staged while chunk c is computed and
   // chunk c + 1's operands are read.
-  __shared__ __attribute__((aligned(16))) Elem lds_kt[3][C::kKTileElems];
-  __shared__ __attribute__((aligned(16))) Elem lds_vt[3][C::kVTileElems];
+  __shared__ __attribute__((aligned(16))) Elem lds_kt[3 * C::kPair][C::kKTileElems];
+  __shared__ __attribute__((aligned(16))) Elem lds_vt[3 * C::kPair][C::kVTileElems];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -447,17 +450,17 @@ __device__ __forceinline__ void prefill_body(const DecodeArgs& a, const int32_t*
     if (more) lds_v<KV, D>(vf, lds_vt[nbuf], r, j);
   };
 
-  // Pipeline: before iteration c, chunks c and c + 1 are in LDS (c's operands
-  // already in registers); iteration c stages chunk c + 2 into the buffer
-  // chunk c - 1 used, whose operands every wave read during iteration c - 2
-  // (before the barrier that ended it).
-  if (nck > 0) {
-    stage_load(0);
-    stage_store(0);
-  }
-  if (nck > 1) {
-    stage_load(1);
-    stage_store(1);
+  // Pipeline over groups of kPair chunks (one barrier per group).  Chunk c
+  // lives in LDS buffer kPair * ((c / kPair) % 3) + c % kPair.  Before
+  // iteration p (chunks kPair p ...), groups p and p + 1 are in LDS;
+  // iteration p stages group p + 2 into group p - 1's buffers, one chunk
+  // after each chunk step; group p - 1's operands were read by the end of
+  // iteration p - 1 (before the barrier that ended it).
+  constexpr int kP = C::kPair;
+  auto bufof = [](int c) { return kP * ((c / kP) % 3) + c % kP; };
+  for (int c = 0; c < 2 * kP && c < nck; ++c) {
+    stage_load(c);
+    stage_store(bufof(c));
   }
   // Every load issued so far (queries included) has landed: without this
   // wait the compiler's counters would treat the query operands as pending
@@ -468,20 +471,21 @@ __device__ __forceinline__ void prefill_body(const DecodeArgs& a, const int32_t*
     lds_k<KV, D>(kf, lds_kt[0], r, j);
     lds_v<KV, D>(vf, lds_vt[0], r, j);
   }
-  int buf = 0;   // buffer of chunk c
-  for (int c = 0; c < nck; ++c) {
-    const int nbuf = buf == 2 ? 0 : buf + 1;
-    const int sbuf = nbuf == 2 ? 0 : nbuf + 1;
-    if (c + 2 < nck) stage_load(c + 2);   // its loads fly while chunk c is computed
-    const int t0 = c * kChunkTokens;
-    if (t0 < kend_w) {
-      const bool more = t0 + kChunkTokens < kend_w;   // this wave computes chunk c + 1 too
-      if (t0 + kChunkTokens > lim_lo) compute(t0, nbuf, more, std::true_type{});
-      else compute(t0, nbuf, more, std::false_type{});
+  for (int c = 0; c < nck; c += kP) {
+#pragma unroll
+    for (int h = 0; h < kP; ++h) {
+      const int cc = c + h;
+      if (cc + 2 * kP < nck) stage_load(cc + 2 * kP);   // its loads fly while chunk cc is computed
+      const int t0 = cc * kChunkTokens;
+      if (cc < nck && t0 < kend_w) {
+        const bool more = t0 + kChunkTokens < kend_w;   // this wave computes chunk cc + 1 too
+        const int nbuf = bufof(cc + 1);
+        if (t0 + kChunkTokens > lim_lo) compute(t0, nbuf, more, std::true_type{});
+        else compute(t0, nbuf, more, std::false_type{});
+      }
+      if (cc + 2 * kP < nck) stage_store(bufof(cc + 2 * kP));
     }
-    if (c + 2 < nck) stage_store(sbuf);
     __syncthreads();
-    buf = nbuf;
   }
 
   OutT* out = static_cast<OutT*>(a.out);
