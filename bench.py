@@ -54,10 +54,16 @@ PREFILL_SOURCES = ["paged_kv_cache_23_amd/csrc/prefill.hip", "paged_kv_cache_23_
 
 
 def kernel_source_hash(sources=None) -> str:
+    """sha256[:16] of the kernel sources' code: '//' comments, trailing
+    blanks and empty lines are dropped first, so a change to the prose alone
+    keeps the recorded measurements valid."""
     h = hashlib.sha256()
     for rel in (KERNEL_SOURCES if sources is None else sources):
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            for line in f:
+                code = re.sub(r"//.*$", "", line).rstrip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 

@@ -23,8 +23,9 @@
 // per SIMD); a workgroup owns one tile and walks every 32-token key chunk up
 // to the tile's last visible token, so no partial results leave the
 // workgroup.  The waves stage each chunk's K (token-major) and V
-// (dimension-major) from the pool into LDS together (three chunk buffers, one
-// barrier per chunk) and each reads its operands from there.  Workgroups are
+// (dimension-major) from the pool into LDS together (three groups of two
+// chunk buffers, one barrier per group) and each reads its operands from
+// there.  Workgroups are
 // issued largest first (the last column tiles see the most keys), and
 // workgroups of the same pair are spaced by the pair count, so with a pair
 // count divisible by 8 they land on the same XCD and share its L2.
