@@ -135,3 +135,32 @@ def test_ten_thousand_token_prompt_in_chunks_sampled():
             lens = np.array([int(wl.context_lens[0]) - L + 1 + i], dtype=np.int32)
             ref = oracle.oracle_decode(**dict(args, q=qh[:, i], context_lens=lens))
             assert_close(torch.from_numpy(got[:, i]), ref, "bf16")
+
+
+def test_lengths_are_clamped_like_decode():
+    """A length above max_context_len (a caller's bound) is clamped to it, as
+    for decode: the chunk's queries then sit at the clamped length's end."""
+    L = 24
+    wl, q = _case("bf16", 128, 4, L, [300, 150], seed=93)
+    dev = Dev(wl)
+    out = ops.paged_attention(q.cuda(), dev.k_pool, dev.v_pool, dev.tables, dev.lens, wl.scale,
+                              max_context_len=200)
+    clamped = dict(oracle_args(wl), context_lens=np.minimum(wl.context_lens.numpy(), 200))
+    ref = oracle.oracle_attention_multi(**dict(clamped, q=storage_numpy(q)))
+    assert_close(out.reshape(wl.batch, -1, 128), ref.reshape(wl.batch, -1, 128), "bf16")
+
+
+def test_many_short_chunks_and_empty_sequences():
+    """64 sequences with 5-token chunks (20 columns per kv head: one partly
+    filled workgroup each), every fourth sequence empty."""
+    L = 5
+    rng = np.random.default_rng(94)
+    lens = [0 if b % 4 == 3 else int(rng.integers(L, 400)) for b in range(64)]
+    wl, q = _case("bf16", 128, 4, L, lens, seed=94, Hkv=2)
+    out = out_f64(_run(wl, q))
+    keep = [b for b in range(64) if lens[b] > 0]
+    sub = dict(oracle_args(wl), block_tables=wl.block_tables.numpy()[keep],
+               context_lens=wl.context_lens.numpy()[keep])
+    ref = oracle.oracle_attention_multi(**dict(sub, q=storage_numpy(q)[keep]))
+    assert_close(torch.from_numpy(out[keep]), ref, "bf16")
+    assert not out[[b for b in range(64) if lens[b] == 0]].any()
