@@ -13,9 +13,12 @@
 // kernel reads keys and values by indirect addressing through the table.
 //
 // Work decomposition.  The batch is a list of 32-token chunks (two blocks)
-// of every (sequence, kv head) pair.  One worker wave per SIMD slot of the
+// of every (sequence, kv head) pair, head-major (all of kv head 0's
+// sequences, then kv head 1's, ...).  One worker wave per SIMD slot of the
 // GPU takes an equal contiguous range of that list (stream-K style), so all
-// waves stream the same bytes; it keeps a running max / sum / accumulator per
+// waves stream the same bytes, and the workgroups of one XCD take adjacent
+// ranges, so a block shared by many sequences is re-read from that XCD's L2.
+// Each wave keeps a running max / sum / accumulator per
 // pair segment for the pair's whole query group.  A pair that one wave covers
 // completely is finished by that wave; a pair split between waves leaves one
 // float32 partial per wave, combined by decode_merge_kernel.
@@ -67,8 +70,8 @@ __device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
   return v;
 }
 
-// Position of a chunk in the global order: pairs (b, g) sequence-major, chunk
-// c of the pair's cb chunks, global chunk index x.  All fields are
+// Position of a chunk in the global order: pairs (b, g) head-major, chunk c
+// of the pair's cb chunks, global chunk index x.  All fields are
 // wave-uniform.
 struct Pos {
   int b, g, c, cb, n;
@@ -79,15 +82,15 @@ struct Pos {
 // Split kernel.
 //
 // The batch's work is the list of 32-token chunks of every (sequence, kv head)
-// pair, pairs ordered sequence-major.  Worker wave w (one per SIMD slot of the
+// pair, pairs ordered head-major.  Worker wave w (one per SIMD slot of the
 // GPU, all resident at once) takes the contiguous chunk range
 // [w*K, (w+1)*K), K = ceil(chunks / workers), so every wave streams the same
 // number of bytes.  It walks its range pair by pair with one online-softmax
 // state.  A pair that lies wholly inside the range is finished at once.  A
 // pair shared with other waves (at most the first and the last pair of a
 // range) leaves a float32 partial (max, sum, unnormalised accumulator) in slot
-// w + pair of the workspace; slots are unique because ranges are contiguous
-// and ordered.  The wave that holds a pair's first chunk records the pair's
+// w + (the pair's place in the order) of the workspace; slots are unique
+// because ranges are contiguous and ordered.  The wave that holds a pair's first chunk records the pair's
 // first wave and number of parts for the merge kernel.
 // ---------------------------------------------------------------------------
 template <int KV, int D, bool KNT, bool VNT>
@@ -103,7 +106,13 @@ __device__ __forceinline__ void split_body(const DecodeArgs& a, const int32_t* _
   const int lane = threadIdx.x & 63;
   const int r = lane & 15;
   const int j = lane >> 4;
-  const int wid = __builtin_amdgcn_readfirstlane(blockIdx.x * kDecodeWaves + (threadIdx.x >> 6));
+  // Workgroups are dealt to the 8 XCDs round robin; renumber them so that
+  // each XCD's workgroups take consecutive ranges (one kv head's chunks each
+  // when there are 8 kv heads): blocks shared by several sequences are then
+  // re-read from that XCD's own L2.
+  int blk = blockIdx.x;
+  if ((gridDim.x & 7) == 0) blk = (blk & 7) * (gridDim.x >> 3) + (blk >> 3);
+  const int wid = __builtin_amdgcn_readfirstlane(blk * kDecodeWaves + (threadIdx.x >> 6));
   const int W = a.num_workers;
   const int B = a.num_seqs;
   const int Hkv = a.num_kv_heads;
@@ -149,7 +158,11 @@ __device__ __forceinline__ void split_body(const DecodeArgs& a, const int32_t* _
   const int64_t x1 = min(x0 + K, C);
   const int nch = (int)(x1 - x0);
 
-  // the sequence holding chunk x0: Hkv*before(b) <= x0 < Hkv*(before(b) + cb)
+  // Chunks are ordered head-major: kv head g's list is every sequence's
+  // chunks in sequence order, total chunks per head.  Chunk x0 is chunk r0 of
+  // head g0's list, in the sequence with before(b) <= r0 < before(b) + cb.
+  const int g0 = uni((int)(x0 / total));
+  const int64_t r0 = x0 - (int64_t)g0 * total;
   int b0 = 0;
   int64_t before0 = 0;
   {
@@ -159,7 +172,7 @@ __device__ __forceinline__ void split_body(const DecodeArgs& a, const int32_t* _
       const int cb = bi < B ? chunks_of(B <= 64 ? n_lane : clamp_len(lens[bi], a)) : 0;
       const int incl = wave_inclusive_scan(cb, lane);
       const int64_t ex = run + incl - cb;
-      const bool hit = cb > 0 && (int64_t)Hkv * ex <= x0 && x0 < (int64_t)Hkv * (ex + cb);
+      const bool hit = cb > 0 && ex <= r0 && r0 < ex + cb;
       const uint64_t mask = __builtin_amdgcn_ballot_w64(hit);
       if (mask) {
         const int idx = uni(__builtin_ctzll(mask));
@@ -175,23 +188,20 @@ __device__ __forceinline__ void split_body(const DecodeArgs& a, const int32_t* _
   pos.n = seq_len(b0);
   pos.cb = chunks_of(pos.n);
   pos.x = x0;
-  {
-    const int off = uni((int)(x0 - (int64_t)Hkv * before0));
-    pos.g = uni(off / pos.cb);
-    pos.c = uni(off - pos.g * pos.cb);
-  }
+  pos.g = g0;
+  pos.c = uni((int)(r0 - before0));
   auto advance = [&](Pos q) -> Pos {
     ++q.x;
     if (++q.c == q.cb) {
       q.c = 0;
-      if (++q.g == Hkv) {
-        q.g = 0;
-        do {   // skip empty sequences; a next chunk exists, so this ends
-          ++q.b;
-          q.n = seq_len(q.b);
-          q.cb = chunks_of(q.n);
-        } while (q.cb == 0);
-      }
+      do {   // next sequence (then next head), skipping empty ones; a next chunk exists, so this ends
+        if (++q.b == B) {
+          q.b = 0;
+          ++q.g;
+        }
+        q.n = seq_len(q.b);
+        q.cb = chunks_of(q.n);
+      } while (q.cb == 0);
     }
     return q;
   };
@@ -275,7 +285,7 @@ __device__ __forceinline__ void split_body(const DecodeArgs& a, const int32_t* _
         for (int t = 0; t < kTiles; ++t) store4<OutT>(dst + 16 * t, acc[t] * f);
       }
     } else {
-      const size_t slot = (size_t)wid + pair;
+      const size_t slot = (size_t)wid + (size_t)q.g * B + q.b;   // wave + the pair's place in the chunk order
       if (r < NC) {
         float* dst = a.ws_acc + (slot * NC + r) * D + 4 * j;
 #pragma unroll
@@ -407,7 +417,7 @@ template <typename OutT, int D>
 __global__ __launch_bounds__(128) void decode_merge_kernel(const int2* __restrict__ meta,
                                                            const float* __restrict__ ws_acc,
                                                            const float* __restrict__ ws_ml, OutT* __restrict__ out,
-                                                           int num_kv_heads, int group, int q_len) {
+                                                           int num_seqs, int num_kv_heads, int group, int q_len) {
   const int pair = blockIdx.x;
   const int2 m = meta[pair];
   if (m.y <= 1) return;   // one wave covered the pair and wrote its output
@@ -415,6 +425,7 @@ __global__ __launch_bounds__(128) void decode_merge_kernel(const int2* __restric
   const int NC = q_len * G;   // (query token, query head) columns of the pair
   const int b = pair / num_kv_heads;
   const int g = pair - b * num_kv_heads;
+  const size_t place = (size_t)g * num_seqs + b;   // the pair's place in the head-major chunk order
   const size_t Hq = (size_t)num_kv_heads * G;
   for (int e = threadIdx.x; e < NC * (D / 4); e += 128) {
     const int c = e / (D / 4);
@@ -424,7 +435,7 @@ __global__ __launch_bounds__(128) void decode_merge_kernel(const int2* __restric
     f32x4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
     for (int w = m.x; w < m.x + m.y; ++w) {
-      const size_t slot = ((size_t)w + pair) * NC + c;
+      const size_t slot = ((size_t)w + place) * NC + c;
       const float2 ml = *reinterpret_cast<const float2*>(ws_ml + slot * 2);
       const f32x4 acc_w = *reinterpret_cast<const f32x4*>(ws_acc + slot * D + 4 * q4);
       const float M2 = fmaxf(M, ml.x);
@@ -468,8 +479,8 @@ hipError_t launch_merge_t(const DecodeArgs& a, hipStream_t stream) {
   const unsigned grid = (unsigned)a.num_seqs * (unsigned)a.num_kv_heads;
   hipLaunchKernelGGL((decode_merge_kernel<OutT, D>), dim3(grid), dim3(128), 0, stream,
                      static_cast<const int2*>(a.pair_meta), static_cast<const float*>(a.ws_acc),
-                     static_cast<const float*>(a.ws_ml), static_cast<OutT*>(a.out), a.num_kv_heads, a.group,
-                     a.q_len);
+                     static_cast<const float*>(a.ws_ml), static_cast<OutT*>(a.out), a.num_seqs, a.num_kv_heads,
+                     a.group, a.q_len);
   return hipGetLastError();
 }
 
