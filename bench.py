@@ -86,7 +86,7 @@ class Runner:
     """Pre-marshalled C-ABI calls for one workload on the current stream."""
 
     def __init__(self, wl, layers: int, workers: int = 0, identity_tables: bool = False, q_len: int = 1,
-                 reread: bool = False):
+                 reread: bool = False, shared_prefix: int = 0):
         import torch
         from paged_kv_cache_23_amd import ops
 
@@ -135,11 +135,20 @@ class Runner:
         lib = ops.library()
         self.lib = lib
         self.explicit_workers = bool(workers)
-        self.workers = workers or lib.pkv_decode_workers(ctypes.byref(self.desc), self.B, self.max_ctx)
+        # the shared-prefix call sizes its workers for the tails after the prefix
+        self.workers = workers or lib.pkv_decode_workers(ctypes.byref(self.desc), self.B,
+                                                         max(self.max_ctx - int(shared_prefix), 0))
         if self.workers <= 0:
             raise RuntimeError(f"pkv_decode_workers failed: {self.workers}")
-        nbytes = lib.pkv_attention_workspace_bytes(ctypes.byref(self.desc), self.B, self.q_len, self.max_ctx,
-                                                   self.workers)
+        self.prefix = int(shared_prefix)
+        if self.prefix:
+            if self.q_len != 1:
+                raise ValueError("the shared-prefix decode takes one query token per sequence")
+            nbytes = lib.pkv_shared_decode_workspace_bytes(ctypes.byref(self.desc), self.B, self.max_ctx, self.prefix,
+                                                           self.workers if self.explicit_workers else 0)
+        else:
+            nbytes = lib.pkv_attention_workspace_bytes(ctypes.byref(self.desc), self.B, self.q_len, self.max_ctx,
+                                                       self.workers)
         if nbytes == 0:
             raise RuntimeError("pkv_attention_workspace_bytes rejected the shape")
         self.ws = ops.new_workspace(nbytes, dev)
@@ -163,7 +172,13 @@ class Runner:
 
     def decode(self, layer: int, stream):
         workers = self.workers if self.explicit_workers else 0
-        if self.q_len == 1:
+        if self.prefix:
+            st = self.lib.pkv_paged_decode_shared(
+                ctypes.byref(self.desc), self.q.data_ptr(), self.k_pools[layer].data_ptr(),
+                self.v_pools[layer].data_ptr(), self.tables.data_ptr(), self.tables.shape[1], self.lens.data_ptr(),
+                self.B, self.max_ctx, self.prefix, self.wl.scale, workers, self.out.data_ptr(), self.ws.data_ptr(),
+                self.ws_bytes, stream)
+        elif self.q_len == 1:
             st = self.lib.pkv_paged_decode_ex(
                 ctypes.byref(self.desc), self.q.data_ptr(), self.k_pools[layer].data_ptr(),
                 self.v_pools[layer].data_ptr(), self.tables.data_ptr(), self.tables.shape[1], self.lens.data_ptr(),
@@ -182,6 +197,21 @@ class Runner:
         if self.append:
             self.append_step(layer, stream)
         self.decode(layer, stream)
+
+
+def common_prefix_tokens(tables, lens, block_size: int) -> int:
+    """Tokens in the leading blocks that every table row shares (whole blocks
+    that every sequence fills)."""
+    import numpy as np
+
+    tables, lens = np.asarray(tables), np.asarray(lens)
+    if tables.shape[0] == 0:
+        return 0
+    full = int(lens.min()) // block_size
+    k = 0
+    while k < full and np.all(tables[:, k] == tables[0, k]):
+        k += 1
+    return k * block_size
 
 
 def unique_kv_bytes(wl, after_append: bool) -> int:
@@ -271,20 +301,36 @@ def cpu_baseline(wl, min_seconds: float = 10.0, max_reps: int = 20):
     }
 
 
-def run_bench(args) -> dict:
-    import numpy as np
-    import torch
-
+def make_runner(args):
+    """The workload and its pre-marshalled calls, in the launch configuration
+    that the benchmark times (and that --profile-one profiles)."""
     from paged_kv_cache_23_amd import workloads as W
 
     wl = W.WORKLOADS[args.workload](block_size=args.block_size)
     log(f"workload {wl.name}: B={wl.batch} Hq={wl.num_q_heads} Hkv={wl.num_kv_heads} D={wl.head_dim} "
         f"kv={wl.kv_dtype} blocks={wl.num_blocks} KV={wl.kv_bytes() / 1e6:.1f} MB")
+    after = wl.k_new is not None
     # a scheduler knows from its reference counts whether the batch shares
     # blocks; here: when the distinct token slots are fewer than 90% of those read
-    shares = unique_kv_bytes(wl, wl.k_new is not None) < 0.9 * wl.kv_bytes(after_append=wl.k_new is not None)
-    reread = shares if args.reread == "auto" else args.reread == "on"
-    runner = Runner(wl, args.layers, args.workers, args.identity_tables, args.q_len, reread)
+    shares = unique_kv_bytes(wl, after) < 0.9 * wl.kv_bytes(after_append=after)
+    prefix = 0
+    if args.shared:
+        prefix = common_prefix_tokens((wl.block_tables_after if after else wl.block_tables).numpy(),
+                                      (wl.context_lens_after if after else wl.context_lens).numpy(), args.block_size)
+        if prefix == 0:
+            raise SystemExit(f"--shared: the tables of {wl.name} share no leading block")
+        log(f"shared-prefix decode: {prefix} tokens ({prefix // args.block_size} blocks) read once per call")
+    # the shared-prefix call reads the prefix once and every tail once: streamed loads
+    reread = (shares and not prefix) if args.reread == "auto" else args.reread == "on"
+    runner = Runner(wl, args.layers, args.workers, args.identity_tables, args.q_len, reread, prefix)
+    return wl, runner, prefix, reread
+
+
+def run_bench(args) -> dict:
+    import numpy as np
+    import torch
+
+    wl, runner, prefix, reread = make_runner(args)
     streamed = not reread and args.block_size <= 32
     loads = "streamed (non-temporal)" if streamed else (
         "cached (PKV_KV_REREAD: blocks shared)" if reread else "cached (blocks above 32 tokens)")
@@ -335,9 +381,13 @@ def run_bench(args) -> dict:
 
     step_bytes = runner.kv_bytes + runner.append_bytes
     gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
-    kern_gbs = runner.kv_bytes / (part_ms.mean() * 1e-3) / 1e9
-    traffic = committed_traffic(wl.name)
     unique = unique_kv_bytes(wl, runner.append)
+    # the shared-prefix call's algorithmic bytes are the distinct slots: the
+    # prefix once plus every tail
+    algo = unique if prefix else runner.kv_bytes
+    kern_gbs = algo / (part_ms.mean() * 1e-3) / 1e9
+    traffic = (committed_traffic(wl.name, "paged_decode_shared", KERNEL_SOURCES + PREFILL_SOURCES[:1]) if prefix
+               else committed_traffic(wl.name))
     result = {
         "metric": METRIC,
         "value": round(gbs, 2),
@@ -360,6 +410,7 @@ def run_bench(args) -> dict:
             "kv_bytes_per_step": step_bytes,
             "worker_waves": runner.workers,
             "kv_loads": loads,
+            "shared_prefix_tokens": prefix,
         },
         "hbm_peak_frac": round(gbs / HBM_PEAK_GBS, 4),
         "unique_kv_bytes_per_step": unique,
@@ -368,14 +419,16 @@ def run_bench(args) -> dict:
         "query_tokens_per_seq": args.q_len,
         "max_abs_err_sampled": err,
         "roofline": {
-            "kernel": "pkv_paged_decode (decode_split_kernel + decode_merge_kernel)",
+            "kernel": ("pkv_paged_decode_shared (prefill_kernel over the prefix + decode_split_kernel + "
+                       "decode_merge_kernel)" if prefix else
+                       "pkv_paged_decode (decode_split_kernel + decode_merge_kernel)"),
             "bound": "hbm",
             "achieved": round(kern_gbs, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(kern_gbs / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "algorithmic_bytes_per_launch": runner.kv_bytes,
+            "algorithmic_bytes_per_launch": algo,
             "mean_call_us": round(float(part_ms.mean()) * 1e3, 2),
         },
     }
@@ -390,10 +443,7 @@ def run_bench(args) -> dict:
 def profile_one(args) -> None:
     import torch
 
-    from paged_kv_cache_23_amd import workloads as W
-
-    wl = W.WORKLOADS[args.workload]()
-    runner = Runner(wl, args.layers, args.workers)
+    wl, runner, _, _ = make_runner(args)
     s = runner.stream()
     for i in range(args.warmup):
         runner.step(i % args.layers, s)
@@ -698,6 +748,8 @@ def main() -> int:
     p.add_argument("--block-size", type=int, default=16, help="tokens per cache block (16, 32, 64, 128, 256)")
     p.add_argument("--reread", choices=["auto", "on", "off"], default="auto",
                    help="PKV_KV_REREAD hint: auto = on when the tables share blocks")
+    p.add_argument("--shared", action="store_true",
+                   help="decode through pkv_paged_decode_shared: the tables' common leading blocks read once")
     p.add_argument("--prefill", action="store_true",
                    help="time chunked prefill (a 10,000-token prompt in 2048-token chunks) instead")
     p.add_argument("--q-len", type=int, default=1,

@@ -158,7 +158,8 @@ size_t pkv_decode_workspace_bytes(const pkv_cache_desc* desc, int32_t num_seqs,
  * Accumulation is float32; out is rounded once to q_dtype (nearest even).
  *
  * Two kernels on `stream`.  The batch's 32-token chunks of every (sequence,
- * kv head) pair, pairs in sequence-major order, are cut into equal contiguous
+ * kv head) pair, pairs in kv-head-major order (every sequence of kv head 0,
+ * then of kv head 1, ...), are cut into equal contiguous
  * ranges, one per worker wave; each wave runs section 3's online softmax over
  * its range and finishes every pair it covers completely; sequences of length
  * 0 get their zero output there too.  For a pair split between waves each wave
@@ -183,6 +184,43 @@ int pkv_paged_decode_ex(const pkv_cache_desc* desc, const void* q, const void* k
                         int32_t num_seqs, int32_t max_context_len, float scale,
                         int32_t num_workers, void* out, void* workspace,
                         size_t workspace_bytes, void* stream);
+
+/* Decode over a batch whose sequences all begin with the same shared blocks
+ * (parallel sampling or best-of-n over one prompt: Habr article, section 4,
+ * "Copy-on-Write for parallel sampling", where the variants reference the
+ * prompt's physical blocks instead of copies; LLM Primer, "Chapter 8 —
+ * Next-generation KV cache", 8.1: best-of-8 on a 2,000-token prompt).  The
+ * result is
+ * pkv_paged_decode_ex's for the same arguments, up to float32 rounding
+ * order; the prefix's blocks are read from HBM once per call instead of once
+ * per sequence.
+ *   prefix_tokens  tokens at the start of every sequence held in the same
+ *                  blocks: entries j < prefix_tokens / B of every table row
+ *                  equal row 0's.  A multiple of the block size B, at most
+ *                  max_context_len and B * max_blocks_per_seq (else
+ *                  PKV_EINVAL); 0 runs pkv_paged_decode_ex.  Every
+ *                  sequence's (clamped) length must be at least prefix_tokens;
+ *                  for one that is not, or a row that differs in the prefix,
+ *                  the output is unspecified (no access leaves the pools).
+ * Three kernels on `stream`: (1) the many-query kernel runs every sequence's
+ * query heads over the prefix (row 0's blocks) as the columns of one
+ * (virtual) sequence per kv head, the prefix cut into key segments, and
+ * leaves float32 partials (max, sum, unnormalised accumulator) per segment;
+ * (2) the decode split kernel runs each sequence's tokens after the prefix,
+ * leaving partials only; (3) the merge kernel combines both sets of partials
+ * per (sequence, head) with section 3's rescale and writes out.
+ *   workspace  pkv_shared_decode_workspace_bytes(...) bytes (same num_workers),
+ *              16-byte aligned scratch; calls sharing it must be ordered. */
+size_t pkv_shared_decode_workspace_bytes(const pkv_cache_desc* desc, int32_t num_seqs,
+                                         int32_t max_context_len, int32_t prefix_tokens,
+                                         int32_t num_workers);
+
+int pkv_paged_decode_shared(const pkv_cache_desc* desc, const void* q, const void* k_pool,
+                            const void* v_pool, const int32_t* block_tables,
+                            int32_t max_blocks_per_seq, const int32_t* context_lens,
+                            int32_t num_seqs, int32_t max_context_len, int32_t prefix_tokens,
+                            float scale, int32_t num_workers, void* out, void* workspace,
+                            size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Host block pool with a prefix-cache index (no GPU work; not thread-safe:

@@ -175,6 +175,51 @@ DecodeArgs make_args(const pkv_cache_desc* d, const void* q, const void* k_pool,
 
 int launch_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ELAUNCH; }
 
+// Shared-prefix decode: key segments of the prefix pass.  About one
+// workgroup per compute unit (each segment adds a float32 partial per query
+// head that is written and read back), at least kMinSegChunks chunks of 32
+// keys per segment, and no segment left empty.
+constexpr int64_t kSegGroupsPerCu = 1;
+constexpr int64_t kMinSegChunks = 4;
+
+int32_t prefix_segments(const pkv_cache_desc* d, int32_t num_seqs, int32_t prefix_tokens) {
+  const int cus = device_cus();
+  if (cus <= 0) return PKV_ELAUNCH;
+  const int64_t cols = (int64_t)num_seqs * (d->num_q_heads / d->num_kv_heads);
+  const int64_t gc = pkv::prefill_group_cols(d->kv_dtype);
+  const int64_t groups = (cols + gc - 1) / gc * d->num_kv_heads;
+  const int64_t chunks = ((int64_t)prefix_tokens + pkv::kChunkTokens - 1) / pkv::kChunkTokens;
+  int64_t s = (kSegGroupsPerCu * cus + groups - 1) / groups;
+  const int64_t cap = chunks / kMinSegChunks;
+  if (s > cap) s = cap;
+  if (s > 1024) s = 1024;
+  if (s < 1) s = 1;
+  const int64_t per = (chunks + s - 1) / s;   // the kernel's chunks per segment
+  return (int32_t)((chunks + per - 1) / per);
+}
+
+// Prefix partials after the decode workspace: accumulators [S][B*Hq][D],
+// then (max, sum) pairs [S][B*Hq][2].
+size_t prefix_acc_bytes(const pkv_cache_desc* d, int32_t num_seqs, int32_t segments) {
+  return align_up((size_t)segments * num_seqs * d->num_q_heads * d->head_dim * sizeof(float));
+}
+size_t prefix_ml_bytes(const pkv_cache_desc* d, int32_t num_seqs, int32_t segments) {
+  return align_up((size_t)segments * num_seqs * d->num_q_heads * 2 * sizeof(float));
+}
+
+// The decode's tail part only reads the tokens after the prefix.
+int32_t tail_ctx(int32_t max_ctx, int32_t prefix_tokens) {
+  return max_ctx > prefix_tokens ? max_ctx - prefix_tokens : 0;
+}
+
+// The prefix is whole blocks of the table, and no longer than the caller's
+// bound on the lengths (every sequence holds at least the prefix).
+int check_prefix(const pkv_cache_desc* d, int32_t prefix_tokens, int32_t max_blocks, int32_t max_ctx) {
+  if (prefix_tokens < 0 || prefix_tokens % d->block_size != 0) return PKV_EINVAL;
+  if (prefix_tokens / d->block_size > max_blocks || prefix_tokens > max_ctx) return PKV_EINVAL;
+  return PKV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -288,6 +333,74 @@ int pkv_paged_decode(const pkv_cache_desc* desc, const void* q, const void* k_po
                      size_t ws_bytes, void* stream) {
   return pkv_paged_decode_ex(desc, q, k_pool, v_pool, block_tables, max_blocks_per_seq, context_lens, num_seqs,
                              max_context_len, scale, 0, out, workspace, ws_bytes, stream);
+}
+
+size_t pkv_shared_decode_workspace_bytes(const pkv_cache_desc* desc, int32_t num_seqs, int32_t max_context_len,
+                                         int32_t prefix_tokens, int32_t num_workers) {
+  if (check_desc(desc) != PKV_OK || num_seqs < 0 || max_context_len < 0 || prefix_tokens < 0) return 0;
+  if (prefix_tokens % desc->block_size != 0 || prefix_tokens > max_context_len) return 0;
+  const int32_t w = resolve_workers(desc, num_seqs, tail_ctx(max_context_len, prefix_tokens), num_workers);
+  if (w <= 0) return 0;
+  const int32_t s = prefix_tokens > 0 ? prefix_segments(desc, num_seqs, prefix_tokens) : 0;
+  if (s < 0) return 0;
+  return workspace_bytes(desc, num_seqs, 1, w) + prefix_acc_bytes(desc, num_seqs, s) +
+         prefix_ml_bytes(desc, num_seqs, s);
+}
+
+int pkv_paged_decode_shared(const pkv_cache_desc* desc, const void* q, const void* k_pool, const void* v_pool,
+                            const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                            int32_t num_seqs, int32_t max_context_len, int32_t prefix_tokens, float scale,
+                            int32_t num_workers, void* out, void* workspace, size_t ws_bytes, void* stream) {
+  int st = check_decode_args(desc, q, k_pool, v_pool, block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                             max_context_len, out);
+  if (st != PKV_OK) return st;
+  st = check_prefix(desc, prefix_tokens, max_blocks_per_seq, max_context_len);
+  if (st != PKV_OK) return st;
+  if (prefix_tokens == 0)
+    return pkv_paged_decode_ex(desc, q, k_pool, v_pool, block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                               max_context_len, scale, num_workers, out, workspace, ws_bytes, stream);
+  const int32_t tctx = tail_ctx(max_context_len, prefix_tokens);
+  const int32_t w = resolve_workers(desc, num_seqs, tctx, num_workers);
+  if (w <= 0) return w == 0 ? PKV_EINVAL : w;
+  if (num_seqs == 0) return PKV_OK;
+  const int32_t segs = prefix_segments(desc, num_seqs, prefix_tokens);
+  if (segs < 0) return segs;
+  const size_t dec = workspace_bytes(desc, num_seqs, 1, w);
+  if (!workspace || ws_bytes < dec + prefix_acc_bytes(desc, num_seqs, segs) + prefix_ml_bytes(desc, num_seqs, segs))
+    return PKV_EWORKSPACE;
+  if (!aligned16(workspace)) return PKV_EINVAL;
+  char* ws = static_cast<char*>(workspace);
+  float* pre_acc = reinterpret_cast<float*>(ws + dec);
+  float* pre_ml = reinterpret_cast<float*>(ws + dec + prefix_acc_bytes(desc, num_seqs, segs));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  // 1. the prefix for every sequence at once: one virtual sequence whose
+  //    query tokens are the batch's sequences, over row 0's prefix blocks
+  DecodeArgs pa = make_args(desc, q, k_pool, v_pool, block_tables, max_blocks_per_seq, context_lens, 1, num_seqs,
+                            max_context_len, scale, w, out, nullptr);
+  pa.prefix_mode = 1;
+  pa.prefix_tokens = prefix_tokens;
+  pa.pre_segments = segs;
+  pa.pre_acc = pre_acc;
+  pa.pre_ml = pre_ml;
+  if (pkv::prefill_groups(pa) > 0x7FFFFFFF) return PKV_EUNSUPPORTED;
+  hipError_t e = pkv::launch_prefill(pa, s);
+  if (e != hipSuccess) return PKV_ELAUNCH;
+  // 2. every sequence's own tokens after the prefix, all as partials
+  //    (each row read from its first block after the prefix; the row stride
+  //    stays max_blocks_per_seq)
+  const int32_t pblocks = prefix_tokens / desc->block_size;
+  DecodeArgs ta = make_args(desc, q, k_pool, v_pool, block_tables + pblocks, max_blocks_per_seq, context_lens,
+                            num_seqs, 1, max_context_len, scale, w, out, workspace);
+  ta.table_offset = pblocks;
+  ta.tail_pass = 1;
+  e = pkv::launch_split(ta, s);
+  if (e != hipSuccess) return PKV_ELAUNCH;
+  // 3. merge the tail pieces with the prefix segments
+  ta.pre_acc = pre_acc;
+  ta.pre_ml = pre_ml;
+  ta.pre_segments = segs;
+  return launch_status(pkv::launch_merge(ta, s));
 }
 
 const char* pkv_strerror(int status) {

@@ -46,9 +46,14 @@
 namespace pkv {
 namespace {
 
+// Tokens of a sequence that this call reads: its length clamped to the
+// caller's bound and the table's capacity; in the tail pass of a
+// shared-prefix decode (kTail), minus the prefix's table_offset blocks.
+template <bool kTail>
 __device__ __forceinline__ int clamp_len(int n, const DecodeArgs& a) {
   n = min(n, a.max_context_len);
   n = (int)min((int64_t)n, (int64_t)a.max_blocks * a.block_size);
+  if constexpr (kTail) n -= a.table_offset * a.block_size;
   return max(n, 0);
 }
 
@@ -93,7 +98,7 @@ struct Pos {
 // because ranges are contiguous and ordered.  The wave that holds a pair's first chunk records the pair's
 // first wave and number of parts for the merge kernel.
 // ---------------------------------------------------------------------------
-template <int KV, int D, bool KNT, bool VNT>
+template <int KV, int D, bool KNT, bool VNT, bool kTail>
 __device__ __forceinline__ void split_body(const DecodeArgs& a, const int32_t* __restrict__ tables,
                                             const int32_t* __restrict__ lens, const float* __restrict__ k_scale,
                                             const float* __restrict__ v_scale) {
@@ -132,22 +137,24 @@ __device__ __forceinline__ void split_body(const DecodeArgs& a, const int32_t* _
   int n_lane = 0;      // length of sequence `lane` (kept when the batch has <= 64 sequences)
   for (int base = 0; base < B; base += 64) {
     const int bi = base + lane;
-    n_lane = bi < B ? clamp_len(lens[bi], a) : 0;
+    n_lane = bi < B ? clamp_len<kTail>(lens[bi], a) : 0;
     total += uni(wave_sum(chunks_of(n_lane)));
   }
   // Length of sequence b: from the registers when the whole batch fits one
   // wave, else a scalar load.
   auto seq_len = [&](int b) -> int {
     if (B <= 64) return uni(__builtin_amdgcn_readlane(n_lane, uni(b)));
-    return uni(clamp_len(lens[uni(b)], a));
+    return uni(clamp_len<kTail>(lens[uni(b)], a));
   };
   // Sequences with no tokens: wave b mod W writes their zero output and a
   // (first wave 0, parts 0) record per pair, so every pair has a fresh record
   // and the merge kernel never needs the lengths.
   for (int b = wid; b < B; b += W) {
     if (seq_len(b) != 0) continue;
-    OutT* o = out + (size_t)b * L * Hq * D;
-    for (int e = lane; e < L * Hq * D; e += 64) o[e] = (OutT)0.f;
+    if constexpr (!kTail) {   // in the tail pass the merge kernel writes every output
+      OutT* o = out + (size_t)b * L * Hq * D;
+      for (int e = lane; e < L * Hq * D; e += 64) o[e] = (OutT)0.f;
+    }
     for (int g = lane; g < Hkv; g += 64) a.pair_meta[b * Hkv + g] = int2{0, 0};
   }
 
@@ -169,7 +176,7 @@ __device__ __forceinline__ void split_body(const DecodeArgs& a, const int32_t* _
     int64_t run = 0;
     for (int base = 0; base < B; base += 64) {
       const int bi = base + lane;
-      const int cb = bi < B ? chunks_of(B <= 64 ? n_lane : clamp_len(lens[bi], a)) : 0;
+      const int cb = bi < B ? chunks_of(B <= 64 ? n_lane : clamp_len<kTail>(lens[bi], a)) : 0;
       const int incl = wave_inclusive_scan(cb, lane);
       const int64_t ex = run + incl - cb;
       const bool hit = cb > 0 && ex <= r0 && r0 < ex + cb;
@@ -277,7 +284,7 @@ __device__ __forceinline__ void split_body(const DecodeArgs& a, const int32_t* _
       const int parts = (int)((s0 + q.cb - 1) / K - s0 / K) + 1;
       if (lane == 0) a.pair_meta[pair] = int2{wid, parts};
     }
-    if (seg_c0 == 0 && q.c == q.cb - 1) {   // the whole pair: finish it here
+    if (seg_c0 == 0 && q.c == q.cb - 1 && !kTail) {   // the whole pair: finish it here
       if (r < NC) {
         OutT* dst = out + (((size_t)q.b * L + qi) * Hq + q.g * G + qh) * D + 4 * j;
         const float f = l_tot > 0.f ? mul / l_tot : 0.f;   // a query that sees no token gets zeros
@@ -392,18 +399,18 @@ __device__ __forceinline__ void split_body(const DecodeArgs& a, const int32_t* _
 // per SIMD (at most 256 VGPRs each) are resident together; the float32 path at
 // head_dim 128 needs more registers for its double buffer and runs one wave
 // per SIMD instead of spilling.
-template <int KV, int D, bool KNT, bool VNT>
+template <int KV, int D, bool KNT, bool VNT, bool kTail>
 __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void decode_split_kernel(DecodeArgs a, const int32_t* __restrict__ tables, const int32_t* __restrict__ lens,
                          const float* __restrict__ k_scale, const float* __restrict__ v_scale) {
-  split_body<KV, D, KNT, VNT>(a, tables, lens, k_scale, v_scale);
+  split_body<KV, D, KNT, VNT, kTail>(a, tables, lens, k_scale, v_scale);
 }
 
-template <int KV, int D, bool KNT, bool VNT>
+template <int KV, int D, bool KNT, bool VNT, bool kTail>
 __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_split_kernel_wide(DecodeArgs a, const int32_t* __restrict__ tables, const int32_t* __restrict__ lens,
                               const float* __restrict__ k_scale, const float* __restrict__ v_scale) {
-  split_body<KV, D, KNT, VNT>(a, tables, lens, k_scale, v_scale);
+  split_body<KV, D, KNT, VNT, kTail>(a, tables, lens, k_scale, v_scale);
 }
 
 // ---------------------------------------------------------------------------
@@ -413,14 +420,17 @@ void decode_split_kernel_wide(DecodeArgs a, const int32_t* __restrict__ tables, 
 // returns at once; a split pair combines its partials with the online-softmax
 // rescale.  Two dependent round trips: the record, then the partials.
 // ---------------------------------------------------------------------------
-template <typename OutT, int D>
+template <typename OutT, int D, bool kPrefix>
 __global__ __launch_bounds__(128) void decode_merge_kernel(const int2* __restrict__ meta,
                                                            const float* __restrict__ ws_acc,
                                                            const float* __restrict__ ws_ml, OutT* __restrict__ out,
-                                                           int num_seqs, int num_kv_heads, int group, int q_len) {
+                                                           int num_seqs, int num_kv_heads, int group, int q_len,
+                                                           const float* __restrict__ pre_acc,
+                                                           const float* __restrict__ pre_ml, int pre_segments) {
   const int pair = blockIdx.x;
   const int2 m = meta[pair];
-  if (m.y <= 1) return;   // one wave covered the pair and wrote its output
+  // One wave covered the pair and wrote its output (no shared-prefix pieces).
+  if (m.y <= 1 && !kPrefix) return;
   const int G = group;
   const int NC = q_len * G;   // (query token, query head) columns of the pair
   const int b = pair / num_kv_heads;
@@ -446,19 +456,44 @@ __global__ __launch_bounds__(128) void decode_merge_kernel(const int2* __restric
       o = o * f_old + acc_w * f_new;
       M = M2;
     }
+    // Shared-prefix pieces: the same column's partials over the prefix's
+    // key segments (one query token per sequence here).  Their maximum
+    // first, then the weighted sums, so that the pieces' loads do not wait
+    // on one another.
+    if constexpr (kPrefix) {
+      const size_t col = (size_t)b * Hq + (size_t)g * G + (c - qi * G);
+      const size_t stride = (size_t)num_seqs * Hq;
+      float Mp = -INFINITY;
+#pragma unroll 8
+      for (int s = 0; s < pre_segments; ++s) Mp = fmaxf(Mp, pre_ml[(s * stride + col) * 2]);
+      const float M2 = fmaxf(M, Mp);
+      const float M2u = M2 == -INFINITY ? 0.f : M2;
+      const float f_old = exp2_fast(M - M2u);
+      L *= f_old;
+      o *= f_old;
+#pragma unroll 8
+      for (int s = 0; s < pre_segments; ++s) {
+        const size_t slot = s * stride + col;
+        const float2 ml = *reinterpret_cast<const float2*>(pre_ml + slot * 2);
+        const f32x4 acc_s = *reinterpret_cast<const f32x4*>(pre_acc + slot * D + 4 * q4);
+        const float w = exp2_fast(ml.x - M2u);
+        L += ml.y * w;
+        o += acc_s * w;
+      }
+    }
     OutT* dst = out + (((size_t)b * q_len + qi) * Hq + (size_t)g * G + (c - qi * G)) * D + 4 * q4;
     store4<OutT>(dst, o * (L > 0.f ? 1.f / L : 0.f));
   }
 }
 
-template <int KV, int D, bool KNT, bool VNT>
+template <int KV, int D, bool KNT, bool VNT, bool kTail>
 hipError_t launch_split_p(const DecodeArgs& a, hipStream_t stream) {
   const unsigned grid = (unsigned)(a.num_workers / kDecodeWaves);
   if constexpr (KV == kF32 && D == 128)
-    hipLaunchKernelGGL((decode_split_kernel_wide<KV, D, KNT, VNT>), dim3(grid), dim3(64 * kDecodeWaves), 0, stream,
+    hipLaunchKernelGGL((decode_split_kernel_wide<KV, D, KNT, VNT, kTail>), dim3(grid), dim3(64 * kDecodeWaves), 0, stream,
                        a, a.block_tables, a.context_lens, a.k_scale, a.v_scale);
   else
-    hipLaunchKernelGGL((decode_split_kernel<KV, D, KNT, VNT>), dim3(grid), dim3(64 * kDecodeWaves), 0, stream, a,
+    hipLaunchKernelGGL((decode_split_kernel<KV, D, KNT, VNT, kTail>), dim3(grid), dim3(64 * kDecodeWaves), 0, stream, a,
                        a.block_tables, a.context_lens, a.k_scale, a.v_scale);
   return hipGetLastError();
 }
@@ -468,39 +503,57 @@ hipError_t launch_split_p(const DecodeArgs& a, hipStream_t stream) {
 // sizes of 64 and more, where a 32-token chunk uses half of each V line and
 // the next chunk reads the other half (measured on MI355X: streaming only K,
 // or both, is slower there than caching both).
+template <int KV, int D, bool kTail>
+hipError_t launch_split_l(const DecodeArgs& a, hipStream_t stream) {
+  if (a.kv_reread || a.block_size > 32) return launch_split_p<KV, D, false, false, kTail>(a, stream);
+  return launch_split_p<KV, D, true, true, kTail>(a, stream);
+}
+
 template <int KV, int D>
 hipError_t launch_split_t(const DecodeArgs& a, hipStream_t stream) {
-  if (a.kv_reread || a.block_size > 32) return launch_split_p<KV, D, false, false>(a, stream);
-  return launch_split_p<KV, D, true, true>(a, stream);
+  if (a.tail_pass) return launch_split_l<KV, D, true>(a, stream);
+  return launch_split_l<KV, D, false>(a, stream);
+}
+
+template <typename OutT, int D, bool kPrefix>
+hipError_t launch_merge_p(const DecodeArgs& a, hipStream_t stream) {
+  const unsigned grid = (unsigned)a.num_seqs * (unsigned)a.num_kv_heads;
+  hipLaunchKernelGGL((decode_merge_kernel<OutT, D, kPrefix>), dim3(grid), dim3(128), 0, stream,
+                     static_cast<const int2*>(a.pair_meta), static_cast<const float*>(a.ws_acc),
+                     static_cast<const float*>(a.ws_ml), static_cast<OutT*>(a.out), a.num_seqs, a.num_kv_heads,
+                     a.group, a.q_len, a.pre_acc, a.pre_ml, a.pre_segments);
+  return hipGetLastError();
 }
 
 template <typename OutT, int D>
 hipError_t launch_merge_t(const DecodeArgs& a, hipStream_t stream) {
-  const unsigned grid = (unsigned)a.num_seqs * (unsigned)a.num_kv_heads;
-  hipLaunchKernelGGL((decode_merge_kernel<OutT, D>), dim3(grid), dim3(128), 0, stream,
-                     static_cast<const int2*>(a.pair_meta), static_cast<const float*>(a.ws_acc),
-                     static_cast<const float*>(a.ws_ml), static_cast<OutT*>(a.out), a.num_seqs, a.num_kv_heads,
-                     a.group, a.q_len);
-  return hipGetLastError();
+  if (a.pre_segments > 0) return launch_merge_p<OutT, D, true>(a, stream);
+  return launch_merge_p<OutT, D, false>(a, stream);
 }
 
 }  // namespace
 
-hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
-  hipError_t e;
-  if (a.head_dim == 64) {
-    if (a.kv_dtype == kF32) e = launch_split_t<kF32, 64>(a, stream);
-    else if (a.kv_dtype == kBF16) e = launch_split_t<kBF16, 64>(a, stream);
-    else e = launch_split_t<kFP8, 64>(a, stream);
-  } else {
-    if (a.kv_dtype == kF32) e = launch_split_t<kF32, 128>(a, stream);
-    else if (a.kv_dtype == kBF16) e = launch_split_t<kBF16, 128>(a, stream);
-    else e = launch_split_t<kFP8, 128>(a, stream);
-  }
-  if (e != hipSuccess) return e;
+hipError_t launch_merge(const DecodeArgs& a, hipStream_t stream) {
   const bool f32 = a.kv_dtype == kF32;
   if (a.head_dim == 64) return f32 ? launch_merge_t<float, 64>(a, stream) : launch_merge_t<__bf16, 64>(a, stream);
   return f32 ? launch_merge_t<float, 128>(a, stream) : launch_merge_t<__bf16, 128>(a, stream);
+}
+
+hipError_t launch_split(const DecodeArgs& a, hipStream_t stream) {
+  if (a.head_dim == 64) {
+    if (a.kv_dtype == kF32) return launch_split_t<kF32, 64>(a, stream);
+    if (a.kv_dtype == kBF16) return launch_split_t<kBF16, 64>(a, stream);
+    return launch_split_t<kFP8, 64>(a, stream);
+  }
+  if (a.kv_dtype == kF32) return launch_split_t<kF32, 128>(a, stream);
+  if (a.kv_dtype == kBF16) return launch_split_t<kBF16, 128>(a, stream);
+  return launch_split_t<kFP8, 128>(a, stream);
+}
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
+  const hipError_t e = launch_split(a, stream);
+  if (e != hipSuccess) return e;
+  return launch_merge(a, stream);
 }
 
 }  // namespace pkv

@@ -43,6 +43,14 @@ struct DecodeArgs {
   int32_t num_workers;   // decode worker waves; a multiple of kDecodeWaves
   int32_t kv_dtype;
   float scale;
+  // Shared-prefix decode (all zero otherwise).
+  int32_t table_offset;   // tail pass: prefix blocks (block_tables points past them)
+  int32_t tail_pass;      // split kernel: tail pass (lengths minus the prefix, every pair leaves partials)
+  float* pre_acc;         // merge input: prefix partials [pre_segments][num_seqs * num_q_heads][head_dim]
+  float* pre_ml;          // [pre_segments][num_seqs * num_q_heads][2]  (max in log2 units, sum)
+  int32_t pre_segments;   // merge: prefix pieces per column; prefill kernel: key segments
+  int32_t prefix_tokens;  // prefill kernel in prefix mode: keys every column sees
+  int32_t prefix_mode;    // prefill kernel: columns are the batch's query heads, output partials
 };
 
 struct AppendArgs {
@@ -79,6 +87,12 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const DecodeArgs& a, hipStream_t stream);
 // Workgroups launch_prefill starts for these arguments.
 int64_t prefill_groups(const DecodeArgs& a);
+// Query columns one prefill workgroup owns.
+int prefill_group_cols(int kv_dtype);
+// Split kernel alone, then merge kernel alone (shared-prefix decode runs the
+// prefix pass between them).
+hipError_t launch_split(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_merge(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
 hipError_t launch_copy(const CopyArgs& a, hipStream_t stream);
 size_t copy_slice_bytes();

@@ -187,7 +187,7 @@ __device__ __forceinline__ void pv_bf16(f32x4* acc, const typename PrefillCfg<KV
   }
 }
 
-template <int KV, int D>
+template <int KV, int D, bool kPrefix>
 __device__ __forceinline__ void prefill_body(const DecodeArgs& a, const int32_t* __restrict__ tables,
                                              const int32_t* __restrict__ lens, const float* __restrict__ k_scale,
                                              const float* __restrict__ v_scale) {
@@ -214,18 +214,36 @@ __device__ __forceinline__ void prefill_body(const DecodeArgs& a, const int32_t*
   const int G = a.group;
   const int L = a.q_len;
   const int NC = a.cols;
+  // Prefix mode (shared-prefix decode): one virtual sequence, the shared
+  // prefix, whose "query tokens" are the batch's sequences (q_len = batch,
+  // q rows [batch][Hq][D]); every column sees all prefix_tokens keys (no
+  // causal mask), the keys are cut into pre_segments ranges, one per
+  // workgroup, and each workgroup leaves float32 partials.
+  // (a run-time value inside the prefix instantiation: folding it there
+  // lets the compiler hoist more state than the registers hold)
+  const bool pm = kPrefix && a.prefix_mode != 0;
   const int pairs = a.num_seqs * Hkv;
   const int ncb = (NC + C::kGroupCols - 1) / C::kGroupCols;
-  const int bid = blockIdx.x;
-  const int cb = ncb - 1 - bid / pairs;   // last column tiles (most keys) first
+  int bid = blockIdx.x;
+  int seg = 0;
+  if (pm) {
+    seg = bid / (ncb * pairs);
+    bid -= seg * ncb * pairs;
+  }
+  const int cb = pm ? bid / pairs : ncb - 1 - bid / pairs;   // causal: last column tiles (most keys) first
   const int pair = bid - (bid / pairs) * pairs;
   const int b = pair / Hkv;
   const int g = pair - b * Hkv;
 
-  int n = min(lens[b], a.max_context_len);
-  n = (int)min((int64_t)n, (int64_t)a.max_blocks * a.block_size);
-  n = max(n, 0);
-  const int base = n - L + 1;   // query token i sees tokens < base + i
+  int n;
+  if (pm) {
+    n = a.prefix_tokens;
+  } else {
+    n = min(lens[b], a.max_context_len);
+    n = (int)min((int64_t)n, (int64_t)a.max_blocks * a.block_size);
+    n = max(n, 0);
+  }
+  const int base = n - L + 1;   // causal: query token i sees tokens < base + i
 
   // Columns of this lane: tile t holds column col0 + 16 t + r.
   const int col0 = cb * C::kGroupCols + wave * C::kWaveCols;
@@ -236,15 +254,25 @@ __device__ __forceinline__ void prefill_body(const DecodeArgs& a, const int32_t*
     const int cc = min(col0 + 16 * t + r, NC - 1);
     qi[t] = cc / G;
     qh[t] = cc - qi[t] * G;
-    lim[t] = base + qi[t];
+    lim[t] = pm ? n : base + qi[t];
   }
-  // Keys this wave and this workgroup need: up to their last column's limit.
+  // Keys this wave and this workgroup need: up to their last column's limit
+  // (prefix mode: the segment's end), from chunk c_begin on.
   const int wave_last = min(col0 + C::kWaveCols, NC) - 1;
-  const int kend_w = col0 < NC ? max(0, base + wave_last / G) : 0;
-  const int lim_lo = base + min(col0, NC - 1) / G;   // smallest limit of the wave
   const int group_last = min(cb * C::kGroupCols + C::kGroupCols, NC) - 1;
-  const int kend = max(0, base + group_last / G);
-  const int nck = (kend + kChunkTokens - 1) / kChunkTokens;
+  int kend = max(0, base + group_last / G);
+  int kend_w = col0 < NC ? max(0, base + wave_last / G) : 0;
+  int lim_lo = base + min(col0, NC - 1) / G;   // smallest limit of the wave
+  int c_begin = 0;
+  if (pm) {
+    const int all = (n + kChunkTokens - 1) / kChunkTokens;
+    const int per = (all + a.pre_segments - 1) / a.pre_segments;
+    c_begin = min(seg * per, all);
+    kend = min(n, (c_begin + per) * kChunkTokens);
+    kend_w = col0 < NC ? kend : 0;
+    lim_lo = n;
+  }
+  const int nck = max(0, (kend + kChunkTokens - 1) / kChunkTokens - c_begin);   // chunks from c_begin
 
   // Score scale in log2 units, kept non-negative: a negative scale flips the
   // sign of the queries instead (exact), so the max of the raw scores times
@@ -308,8 +336,8 @@ __device__ __forceinline__ void prefill_body(const DecodeArgs& a, const int32_t*
     u32x4 v[C::kVPerThread];
   } st;
 
-  auto stage_load = [&](int c) {
-    const int t0 = c * kChunkTokens;
+  auto stage_load = [&](int c) {   // c counts from c_begin
+    const int t0 = (c_begin + c) * kChunkTokens;
     // Blocks holding the chunk's two 16-token halves, and where each half
     // starts in its block's K tile and V tile (wave-uniform).
     const int i0 = min(max(table[min(t0 >> bshift, last_blk)], 0), a.num_blocks - 1);
@@ -477,7 +505,7 @@ __device__ __forceinline__ void prefill_body(const DecodeArgs& a, const int32_t*
     for (int h = 0; h < kP; ++h) {
       const int cc = c + h;
       if (cc + 2 * kP < nck) stage_load(cc + 2 * kP);   // its loads fly while chunk cc is computed
-      const int t0 = cc * kChunkTokens;
+      const int t0 = (c_begin + cc) * kChunkTokens;
       if (cc < nck && t0 < kend_w) {
         const bool more = t0 + kChunkTokens < kend_w;   // this wave computes chunk cc + 1 too
         const int nbuf = bufof(cc + 1);
@@ -489,6 +517,22 @@ __device__ __forceinline__ void prefill_body(const DecodeArgs& a, const int32_t*
     __syncthreads();
   }
 
+  if (pm) {   // partials of this key segment: (reference max, sum), unnormalised accumulator
+#pragma unroll
+    for (int t = 0; t < kT; ++t) {
+      float l_tot;
+      if constexpr (kMfmaSum) l_tot = lsum[t][0];
+      else l_tot = row_sum4(l_run[t]);
+      if (col0 + 16 * t + r < NC) {
+        const size_t slot = ((size_t)seg * L + qi[t]) * Hq + (size_t)g * G + qh[t];
+        float* dst = a.pre_acc + slot * D + 4 * j;
+#pragma unroll
+        for (int u = 0; u < kTiles; ++u) *reinterpret_cast<f32x4*>(dst + 16 * u) = acc[t][u] * mul;
+        if (j == 0) *reinterpret_cast<float2*>(a.pre_ml + slot * 2) = float2{m_ref[t], l_tot};
+      }
+    }
+    return;
+  }
   OutT* out = static_cast<OutT*>(a.out);
 #pragma unroll
   for (int t = 0; t < kT; ++t) {
@@ -506,40 +550,50 @@ __device__ __forceinline__ void prefill_body(const DecodeArgs& a, const int32_t*
 
 // Tables, lengths and scales as restrict parameters: nothing the kernel
 // writes aliases them, so their wave-uniform reads use the scalar cache.
-template <int KV, int D>
+template <int KV, int D, bool kPrefix>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_kernel(DecodeArgs a, const int32_t* __restrict__ tables, const int32_t* __restrict__ lens,
                     const float* __restrict__ k_scale, const float* __restrict__ v_scale) {
-  prefill_body<KV, D>(a, tables, lens, k_scale, v_scale);
+  prefill_body<KV, D, kPrefix>(a, tables, lens, k_scale, v_scale);
 }
 
-template <int KV, int D>
+template <int KV, int D, bool kPrefix>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void prefill_kernel_wide(DecodeArgs a, const int32_t* __restrict__ tables, const int32_t* __restrict__ lens,
                          const float* __restrict__ k_scale, const float* __restrict__ v_scale) {
-  prefill_body<KV, D>(a, tables, lens, k_scale, v_scale);
+  prefill_body<KV, D, kPrefix>(a, tables, lens, k_scale, v_scale);
+}
+
+template <int KV, int D, bool kPrefix>
+hipError_t launch_prefill_p(const DecodeArgs& a, hipStream_t stream) {
+  using C = PrefillCfg<KV, D>;
+  const int64_t ncb = (a.cols + C::kGroupCols - 1) / C::kGroupCols;
+  const int64_t grid = ncb * a.num_seqs * a.num_kv_heads * (kPrefix ? a.pre_segments : 1);
+  if (grid <= 0) return hipSuccess;
+  if constexpr (KV == kF32)
+    hipLaunchKernelGGL((prefill_kernel_wide<KV, D, kPrefix>), dim3((unsigned)grid), dim3(C::kThreads), 0, stream,
+                       a, a.block_tables, a.context_lens, a.k_scale, a.v_scale);
+  else
+    hipLaunchKernelGGL((prefill_kernel<KV, D, kPrefix>), dim3((unsigned)grid), dim3(C::kThreads), 0, stream, a,
+                       a.block_tables, a.context_lens, a.k_scale, a.v_scale);
+  return hipGetLastError();
 }
 
 template <int KV, int D>
 hipError_t launch_prefill_t(const DecodeArgs& a, hipStream_t stream) {
-  using C = PrefillCfg<KV, D>;
-  const int64_t ncb = (a.cols + C::kGroupCols - 1) / C::kGroupCols;
-  const int64_t grid = ncb * a.num_seqs * a.num_kv_heads;
-  if (grid <= 0) return hipSuccess;
-  if constexpr (KV == kF32)
-    hipLaunchKernelGGL((prefill_kernel_wide<KV, D>), dim3((unsigned)grid), dim3(C::kThreads), 0, stream, a,
-                       a.block_tables, a.context_lens, a.k_scale, a.v_scale);
-  else
-    hipLaunchKernelGGL((prefill_kernel<KV, D>), dim3((unsigned)grid), dim3(C::kThreads), 0, stream, a,
-                       a.block_tables, a.context_lens, a.k_scale, a.v_scale);
-  return hipGetLastError();
+  if (a.prefix_mode) return launch_prefill_p<KV, D, true>(a, stream);
+  return launch_prefill_p<KV, D, false>(a, stream);
 }
 
 }  // namespace
 
 int64_t prefill_groups(const DecodeArgs& a) {
   const int cols = a.kv_dtype == kF32 ? PrefillCfg<kF32, 64>::kGroupCols : PrefillCfg<kBF16, 64>::kGroupCols;
-  return ((int64_t)a.cols + cols - 1) / cols * a.num_seqs * a.num_kv_heads;
+  return ((int64_t)a.cols + cols - 1) / cols * a.num_seqs * a.num_kv_heads * (a.prefix_mode ? a.pre_segments : 1);
+}
+
+int prefill_group_cols(int kv_dtype) {
+  return kv_dtype == kF32 ? PrefillCfg<kF32, 64>::kGroupCols : PrefillCfg<kBF16, 64>::kGroupCols;
 }
 
 hipError_t launch_prefill(const DecodeArgs& a, hipStream_t stream) {

@@ -67,6 +67,9 @@ def library() -> ctypes.CDLL:
             "pkv_paged_decode_ex": (ctypes.c_int, [D, P, P, P, P, I32, P, I32, I32, F, I32, P, P, SZ, P]),
             "pkv_paged_attention": (ctypes.c_int, [D, P, P, P, P, I32, P, I32, I32, I32, F, I32, P, P, SZ, P]),
             "pkv_attention_workspace_bytes": (SZ, [D, I32, I32, I32, I32]),
+            "pkv_shared_decode_workspace_bytes": (SZ, [D, I32, I32, I32, I32]),
+            "pkv_paged_decode_shared": (ctypes.c_int,
+                                        [D, P, P, P, P, I32, P, I32, I32, I32, F, I32, P, P, SZ, P]),
             "pkv_strerror": (ctypes.c_char_p, [ctypes.c_int]),
             "pkv_version": (ctypes.c_char_p, []),
         }
@@ -289,4 +292,44 @@ def paged_decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
                                    block_tables.shape[1], _ptr(context_lens), q.shape[0], mctx, float(scale),
                                    int(num_workers), _ptr(out), _ptr(workspace), wbytes, _stream(stream)),
            "pkv_paged_decode_ex")
+    return out
+
+
+def shared_decode_workspace_bytes(k_pool, v_pool, num_q_heads: int, num_seqs: int, max_context_len: int,
+                                  prefix_tokens: int, num_workers: int = 0, k_scale=None, v_scale=None) -> int:
+    desc = cache_desc(k_pool, v_pool, num_q_heads, k_scale, v_scale)
+    return int(library().pkv_shared_decode_workspace_bytes(ctypes.byref(desc), num_seqs, max_context_len,
+                                                           prefix_tokens, num_workers))
+
+
+def paged_decode_shared(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                        block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
+                        prefix_tokens: int, out: Optional[torch.Tensor] = None,
+                        k_scale: Optional[torch.Tensor] = None, v_scale: Optional[torch.Tensor] = None,
+                        max_context_len: Optional[int] = None, workspace: Optional[torch.Tensor] = None,
+                        num_workers: int = 0, stream=None) -> torch.Tensor:
+    """``paged_decode`` for a batch whose table rows all start with the same
+    ``prefix_tokens // block_size`` blocks (parallel sampling over one prompt).
+
+    The prefix's K/V are read once for the whole batch.  ``prefix_tokens`` is
+    a multiple of the block size and every sequence holds at least that many
+    tokens; ``workspace`` must hold ``shared_decode_workspace_bytes`` bytes.
+    """
+    desc, out = _decode_checks(q, k_pool, v_pool, block_tables, context_lens, k_scale, v_scale, out, False)
+    mctx = _max_ctx(block_tables, max_context_len, k_pool.shape[2])
+    lib = library()
+    B = q.shape[0]
+    need = lib.pkv_shared_decode_workspace_bytes(ctypes.byref(desc), B, mctx, int(prefix_tokens), int(num_workers))
+    if need == 0:
+        _check(-1, "pkv_shared_decode_workspace_bytes")
+    if workspace is None:
+        workspace = new_workspace(need, q.device)
+    wbytes = workspace.numel() * workspace.element_size()
+    if workspace.device.type != "cuda" or wbytes < need:
+        raise ValueError(f"workspace must be a device buffer of at least {need} bytes")
+    _check(lib.pkv_paged_decode_shared(ctypes.byref(desc), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
+                                       block_tables.shape[1], _ptr(context_lens), B, mctx, int(prefix_tokens),
+                                       float(scale), int(num_workers), _ptr(out), _ptr(workspace), wbytes,
+                                       _stream(stream)),
+           "pkv_paged_decode_shared")
     return out

@@ -28,7 +28,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for required in ("pkv_kv_append", "pkv_copy_blocks", "pkv_paged_decode", "pkv_paged_decode_ex",
-                     "pkv_decode_workspace_bytes", "pkv_decode_workers", "pkv_strerror"):
+                     "pkv_decode_workspace_bytes", "pkv_decode_workers", "pkv_strerror",
+                     "pkv_paged_decode_shared", "pkv_shared_decode_workspace_bytes"):
         assert required in names
 
 
@@ -150,6 +151,25 @@ def test_many_query_sizing():
     # the prefill route needs no workspace: with zero sequences nothing is launched
     assert lib.pkv_paged_attention(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 16, FAKE, 0, 64, 150, 0.1,
                                    64, FAKE, None, 0, None) == 0
+
+
+def test_shared_decode_sizing_and_checks():
+    """Shared-prefix decode: with no prefix the workspace is the decode's; the
+    prefix must be whole blocks, no longer than the length bound or the table
+    (checked before anything is launched); zero sequences launch nothing."""
+    lib = ops.library()
+    d = _desc()                                 # block size 16
+    assert lib.pkv_shared_decode_workspace_bytes(ctypes.byref(d), 4, 150, 0, 64) == \
+        lib.pkv_decode_workspace_bytes(ctypes.byref(d), 4, 150, 64)
+    assert lib.pkv_shared_decode_workspace_bytes(ctypes.byref(d), 4, 150, 24, 64) == 0   # not whole blocks
+    assert lib.pkv_shared_decode_workspace_bytes(ctypes.byref(d), 4, 150, 160, 64) == 0  # past the bound
+    args = lambda P, mctx, seqs=4, mb=16: (ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, mb, FAKE, seqs, mctx, P, 0.1,
+                                          64, FAKE, FAKE, 1 << 30, None)
+    assert lib.pkv_paged_decode_shared(*args(24, 150)) == EINVAL
+    assert lib.pkv_paged_decode_shared(*args(160, 150)) == EINVAL
+    assert lib.pkv_paged_decode_shared(*args(-16, 150)) == EINVAL
+    assert lib.pkv_paged_decode_shared(*args(64, 150, mb=3)) == EINVAL                 # 4 blocks, table of 3
+    assert lib.pkv_paged_decode_shared(*args(64, 150, seqs=0)) == 0
 
 
 def test_strerror_and_version():

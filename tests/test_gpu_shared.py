@@ -1,0 +1,128 @@
+"""GPU parity of pkv_paged_decode_shared (decode over a batch that shares
+its leading blocks: the prefix read once for all sequences) against the fp64
+oracle's decode over each sequence's own table, through the C ABI."""
+
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+from paged_kv_cache_23_amd import ops
+from paged_kv_cache_23_amd import workloads as W
+from paged_kv_cache_23_amd.workloads import build_workload
+from tests.gpu_util import Dev, assert_close, oracle_full, oracle_pairs, out_f64, pair_rows
+
+pytestmark = pytest.mark.gpu
+
+
+def _shared(dev: Dev, prefix_tokens: int, max_context_len=None, workers=0, workspace=None):
+    wl = dev.wl
+    mctx = int(wl.context_lens.max()) if max_context_len is None else max_context_len
+    return ops.paged_decode_shared(dev.q, dev.k_pool, dev.v_pool, dev.tables, dev.lens, wl.scale, prefix_tokens,
+                                   k_scale=dev.k_scale, v_scale=dev.v_scale, max_context_len=mctx,
+                                   num_workers=workers, workspace=workspace)
+
+
+def _tails(rng, B, hi):
+    """Tail lengths after the prefix: empty, 1, one chunk's edges, the rest random."""
+    fixed = [0, 1, 31, 32, 33, 100]
+    return [fixed[b] if b < len(fixed) else int(rng.integers(0, hi)) for b in range(B)]
+
+
+# (query heads per kv head) x batch = columns of the prefix pass: under one
+# MFMA tile (8), one workgroup, several with a ragged last one (528, 1200).
+@pytest.mark.parametrize("kv_dtype,D,G,B,P,bs", [
+    ("bf16", 128, 4, 37, 640, 16), ("bf16", 64, 16, 33, 1024, 16), ("bf16", 128, 1, 300, 4096, 256),
+    ("bf16", 128, 8, 1, 320, 16), ("fp8", 128, 8, 20, 2000, 16), ("fp8", 64, 2, 9, 512, 32),
+    ("f32", 64, 2, 9, 256, 16), ("f32", 128, 4, 70, 1024, 64),
+])
+def test_shared_parity(kv_dtype, D, G, B, P, bs):
+    rng = np.random.default_rng(B * 7 + P)
+    lens = [P + t for t in _tails(rng, B, 300)]
+    wl = build_workload("shared", lens, 2 * G, 2, D, kv_dtype, seed=B + P, shared_prefix=P, rng=rng,
+                        block_size=bs)
+    print(f"shared {kv_dtype} D={D} G={G} B={B} P={P} bs={bs}", flush=True)
+    out = _shared(Dev(wl), P)
+    assert out.shape == wl.q.shape
+    assert_close(out, oracle_full(wl), kv_dtype)
+
+
+def test_any_block_aligned_part_of_the_shared_prefix():
+    """prefix_tokens may name any whole-block part of what the rows share
+    (0 runs the plain decode); the result is the same decode every time."""
+    rng = np.random.default_rng(5)
+    P = 800
+    wl = build_workload("shared", [P + t for t in _tails(rng, 24, 200)], 16, 4, 128, "bf16", seed=5,
+                        shared_prefix=P, rng=rng)
+    dev = Dev(wl)
+    ref = oracle_full(wl)
+    for p in (0, 16, 400, 784, 800):
+        assert_close(_shared(dev, p), ref, "bf16")
+
+
+def test_every_tail_empty():
+    """Every sequence is exactly the prefix: the output comes from the prefix
+    pass alone."""
+    P = 1024
+    wl = build_workload("shared", [P] * 12, 32, 8, 128, "bf16", seed=6, shared_prefix=P)
+    assert_close(_shared(Dev(wl), P), oracle_full(wl), "bf16")
+
+
+def test_worker_counts_and_a_reused_workspace():
+    rng = np.random.default_rng(7)
+    P = 512
+    wl = build_workload("shared", [P + t for t in _tails(rng, 40, 600)], 32, 8, 128, "bf16", seed=7,
+                        shared_prefix=P, rng=rng)
+    dev = Dev(wl)
+    ref = oracle_full(wl)
+    mctx = int(wl.context_lens.max())
+    for w in (4, 64, 1024):
+        need = ops.shared_decode_workspace_bytes(dev.k_pool, dev.v_pool, 32, 40, mctx, P, w)
+        ws = torch.full((need,), 0xFF, dtype=torch.uint8, device=dev.q.device)   # stale bytes: NaN floats
+        for _ in range(2):
+            assert_close(_shared(dev, P, workers=w, workspace=ws), ref, "bf16")
+
+
+def test_lengths_clamped_by_max_context_len():
+    rng = np.random.default_rng(8)
+    P = 320
+    wl = build_workload("shared", [P + t for t in _tails(rng, 16, 400)], 32, 8, 128, "bf16", seed=8,
+                        shared_prefix=P, rng=rng)
+    bound = P + 40
+    out = _shared(Dev(wl), P, max_context_len=bound)
+    clamped = dataclasses.replace(wl, context_lens=wl.context_lens.clamp(max=bound))
+    assert_close(out, oracle_full(clamped), "bf16")
+
+
+def test_argument_errors():
+    P = 320
+    wl = build_workload("shared", [P + 5, P + 60], 8, 2, 128, "bf16", seed=9, shared_prefix=P)
+    dev = Dev(wl)
+    with pytest.raises(RuntimeError, match="invalid"):
+        _shared(dev, P - 8)                               # not a whole number of blocks
+    with pytest.raises(RuntimeError, match="invalid"):
+        _shared(dev, P, max_context_len=P - 16)           # longer than the bound on the lengths
+    with pytest.raises(RuntimeError, match="invalid"):
+        _shared(dev, 16 * (wl.block_tables.shape[1] + 1), max_context_len=10 ** 6)   # past the table
+
+
+# ---------------------------------------------------------------------------
+# Full-size batches, in the launch configuration the benchmark times
+# ---------------------------------------------------------------------------
+def test_shared_prefix_256_sampled_pairs():
+    """256 sequences over one 4096-token prefix (+ 64..512-token tails)."""
+    wl = W.shared_prefix_256()
+    out = _shared(Dev(wl), 4096)
+    rng = np.random.default_rng(1)
+    pairs = [(int(b), int(g)) for b, g in zip(rng.integers(0, 256, 24), rng.integers(0, 8, 24))]
+    assert_close(pair_rows(out, pairs, 4), oracle_pairs(wl, pairs), "bf16")
+    assert np.all(np.isfinite(out_f64(out)))
+
+
+def test_best_of_8_all_outputs():
+    """Best-of-8 over a 2,000-token prompt (125 shared blocks)."""
+    wl = W.best_of_8()
+    assert_close(_shared(Dev(wl), 2000), oracle_full(wl), "bf16")
