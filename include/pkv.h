@@ -211,6 +211,13 @@ int pkv_paged_decode_ex(const pkv_cache_desc* desc, const void* q, const void* k
  * per (sequence, head) with section 3's rescale and writes out.
  *   workspace  pkv_shared_decode_workspace_bytes(...) bytes (same num_workers),
  *              16-byte aligned scratch; calls sharing it must be ordered. */
+/* Whether pkv_paged_decode_shared is expected to beat pkv_paged_decode_ex
+ * for this batch: 1 when the prefix bytes the plain decode would read again,
+ * (num_seqs - 1) * prefix_tokens * 2 * num_kv_heads * head_dim * element
+ * size, reach 192 MiB (the crossover measured on MI355X), else 0; a negative
+ * PKV_E* code on bad arguments.  Host arithmetic only. */
+int32_t pkv_shared_prefix_pays(const pkv_cache_desc* desc, int32_t num_seqs, int32_t prefix_tokens);
+
 size_t pkv_shared_decode_workspace_bytes(const pkv_cache_desc* desc, int32_t num_seqs,
                                          int32_t max_context_len, int32_t prefix_tokens,
                                          int32_t num_workers);

@@ -68,6 +68,7 @@ def library() -> ctypes.CDLL:
             "pkv_paged_attention": (ctypes.c_int, [D, P, P, P, P, I32, P, I32, I32, I32, F, I32, P, P, SZ, P]),
             "pkv_attention_workspace_bytes": (SZ, [D, I32, I32, I32, I32]),
             "pkv_shared_decode_workspace_bytes": (SZ, [D, I32, I32, I32, I32]),
+            "pkv_shared_prefix_pays": (I32, [D, I32, I32]),
             "pkv_paged_decode_shared": (ctypes.c_int,
                                         [D, P, P, P, P, I32, P, I32, I32, I32, F, I32, P, P, SZ, P]),
             "pkv_strerror": (ctypes.c_char_p, [ctypes.c_int]),
@@ -307,18 +308,27 @@ def paged_decode_shared(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Ten
                         prefix_tokens: int, out: Optional[torch.Tensor] = None,
                         k_scale: Optional[torch.Tensor] = None, v_scale: Optional[torch.Tensor] = None,
                         max_context_len: Optional[int] = None, workspace: Optional[torch.Tensor] = None,
-                        num_workers: int = 0, stream=None) -> torch.Tensor:
+                        num_workers: int = 0, stream=None, always: bool = True) -> torch.Tensor:
     """``paged_decode`` for a batch whose table rows all start with the same
     ``prefix_tokens // block_size`` blocks (parallel sampling over one prompt).
 
     The prefix's K/V are read once for the whole batch.  ``prefix_tokens`` is
     a multiple of the block size and every sequence holds at least that many
     tokens; ``workspace`` must hold ``shared_decode_workspace_bytes`` bytes.
+    ``always=False`` runs the plain decode (cached loads) instead when
+    ``shared_prefix_pays`` says the batch is too small to gain.
     """
     desc, out = _decode_checks(q, k_pool, v_pool, block_tables, context_lens, k_scale, v_scale, out, False)
     mctx = _max_ctx(block_tables, max_context_len, k_pool.shape[2])
     lib = library()
     B = q.shape[0]
+    if not always:
+        pays = lib.pkv_shared_prefix_pays(ctypes.byref(desc), B, int(prefix_tokens))
+        _check(min(pays, 0), "pkv_shared_prefix_pays")
+        if not pays:
+            return paged_decode(q, k_pool, v_pool, block_tables, context_lens, scale, out=out, k_scale=k_scale,
+                                v_scale=v_scale, max_context_len=max_context_len, num_workers=num_workers,
+                                stream=stream, reread=True)
     need = lib.pkv_shared_decode_workspace_bytes(ctypes.byref(desc), B, mctx, int(prefix_tokens), int(num_workers))
     if need == 0:
         _check(-1, "pkv_shared_decode_workspace_bytes")
@@ -333,3 +343,12 @@ def paged_decode_shared(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Ten
                                        _stream(stream)),
            "pkv_paged_decode_shared")
     return out
+
+
+def shared_prefix_pays(k_pool, v_pool, num_q_heads: int, num_seqs: int, prefix_tokens: int,
+                       k_scale=None, v_scale=None) -> bool:
+    """Whether the shared-prefix decode is expected to beat the plain one."""
+    desc = cache_desc(k_pool, v_pool, num_q_heads, k_scale, v_scale)
+    res = library().pkv_shared_prefix_pays(ctypes.byref(desc), num_seqs, prefix_tokens)
+    _check(min(res, 0), "pkv_shared_prefix_pays")
+    return bool(res)

@@ -172,6 +172,21 @@ def test_shared_decode_sizing_and_checks():
     assert lib.pkv_paged_decode_shared(*args(64, 150, seqs=0)) == 0
 
 
+def test_shared_prefix_policy():
+    """The cascade is chosen from 192 MiB of avoided prefix re-reads: with 8 kv
+    heads, head_dim 128 and bf16 (4 KiB per token), a 2,000-token prefix pays
+    from 26 sequences, a 4,096-token one from 13; fp8 needs about twice as many."""
+    lib = ops.library()
+    d = _desc(num_kv_heads=8, num_q_heads=32)
+    pays = lambda B, P, dd=d: lib.pkv_shared_prefix_pays(ctypes.byref(dd), B, P)
+    assert [pays(B, 2000) for B in (8, 16, 25, 26, 32, 256)] == [0, 0, 0, 1, 1, 1]
+    assert [pays(B, 4096) for B in (8, 12, 13, 256)] == [0, 0, 1, 1]
+    assert pays(1, 10 ** 6) == 0 and pays(256, 0) == 0
+    fp8 = _desc(num_kv_heads=8, num_q_heads=32, kv_dtype=2, q_dtype=1, k_scale=FAKE, v_scale=FAKE)
+    assert pays(26, 2000, fp8) == 0 and pays(50, 2000, fp8) == 0 and pays(51, 2000, fp8) == 1
+    assert pays(-1, 16) == EINVAL
+
+
 def test_strerror_and_version():
     lib = ops.library()
     assert lib.pkv_strerror(0) == b"ok"

@@ -1,8 +1,8 @@
 """Invariants of the GPU decode that need no tolerance: bit-identity under
 block-id permutation, prefix sharing and identity-vs-shuffled tables (the
 arithmetic order depends on logical positions only), normalisation (V = 1
-gives exactly 1), poison in masked slots and unused table entries, and the
-two-kernel form equal to the fused call."""
+gives exactly 1), poison in masked slots and unused table entries,
+determinism, and workspace reuse (stale bytes, calls of other shapes)."""
 
 from __future__ import annotations
 
@@ -153,8 +153,8 @@ def test_repeated_calls_are_deterministic(workers):
 
 
 def test_reused_workspace_stays_valid():
-    """One workspace across many calls and shapes: every call leaves its
-    counters at zero, so later calls merge correctly."""
+    """One workspace across many calls and shapes: every call writes the pair
+    records and partials it reads, so what earlier calls left changes nothing."""
     big = build_workload("ws-a", LENS, 8, 2, 128, "bf16", seed=5)
     small = build_workload("ws-b", [40, 3000, 7], 8, 2, 128, "bf16", seed=6)
     dev_big, dev_small = Dev(big), Dev(small)
@@ -170,6 +170,18 @@ def test_reused_workspace_stays_valid():
         assert np.array_equal(_bits(out), first)
         assert_close(out, ref_big, "bf16")
         assert_close(dev_small.decode(workers=8, workspace=ws), ref_small, "bf16")
+
+
+def test_stale_bytes_in_the_workspace():
+    """The workspace needs no initialisation: partial states and pair records
+    full of NaN bytes left by something else change no bit of the result."""
+    wl = _wl("bf16")
+    dev = Dev(wl)
+    base = _bits(dev.decode(workers=8))
+    nbytes = ops.decode_workspace_bytes(dev.k_pool, dev.v_pool, 8, len(LENS), max(LENS), 8)
+    for _ in range(2):
+        ws = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device=dev.q.device)
+        assert np.array_equal(_bits(dev.decode(workers=8, workspace=ws)), base)
 
 
 @pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])

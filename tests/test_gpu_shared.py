@@ -79,11 +79,11 @@ def test_worker_counts_and_a_reused_workspace():
     dev = Dev(wl)
     ref = oracle_full(wl)
     mctx = int(wl.context_lens.max())
-    for w in (4, 64, 1024):
-        need = ops.shared_decode_workspace_bytes(dev.k_pool, dev.v_pool, 32, 40, mctx, P, w)
-        ws = torch.full((need,), 0xFF, dtype=torch.uint8, device=dev.q.device)   # stale bytes: NaN floats
-        for _ in range(2):
-            assert_close(_shared(dev, P, workers=w, workspace=ws), ref, "bf16")
+    need = max(ops.shared_decode_workspace_bytes(dev.k_pool, dev.v_pool, 32, 40, mctx, P, w) for w in (4, 64, 1024))
+    ws = ops.new_workspace(need, dev.q.device)
+    for w in (4, 64, 1024, 4):   # partials of the earlier calls stay behind
+        for p in (P, 0):         # the plain decode (no prefix) shares the workspace too
+            assert_close(_shared(dev, p, workers=w, workspace=ws), ref, "bf16")
 
 
 def test_lengths_clamped_by_max_context_len():
@@ -126,3 +126,18 @@ def test_best_of_8_all_outputs():
     """Best-of-8 over a 2,000-token prompt (125 shared blocks)."""
     wl = W.best_of_8()
     assert_close(_shared(Dev(wl), 2000), oracle_full(wl), "bf16")
+
+
+def test_policy_picks_either_path_with_the_same_result():
+    """always=False consults the crossover: a best-of-8 batch runs the plain
+    decode, 64 sequences over a 4,096-token prefix the cascade; both agree
+    with the oracle."""
+    for B, P in ((8, 2000), (64, 4096)):
+        rng = np.random.default_rng(B)
+        wl = build_workload("shared", [P + int(t) for t in rng.integers(1, 201, size=B)], 32, 8, 128, "bf16",
+                            seed=B, shared_prefix=P, rng=rng)
+        dev = Dev(wl)
+        assert ops.shared_prefix_pays(dev.k_pool, dev.v_pool, 32, B, P) == (B == 64)
+        out = ops.paged_decode_shared(dev.q, dev.k_pool, dev.v_pool, dev.tables, dev.lens, wl.scale, P,
+                                      max_context_len=int(wl.context_lens.max()), always=False)
+        assert_close(out, oracle_full(wl), "bf16")
