@@ -430,6 +430,7 @@ def run_bench(args) -> dict:
             "traffic": traffic,
             "algorithmic_bytes_per_launch": algo,
             "mean_call_us": round(float(part_ms.mean()) * 1e3, 2),
+            "call_us_p10_p50_p90": [round(float(np.percentile(part_ms, q)) * 1e3, 2) for q in (10, 50, 90)],
         },
     }
     if not args.no_cpu_baseline:
