@@ -410,6 +410,11 @@ __device__ __forceinline__ void prefill_body(const DecodeArgs& a, const int32_t*
   auto compute = [&](int t0, int nbuf, bool more, auto mask_tag) {
     constexpr bool kMask = decltype(mask_tag)::value;
     f32x4 sx[kT], sy[kT];
+    // Wave priority: raised from the score MFMAs through the softmax and
+    // dropped for the P.V MFMAs, so that when both waves of a SIMD are ready
+    // the one in the earlier phase issues first and the two drift apart,
+    // overlapping one's vector work with the other's MFMAs (+1.3% on MI355X).
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int t = 0; t < kT; ++t) T::scores(kf, qop[t], sx[t], sy[t]);
     if (more) lds_k<KV, D>(kf, lds_kt[nbuf], r, j);
@@ -470,9 +475,11 @@ __device__ __forceinline__ void prefill_body(const DecodeArgs& a, const int32_t*
         bf16x8 pb;
 #pragma unroll
         for (int k = 0; k < 8; ++k) pb[k] = (__bf16)pk[k];
+        __builtin_amdgcn_s_setprio(0);
         pv_bf16<KV, D>(acc[t], vf, pb);
         pv_ones(lsum[t], pb);
       } else {
+        __builtin_amdgcn_s_setprio(0);
         l_run[t] += T::pv(acc[t], vf, pk);
       }
     }
