@@ -542,19 +542,21 @@ def cow_bench(args) -> dict:
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0
+MFMA_F32_PEAK_TFLOPS = 157.3
 
 
 class PrefillRunner:
     """The chunk steps of one prompt's chunked prefill, pre-marshalled."""
 
-    def __init__(self, block_size: int = 16):
+    def __init__(self, block_size: int = 16, kv_dtype: str = "bf16"):
         import torch
         from paged_kv_cache_23_amd import ops
         from paged_kv_cache_23_amd.workloads import prefill_chunks
 
         self.torch, self.ops = torch, ops
         dev = torch.device("cuda:0")
-        self.steps = prefill_chunks(block_size=block_size)
+        self.kv_dtype = kv_dtype
+        self.steps = prefill_chunks(block_size=block_size, kv_dtype=kv_dtype)
         wl = self.steps[0].wl
         self.wl = wl
         self.k_pool, self.v_pool = wl.k_pool.to(dev), wl.v_pool.to(dev)
@@ -564,7 +566,9 @@ class PrefillRunner:
         self.lens = [s.wl.context_lens.to(dev) for s in self.steps]
         self.n = [int(s.wl.context_lens[0]) for s in self.steps]
         self.flops = [s.flops() for s in self.steps]
-        self.desc = ops.cache_desc(self.k_pool, self.v_pool, wl.num_q_heads)
+        self.k_scale = None if wl.k_scale is None else wl.k_scale.to(dev)
+        self.v_scale = None if wl.v_scale is None else wl.v_scale.to(dev)
+        self.desc = ops.cache_desc(self.k_pool, self.v_pool, wl.num_q_heads, self.k_scale, self.v_scale)
         self.lib = ops.library()
         self.ws = ops.new_workspace(256, dev)
 
@@ -599,9 +603,14 @@ def prefill_parity(runner, outs, rows: int = 4) -> float:
         for i in np.linspace(0, L - 1, rows).astype(int):
             lens = np.array([runner.n[k] - L + 1 + int(i)], dtype=np.int32)
             ref = oracle.oracle_decode(storage_numpy(s.q[:, i]), wl.q_dtype, kp, vp, wl.kv_dtype,
-                                       wl.block_tables.numpy(), lens, wl.scale)
+                                       wl.block_tables.numpy(), lens, wl.scale, *_scales(wl))
             worst = max(worst, float(np.max(np.abs(got[:, i] - ref))))
     return worst
+
+
+def _scales(wl):
+    """The fp8 pools' per-head scales as host arrays (None, None otherwise)."""
+    return (None if wl.k_scale is None else wl.k_scale.numpy(), None if wl.v_scale is None else wl.v_scale.numpy())
 
 
 def prefill_cpu_baseline(runner, min_seconds: float):
@@ -623,7 +632,7 @@ def prefill_cpu_baseline(runner, min_seconds: float):
             rows = min(8, L - done)
             lens = [n - L + done + rows]
             oracle.oracle_attention_multi(q[:, done:done + rows], wl.q_dtype, kp, vp, wl.kv_dtype,
-                                          wl.block_tables.numpy(), lens, wl.scale)
+                                          wl.block_tables.numpy(), lens, wl.scale, *_scales(wl))
             flops += sum(4 * wl.num_q_heads * wl.head_dim * (n - L + 1 + i) for i in range(done, done + rows))
             done += rows
     sec = time.perf_counter() - t0
@@ -643,9 +652,14 @@ def prefill_bench(args) -> dict:
     import numpy as np
     import torch
 
-    runner = PrefillRunner(args.block_size)
+    runner = PrefillRunner(args.block_size, args.kv_dtype)
     wl = runner.wl
     flops = sum(runner.flops)
+    kv = args.kv_dtype
+    # fp8 codes are widened to bf16 for the bf16 MFMA; a float32 cache runs
+    # the float32 MFMA (dense peak 157.3 TFLOP/s)
+    peak = MFMA_F32_PEAK_TFLOPS if kv == "f32" else MFMA_BF16_PEAK_TFLOPS
+    mfma = "f32" if kv == "f32" else "bf16"
     log(f"prefill {wl.name}: chunks {[int(q.shape[1]) for q in runner.q]} over n = {runner.n}, "
         f"Hq={wl.num_q_heads} Hkv={wl.num_kv_heads} D={wl.head_dim}, {flops / 1e9:.1f} GFLOP per step")
     s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
@@ -680,7 +694,7 @@ def prefill_bench(args) -> dict:
     log(f"{K} steps: {ms_per_step * 1e3:.1f} us/step, {tflops:.1f} TFLOP/s; per chunk call (us) "
         f"{[round(float(m) * 1e3, 1) for m in mean_call]}, TFLOP/s {per_chunk}")
     result = {
-        "metric": "chunked-prefill paged attention TFLOP/s (bf16 MFMA)",
+        "metric": f"chunked-prefill paged attention TFLOP/s ({mfma} MFMA)",
         "value": round(tflops, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -690,10 +704,10 @@ def prefill_bench(args) -> dict:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": {"f32": "f32", "bf16": "bf16", "fp8": "fp8-e4m3 kv / bf16 q"}[kv],
         "data": "synthetic",
         "config": {
-            "workload": f"{wl.name}: one layer (64 q / 8 kv heads, head_dim 128, bf16, {args.block_size}-token "
+            "workload": f"{wl.name}: one layer (64 q / 8 kv heads, head_dim 128, {kv} cache, {args.block_size}-token "
                         f"blocks, shuffled pool) prefilling a 10,000-token prompt in chunks of "
                         f"{[int(q.shape[1]) for q in runner.q]}, each attending causally to all chunks before it",
             "flops_per_step": flops,
@@ -704,13 +718,14 @@ def prefill_bench(args) -> dict:
         "per_chunk_call_us": [round(float(m) * 1e3, 2) for m in mean_call],
         "per_chunk_tflops": per_chunk,
         "roofline": {
-            "kernel": "prefill_kernel<bf16, 128>",
+            "kernel": f"prefill_kernel<{kv}, 128>",
             "bound": "mfma",
             "achieved": round(kern_tflops, 2),
-            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "peak": peak,
             "unit": "TFLOP/s",
-            "frac": round(kern_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-            "traffic": committed_traffic(wl.name, "prefill_kernel", PREFILL_SOURCES),
+            "frac": round(kern_tflops / peak, 4),
+            # the committed counters were taken on the bf16 cache
+            "traffic": committed_traffic(wl.name, "prefill_kernel", PREFILL_SOURCES) if kv == "bf16" else None,
             "traffic_unit": "HBM bytes per step (five calls)",
             "algorithmic_flops_per_step": flops,
             "mean_step_kernel_us": round(float(mean_call.sum()) * 1e3, 2),
@@ -730,7 +745,7 @@ def prefill_bench(args) -> dict:
 def prefill_profile(args) -> None:
     import torch
 
-    runner = PrefillRunner(args.block_size)
+    runner = PrefillRunner(args.block_size, args.kv_dtype)
     s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     for _ in range(args.warmup + args.steps):
         runner.step(s)
@@ -758,6 +773,8 @@ def main() -> int:
                    help="PKV_KV_REREAD hint: auto = on when the tables share blocks")
     p.add_argument("--shared", action="store_true",
                    help="decode through pkv_paged_decode_shared: the tables' common leading blocks read once")
+    p.add_argument("--kv-dtype", choices=["bf16", "fp8", "f32"], default="bf16",
+                   help="cache dtype of the --prefill workload")
     p.add_argument("--prefill", action="store_true",
                    help="time chunked prefill (a 10,000-token prompt in 2048-token chunks) instead")
     p.add_argument("--q-len", type=int, default=1,

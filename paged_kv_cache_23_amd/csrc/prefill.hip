@@ -25,14 +25,16 @@
 // workgroup.  The waves stage each chunk's K (token-major) and V
 // (dimension-major) from the pool into LDS together (three groups of two
 // chunk buffers, one barrier per group) and each reads its operands from
-// there.  Workgroups are
+// there; an fp8 cache is widened to bf16 (exactly) as it is staged, so the
+// LDS tiles and the operand reads are the bf16 ones.  Workgroups are
 // issued largest first (the last column tiles see the most keys), and
 // workgroups of the same pair are spaced by the pair count, so with a pair
 // count divisible by 8 they land on the same XCD and share its L2.
 //
 // Tile math: the transposed-score layout of the decode kernel (tile_math.h):
 // per chunk and column tile, 2 * D/32 score MFMAs, D/16 P.V MFMAs and one
-// row-sum MFMA (bf16), all operands read from LDS with 16-byte reads.
+// row-sum MFMA (bf16 and fp8 caches), all operands read from LDS with
+// 16-byte reads.
 
 #include "pkv_internal.h"
 #include "tile_math.h"
@@ -64,11 +66,16 @@ __device__ __forceinline__ int k_row(int t) { return t ^ ((t >> 1) & 12); }
 
 template <int KV, int D>
 struct PrefillCfg {
-  using Tile = typename TileOf<KV, D>::type;
-  using Elem = typename Tile::Elem;
+  // fp8 codes are widened to bf16 once, as a chunk is staged into LDS (by
+  // the staging threads, not by every wave that reads it), so the LDS tiles
+  // and the operand reads are the bf16 ones for both cache dtypes.
+  static constexpr int kLds = KV == kFP8 ? kBF16 : KV;           // dtype of the LDS tiles
+  using Tile = typename TileOf<kLds, D>::type;                    // operand tiles read from LDS
+  using Elem = typename Tile::Elem;                               // LDS element
   using Out = typename TileOf<KV, D>::Out;
-  static constexpr int kEs = (int)sizeof(Elem);
-  static constexpr int kPerPiece = 16 / kEs;                     // elements per 16-byte piece
+  static constexpr int kEs = (int)sizeof(Elem);                  // LDS element bytes
+  static constexpr int kPs = KV == kFP8 ? 1 : kEs;               // pool element bytes
+  static constexpr int kPerPiece = 16 / kPs;                     // pool elements per 16-byte piece
   // Eight waves of two column tiles (two waves per SIMD, at most 256
   // registers each) for bf16 / fp8; the float32 tiles need more registers
   // and run four waves, one per SIMD.
@@ -77,7 +84,7 @@ struct PrefillCfg {
   static constexpr int kWaveCols = 16 * kT;
   static constexpr int kGroupCols = kWaves * kWaveCols;          // columns per workgroup
   static constexpr int kSK = D + 32 / kEs;                       // K tile row stride: +32 bytes
-  static constexpr int kSV = kChunkTokens + (KV == kFP8 ? 64 : 32) / kEs;   // V row: 96 / 96 / 160 bytes
+  static constexpr int kSV = kChunkTokens + 32 / kEs;          // V row: 96 bytes (bf16 tiles), 160 (float32)
   static constexpr int kKRowPieces = D / kPerPiece;
   static constexpr int kVRowPieces = kChunkTokens / kPerPiece;
   static constexpr int kKPieces = kChunkTokens * kKRowPieces;
@@ -119,12 +126,6 @@ __device__ __forceinline__ void lds_k(typename PrefillCfg<KV, D>::Tile::K& k,
       k.x[s] = *reinterpret_cast<const u32x4*>(rx + 32 * s + 8 * j);
       k.y[s] = *reinterpret_cast<const u32x4*>(ry + 32 * s + 8 * j);
     }
-  } else if constexpr (KV == kFP8) {
-#pragma unroll
-    for (int s = 0; s < D / 64; ++s) {
-      k.x[s] = *reinterpret_cast<const u32x4*>(rx + j * (D / 4) + 16 * s);
-      k.y[s] = *reinterpret_cast<const u32x4*>(ry + j * (D / 4) + 16 * s);
-    }
   } else {
 #pragma unroll
     for (int a = 0; a < D / 16; ++a) {
@@ -145,8 +146,6 @@ __device__ __forceinline__ void lds_v(typename PrefillCfg<KV, D>::Tile::V& v,
     const typename C::Elem* p = base + 16 * u * C::kSV;
     if constexpr (KV == kBF16) {
       v.t[u] = *reinterpret_cast<const u32x4*>(p);
-    } else if constexpr (KV == kFP8) {
-      v.t[u] = *reinterpret_cast<const u32x2*>(p);
     } else {
       v.t[u][0] = *reinterpret_cast<const f32x4*>(p);
       v.t[u][1] = *reinterpret_cast<const f32x4*>(p + 4);
@@ -180,10 +179,7 @@ template <int KV, int D>
 __device__ __forceinline__ void pv_bf16(f32x4* acc, const typename PrefillCfg<KV, D>::Tile::V& v, const bf16x8& pb) {
 #pragma unroll
   for (int u = 0; u < D / 16; ++u) {
-    u32x4 op;
-    if constexpr (KV == kFP8) op = fp8x8_to_bf16x8(v.t[u][0], v.t[u][1]);
-    else op = v.t[u];
-    acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, op), pb, acc[u], 0, 0, 0);
+    acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v.t[u]), pb, acc[u], 0, 0, 0);
   }
 }
 
@@ -310,7 +306,7 @@ __device__ __forceinline__ void prefill_body(const DecodeArgs& a, const int32_t*
   const char* vpool = static_cast<const char*>(a.v_pool);
   constexpr int KR = C::kKRowPieces;
   constexpr int VH = C::kVRowPieces / 2;
-  constexpr int kEs = C::kEs;
+  constexpr int kPs = C::kPs;   // pool element bytes
   uint32_t k_src[C::kKPerThread], v_src[C::kVPerThread];   // byte offsets inside a half
   int k_dst[C::kKPerThread], v_dst[C::kVPerThread];        // LDS element offsets
   int k_half[C::kKPerThread], v_half[C::kVPerThread], v_tok[C::kVPerThread];
@@ -319,7 +315,7 @@ __device__ __forceinline__ void prefill_body(const DecodeArgs& a, const int32_t*
     const int p = tid + C::kThreads * i;
     const int u = (p / KR) % 16, e = p % KR;
     k_half[i] = uni(p / (16 * KR));
-    k_src[i] = (uint32_t)((u * D + e * C::kPerPiece) * kEs);
+    k_src[i] = (uint32_t)((u * D + e * C::kPerPiece) * kPs);
     k_dst[i] = k_row(16 * k_half[i] + u) * C::kSK + e * C::kPerPiece;
   }
 #pragma unroll
@@ -328,7 +324,7 @@ __device__ __forceinline__ void prefill_body(const DecodeArgs& a, const int32_t*
     const int d = (p / VH) % D, q = p % VH;
     v_half[i] = uni(p / (D * VH));
     v_tok[i] = 16 * v_half[i] + q * C::kPerPiece;
-    v_src[i] = (uint32_t)((d * bs + q * C::kPerPiece) * kEs);
+    v_src[i] = (uint32_t)((d * bs + q * C::kPerPiece) * kPs);
     v_dst[i] = d * C::kSV + v_tok[i];
   }
   struct Stage {
@@ -345,10 +341,10 @@ __device__ __forceinline__ void prefill_body(const DecodeArgs& a, const int32_t*
     const int off0 = t0 & (bs - 1);
     const int off1 = (t0 + 16) & (bs - 1);
     const size_t tile0 = ((size_t)i0 * Hkv + g) * bs * D, tile1 = ((size_t)i1 * Hkv + g) * bs * D;
-    const char* kb0 = kpool + (tile0 + (size_t)off0 * D) * kEs;
-    const char* kb1 = kpool + (tile1 + (size_t)off1 * D) * kEs;
-    const char* vb0 = vpool + (tile0 + off0) * kEs;
-    const char* vb1 = vpool + (tile1 + off1) * kEs;
+    const char* kb0 = kpool + (tile0 + (size_t)off0 * D) * kPs;
+    const char* kb1 = kpool + (tile1 + (size_t)off1 * D) * kPs;
+    const char* vb0 = vpool + (tile0 + off0) * kPs;
+    const char* vb1 = vpool + (tile1 + off1) * kPs;
 #pragma unroll
     for (int i = 0; i < C::kKPerThread; ++i)
       if (C::kKPieces % C::kThreads == 0 || tid + C::kThreads * i < C::kKPieces)
@@ -364,19 +360,27 @@ __device__ __forceinline__ void prefill_body(const DecodeArgs& a, const int32_t*
 #pragma unroll
       for (int i = 0; i < C::kVPerThread; ++i) {
         const int valid = n - (t0 + v_tok[i]);
-        if (valid < C::kPerPiece) st.v[i] = keep_bytes(st.v[i], max(valid, 0) * kEs);
+        if (valid < C::kPerPiece) st.v[i] = keep_bytes(st.v[i], max(valid, 0) * kPs);
       }
+    }
+  };
+  // A piece of 16 fp8 codes is widened (exactly) to 16 bf16 values: two
+  // 16-byte LDS stores.
+  auto put = [&](Elem* dst, const u32x4& w) {
+    if constexpr (KV == kFP8) {
+      *reinterpret_cast<u32x4*>(dst) = fp8x8_to_bf16x8(w[0], w[1]);
+      *reinterpret_cast<u32x4*>(dst + 8) = fp8x8_to_bf16x8(w[2], w[3]);
+    } else {
+      *reinterpret_cast<u32x4*>(dst) = w;
     }
   };
   auto stage_store = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < C::kKPerThread; ++i)
-      if (C::kKPieces % C::kThreads == 0 || tid + C::kThreads * i < C::kKPieces)
-        *reinterpret_cast<u32x4*>(&lds_kt[buf][k_dst[i]]) = st.k[i];
+      if (C::kKPieces % C::kThreads == 0 || tid + C::kThreads * i < C::kKPieces) put(&lds_kt[buf][k_dst[i]], st.k[i]);
 #pragma unroll
     for (int i = 0; i < C::kVPerThread; ++i)
-      if (C::kVPieces % C::kThreads == 0 || tid + C::kThreads * i < C::kVPieces)
-        *reinterpret_cast<u32x4*>(&lds_vt[buf][v_dst[i]]) = st.v[i];
+      if (C::kVPieces % C::kThreads == 0 || tid + C::kThreads * i < C::kVPieces) put(&lds_vt[buf][v_dst[i]], st.v[i]);
   };
 
   // Per column tile: accumulator, the reference max m_ref of its
@@ -417,7 +421,7 @@ __device__ __forceinline__ void prefill_body(const DecodeArgs& a, const int32_t*
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int t = 0; t < kT; ++t) T::scores(kf, qop[t], sx[t], sy[t]);
-    if (more) lds_k<KV, D>(kf, lds_kt[nbuf], r, j);
+    if (more) lds_k<C::kLds, D>(kf, lds_kt[nbuf], r, j);
     float s[kT][8];   // raw scores q . k; scaled inside the exponent
     int nvalid[kT];
     bool raise[kT];
@@ -476,14 +480,14 @@ __device__ __forceinline__ void prefill_body(const DecodeArgs& a, const int32_t*
 #pragma unroll
         for (int k = 0; k < 8; ++k) pb[k] = (__bf16)pk[k];
         __builtin_amdgcn_s_setprio(0);
-        pv_bf16<KV, D>(acc[t], vf, pb);
+        pv_bf16<C::kLds, D>(acc[t], vf, pb);
         pv_ones(lsum[t], pb);
       } else {
         __builtin_amdgcn_s_setprio(0);
         l_run[t] += T::pv(acc[t], vf, pk);
       }
     }
-    if (more) lds_v<KV, D>(vf, lds_vt[nbuf], r, j);
+    if (more) lds_v<C::kLds, D>(vf, lds_vt[nbuf], r, j);
   };
 
   // Pipeline over groups of kPair chunks (one barrier per group).  Chunk c
@@ -504,8 +508,8 @@ __device__ __forceinline__ void prefill_body(const DecodeArgs& a, const int32_t*
   __builtin_amdgcn_s_waitcnt(kVmcntZero);
   __syncthreads();
   if (nck > 0 && kend_w > 0) {
-    lds_k<KV, D>(kf, lds_kt[0], r, j);
-    lds_v<KV, D>(vf, lds_vt[0], r, j);
+    lds_k<C::kLds, D>(kf, lds_kt[0], r, j);
+    lds_v<C::kLds, D>(vf, lds_vt[0], r, j);
   }
   for (int c = 0; c < nck; c += kP) {
 #pragma unroll
