@@ -49,6 +49,7 @@ def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+COPY_SOURCES = ["paged_kv_cache_23_amd/csrc/copy.hip", "paged_kv_cache_23_amd/csrc/pkv_internal.h"]
 PREFILL_SOURCES = ["paged_kv_cache_23_amd/csrc/prefill.hip", "paged_kv_cache_23_amd/csrc/tile_math.h",
                    "paged_kv_cache_23_amd/csrc/pkv_internal.h"]
 
@@ -527,9 +528,20 @@ def cow_bench(args) -> dict:
     step_us = timed(step, 200)
     log(f"copy 8 pairs: {small_us:.2f} us; copy 4096 pairs: {big_us:.1f} us "
         f"({big_bytes / big_us / 1e3:.0f} GB/s); sampling step: {step_us:.1f} us")
-    return {
-        "metric": "copy-on-write block copy (pkv_copy_blocks) and parallel-sampling step",
-        "unit": "us",
+    big_gbs = big_bytes / big_us / 1e3
+    result = {
+        "metric": "copy-on-write block copy GB/s (pkv_copy_blocks, read + write) and parallel-sampling step",
+        "value": round(big_gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": 50,
+        "warmup": 10,
+        "ms_per_step": round(big_us / 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
         "copy_8_pairs_us": round(small_us, 2),
         "copy_8_pairs_bytes": small_bytes,
         "copy_4096_pairs_us": round(big_us, 2),
@@ -537,7 +549,58 @@ def cow_bench(args) -> dict:
         "copy_4096_pairs_gbs": round(big_bytes / big_us / 1e3, 1),
         "copy_4096_pairs_hbm_frac": round(big_bytes / big_us / 1e3 / HBM_PEAK_GBS, 4),
         "sampling_step_us": round(step_us, 2),
-        "config": {"workload": "8 samples of a 2005-token prompt, 32 q / 8 kv heads, head_dim 128, bf16"},
+        "config": {"workload": "4096 block pairs of a 16384-block bf16 pool (8 kv heads, 16 tokens, head_dim 128: "
+                               "32 KiB per block and pool); the sampling step: 8 samples of a 2005-token prompt, "
+                               "32 q / 8 kv heads"},
+        "roofline": {
+            "kernel": "copy_blocks_kernel (4096 pairs)",
+            "bound": "hbm",
+            "achieved": round(big_gbs, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(big_gbs / HBM_PEAK_GBS, 4),
+            "traffic": committed_traffic("copy-4096", "copy_blocks_kernel", COPY_SOURCES),
+            "algorithmic_bytes_per_launch": big_bytes,
+            "mean_call_us": round(big_us, 2),
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on the host ...")
+        result["cpu_baseline"] = cow_cpu_baseline(args.cpu_seconds)
+    else:
+        result["cpu_baseline"] = None
+    return result
+
+
+def cow_cpu_baseline(min_seconds: float):
+    """The oracle's block copy on this host over a bounded sample: 512 pairs
+    of a 2048-block bf16 pool per call, repeated for min_seconds."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+
+    rng = np.random.default_rng(8)
+    NB, pairs = 2048, 512
+    kp = rng.integers(0, 1 << 16, size=(NB, 8, 16, 128), dtype=np.uint16)
+    vp = rng.integers(0, 1 << 16, size=(NB, 8, 128, 16), dtype=np.uint16)
+    perm = rng.permutation(NB)
+    src, dst = perm[:pairs], perm[pairs:2 * pairs]
+    block_bytes = 8 * 16 * 128 * 2
+    reps, t0 = 0, time.perf_counter()
+    with threadpool_limits(1):
+        while reps == 0 or time.perf_counter() - t0 < min_seconds:
+            oracle.oracle_copy_blocks(kp, vp, src, dst)
+            reps += 1
+    sec = time.perf_counter() - t0
+    return {
+        "value": round(reps * 2 * 2 * pairs * block_bytes / sec / 1e9, 3),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{pairs} block copies (K and V, 32 KiB per block and pool) in a {NB}-block bf16 pool through "
+                  f"oracle_copy_blocks (which copies the whole pool first), {reps} calls, {sec:.1f} s on one "
+                  f"host thread; value counts the copied blocks' read + write bytes",
     }
 
 
