@@ -604,6 +604,127 @@ def cow_cpu_baseline(min_seconds: float):
     }
 
 
+def append_bench(args) -> dict:
+    """kv_append on its own: 65,536 new tokens of a Llama-3-8B layer (8 kv
+    heads, head_dim 128) into consecutive slots (a prefill chunk's appends,
+    the line's value), plus scattered slots at 65,536, 4,096 and 256 tokens
+    (decode steps append one token per sequence into its own block)."""
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_23_amd import ops
+    from paged_kv_cache_23_amd.workloads import storage_numpy
+
+    dev = torch.device("cuda:0")
+    kv = args.kv_dtype
+    Hkv, D, bs = 8, 128, args.block_size
+    fp8 = kv == "fp8"
+    elt = {"f32": 4, "bf16": 2, "fp8": 1}[kv]
+    in_elt = 4 if kv == "f32" else 2
+    pool_dtype = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}[kv]
+    new_dtype = torch.float32 if kv == "f32" else torch.bfloat16
+    scales = (torch.full((Hkv,), 4.0 / 448.0, dtype=torch.float32, device=dev),) * 2 if fp8 else (None, None)
+    gen = torch.Generator().manual_seed(9)
+    rng = np.random.default_rng(9)
+
+    def case(T, pattern, reps):
+        NB = (T // bs + 8) if pattern == "consecutive" else 2 * T + 8
+        kp = torch.zeros((NB, Hkv, bs, D), dtype=pool_dtype, device=dev)
+        vp = torch.zeros((NB, Hkv, D, bs), dtype=pool_dtype, device=dev)
+        kn = torch.randn((T, Hkv, D), generator=gen).to(new_dtype).to(dev)
+        vn = torch.randn((T, Hkv, D), generator=gen).to(new_dtype).to(dev)
+        if pattern == "consecutive":
+            slots = np.arange(T, dtype=np.int64) + 3 * bs
+        else:
+            slots = rng.permutation(NB)[:T].astype(np.int64) * bs + rng.integers(0, bs, size=T)
+        sl = torch.from_numpy(slots).to(dev)
+        call = lambda: ops.kv_append(kn, vn, sl, kp, vp, *scales)
+        for _ in range(5):
+            call()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            call()
+        b.record()
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) / reps * 1e3
+        nbytes = T * Hkv * D * 2 * (in_elt + elt)   # K and V: read the new values, write the pool
+        log(f"append {kv} T={T} {pattern}: {us:.1f} us per call, {nbytes / us / 1e3:.1f} GB/s")
+        return us, nbytes, (kp, vp, kn, vn, slots)
+
+    us, nbytes, keep = case(65536, "consecutive", args.steps)
+    others = {f"{p}_{T}": case(T, p, args.steps)[:2] for T, p in ((65536, "scattered"), (4096, "scattered"),
+                                                                     (256, "scattered"))}
+    gbs = nbytes / us / 1e3
+    result = {
+        "metric": "kv_append GB/s (new K/V read + pool written), 65,536 tokens into consecutive slots",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": 5,
+        "ms_per_step": round(us / 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"f32": "f32", "bf16": "bf16", "fp8": "fp8-e4m3 kv / bf16 input"}[kv],
+        "data": "synthetic",
+        "config": {"workload": f"65,536 new tokens, 8 kv heads, head_dim 128, {bs}-token blocks, {kv} cache"},
+        "scattered_us": {k: round(v[0], 2) for k, v in others.items()},
+        "scattered_gbs": {k: round(v[1] / v[0] / 1e3, 1) for k, v in others.items()},
+        "max_abs_err_sampled": None,
+        "roofline": {
+            "kernel": f"append_kernel<{kv}, 128>",
+            "bound": "hbm",
+            "achieved": round(gbs, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "algorithmic_bytes_per_launch": nbytes,
+            "mean_call_us": round(us, 2),
+        },
+    }
+    if not args.no_cpu_baseline:
+        # the oracle leg: the first 512 tokens' slots compared bit for bit,
+        # then the oracle's append timed on the host
+        import oracle
+        from threadpoolctl import threadpool_limits
+
+        kp, vp, kn, vn, slots = keep
+        n = 512
+        sub = slice(0, (n + 3 * bs) // bs)   # the blocks that only these tokens fill
+        k0 = np.zeros(storage_numpy(kp[sub].cpu()).shape, dtype=storage_numpy(kp[sub].cpu()).dtype)
+        v0 = np.zeros(storage_numpy(vp[sub].cpu()).shape, dtype=k0.dtype)
+        sc = (None, None) if not fp8 else tuple(x.cpu().numpy() for x in scales)
+        ref_k, ref_v = oracle.oracle_append(k0, v0, storage_numpy(kn[:n].cpu()), storage_numpy(vn[:n].cpu()),
+                                            slots[:n], kv, *sc)
+        exact = bool(np.array_equal(storage_numpy(kp[sub].cpu()), ref_k) and
+                     np.array_equal(storage_numpy(vp[sub].cpu()), ref_v))
+        log(f"first {n} tokens' slots equal the oracle's append: {exact}")
+        result["max_abs_err_sampled"] = 0.0 if exact else None
+        result["append_bit_exact_sampled"] = exact
+        reps, t0 = 0, time.perf_counter()
+        with threadpool_limits(1):
+            while reps == 0 or time.perf_counter() - t0 < args.cpu_seconds:
+                oracle.oracle_append(k0, v0, storage_numpy(kn[:n].cpu()), storage_numpy(vn[:n].cpu()), slots[:n], kv,
+                                     *sc)
+                reps += 1
+        sec = time.perf_counter() - t0
+        result["cpu_baseline"] = {
+            "value": round(reps * n * Hkv * D * 2 * (in_elt + elt) / sec / 1e9, 4),
+            "unit": "GB/s",
+            "cores": 1,
+            "kind": "oracle",
+            "sample": f"oracle_append of {n} tokens into a {k0.shape[0]}-block pool (which it copies first), "
+                      f"{reps} calls, {sec:.1f} s on one host thread",
+        }
+    else:
+        result["cpu_baseline"] = None
+    return result
+
+
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 MFMA_F32_PEAK_TFLOPS = 157.3
 
@@ -837,7 +958,8 @@ def main() -> int:
     p.add_argument("--shared", action="store_true",
                    help="decode through pkv_paged_decode_shared: the tables' common leading blocks read once")
     p.add_argument("--kv-dtype", choices=["bf16", "fp8", "f32"], default="bf16",
-                   help="cache dtype of the --prefill workload")
+                   help="cache dtype of the --prefill and --append workloads")
+    p.add_argument("--append", action="store_true", help="time kv_append on its own instead")
     p.add_argument("--prefill", action="store_true",
                    help="time chunked prefill (a 10,000-token prompt in 2048-token chunks) instead")
     p.add_argument("--q-len", type=int, default=1,
@@ -861,6 +983,9 @@ def main() -> int:
         return 0
     if args.cow:
         print(json.dumps(cow_bench(args)), flush=True)
+        return 0
+    if args.append:
+        print(json.dumps(append_bench(args)), flush=True)
         return 0
     result = run_bench(args)
     print(json.dumps(result), flush=True)

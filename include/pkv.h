@@ -105,10 +105,15 @@ typedef struct pkv_cache_desc {
  *   slot_mapping  device [num_tokens]; a slot outside [0, num_blocks * B) is
  *                 padding and writes nothing
  *   k_pool, v_pool device pools, updated in place
+ * k_new, v_new and the pools must be 16-byte aligned (else PKV_EINVAL).
  * FP8: code = E4M3 round-to-nearest-even, saturating to +-448, of the IEEE
  * float32 quotient x / scale[h].  Slots must be distinct and must not lie in
  * blocks shared with other sequences; two tokens with the same slot leave
- * one of them.  num_tokens == 0 is a no-op. */
+ * one of them.  num_tokens == 0 is a no-op.
+ * One kernel: a workgroup per 16 consecutive new tokens and kv head.  When
+ * their slots are 16 consecutive rows of one block (a prefill chunk's
+ * appends) it writes the block's K rows as one run and its V tile row by row
+ * through LDS; otherwise it scatters element by element. */
 int pkv_kv_append(const pkv_cache_desc* desc, const void* k_new, const void* v_new,
                   const int64_t* slot_mapping, int32_t num_tokens, void* k_pool,
                   void* v_pool, void* stream);

@@ -239,6 +239,7 @@ int pkv_kv_append(const pkv_cache_desc* desc, const void* k_new, const void* v_n
   if (num_tokens < 0) return PKV_EINVAL;
   if (num_tokens == 0) return PKV_OK;
   if (!k_new || !v_new || !slot_mapping || !k_pool || !v_pool) return PKV_EINVAL;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_pool) || !aligned16(v_pool)) return PKV_EINVAL;
   pkv::AppendArgs a{};
   a.k_new = k_new;
   a.v_new = v_new;

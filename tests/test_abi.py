@@ -81,6 +81,8 @@ def test_null_and_size_errors():
     assert lib.pkv_kv_append(None, FAKE, FAKE, FAKE, 1, FAKE, FAKE, None) == EINVAL
     assert lib.pkv_kv_append(ctypes.byref(d), None, FAKE, FAKE, 1, FAKE, FAKE, None) == EINVAL
     assert lib.pkv_kv_append(ctypes.byref(d), FAKE, FAKE, FAKE, -1, FAKE, FAKE, None) == EINVAL
+    assert lib.pkv_kv_append(ctypes.byref(d), FAKE + 8, FAKE, FAKE, 1, FAKE, FAKE, None) == EINVAL   # misaligned k_new
+    assert lib.pkv_kv_append(ctypes.byref(d), FAKE, FAKE, FAKE, 1, FAKE, FAKE + 2, None) == EINVAL   # misaligned pool
     assert lib.pkv_kv_append(ctypes.byref(d), None, None, None, 0, None, None, None) == 0  # no-op
     assert lib.pkv_paged_decode(ctypes.byref(d), None, FAKE, FAKE, FAKE, 4, FAKE, 2, 64, 0.1,
                                 FAKE, None, 0, None) == EINVAL

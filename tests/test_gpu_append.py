@@ -76,3 +76,59 @@ def test_fp8_quantiser_exhaustive(scale):
                                         storage_numpy(v_new), slots.numpy(), "fp8", ks.numpy(), vs.numpy())
     assert np.array_equal(kp.cpu().numpy(), ref_k)
     assert np.array_equal(vp.cpu().numpy(), ref_v)
+
+
+def _bulk(kv_dtype, D, Hkv, bs, slots, seed):
+    """Append len(slots) new tokens at the given slots of a zeroed pool (test
+    data: N(0, 1) values; fp8 pools with per-head scales)."""
+    gen = torch.Generator().manual_seed(seed)
+    T = len(slots)
+    NB = int(max(max(slots) // bs + 2, 4))
+    in_dtype = torch.float32 if kv_dtype == "f32" else torch.bfloat16
+    pool_dtype = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}[kv_dtype]
+    k_new = torch.randn((T, Hkv, D), generator=gen).to(in_dtype)
+    v_new = torch.randn((T, Hkv, D), generator=gen).to(in_dtype)
+    k_pool = torch.zeros((NB, Hkv, bs, D), dtype=pool_dtype)
+    v_pool = torch.zeros((NB, Hkv, D, bs), dtype=pool_dtype)
+    ks = vs = None
+    if kv_dtype == "fp8":
+        ks = torch.linspace(0.004, 0.02, Hkv, dtype=torch.float32)
+        vs = ks * 1.5
+    sl = torch.tensor(slots, dtype=torch.int64)
+    d = torch.device("cuda:0")
+    kp, vp = k_pool.to(d), v_pool.to(d)
+    ops.kv_append(k_new.to(d), v_new.to(d), sl.to(d), kp, vp, None if ks is None else ks.to(d),
+                  None if vs is None else vs.to(d))
+    torch.cuda.synchronize()
+    ref_k, ref_v = oracle.oracle_append(storage_numpy(k_pool), storage_numpy(v_pool), storage_numpy(k_new),
+                                        storage_numpy(v_new), sl.numpy(), kv_dtype,
+                                        None if ks is None else ks.numpy(), None if vs is None else vs.numpy())
+    assert np.array_equal(storage_numpy(kp.cpu()), ref_k)
+    assert np.array_equal(storage_numpy(vp.cpu()), ref_v)
+
+
+@pytest.mark.parametrize("kv_dtype,D", [("bf16", 128), ("fp8", 128), ("f32", 64), ("bf16", 64)])
+@pytest.mark.parametrize("bs", [16, 32, 256])
+@pytest.mark.parametrize("first_run", [200, 1200])
+def test_bulk_appends_into_consecutive_slots(kv_dtype, D, bs, first_run):
+    """A prefill chunk's appends: runs of consecutive slots.  From 1,024 new
+    tokens the tiled kernel writes 16 tokens that fill 16 consecutive rows of
+    one block tile-wise and scatters the others; fewer tokens take the
+    one-wave-per-token kernel.  Runs starting on a 16-row boundary and off
+    it, a ragged last group, a run crossing a block boundary, padding inside
+    a run."""
+    up = lambda x: -(-x // bs) * bs                             # next block boundary
+    a1 = 3 * bs                                                 # aligned start, ragged end
+    a2 = up(a1 + first_run) + bs + 5                            # unaligned start
+    a3 = up(a2 + 77) + 2 * bs - 8                               # crosses into the next block
+    a4 = up(a3 + 48) + bs
+    pad = list(range(a4, a4 + 32))
+    pad[7] = -1                                                 # padding inside a would-be run
+    slots = list(range(a1, a1 + first_run)) + list(range(a2, a2 + 77)) + list(range(a3, a3 + 48)) + pad
+    assert len(set(s for s in slots if s >= 0)) == len([s for s in slots if s >= 0])   # distinct slots
+    _bulk(kv_dtype, D, 2, bs, slots, seed=bs + D)
+
+
+def test_bulk_append_large_run():
+    """4,096 tokens into consecutive slots across 8 kv heads: 256 full tiles per head."""
+    _bulk("bf16", 128, 8, 16, list(range(16, 16 + 4096)), seed=3)
