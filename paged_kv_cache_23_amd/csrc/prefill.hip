@@ -23,8 +23,9 @@
 // per SIMD); a workgroup owns one tile and walks every 32-token key chunk up
 // to the tile's last visible token, so no partial results leave the
 // workgroup.  The waves stage each chunk's K (token-major) and V
-// (dimension-major) from the pool into LDS together (three groups of two
-// chunk buffers, one barrier per group) and each reads its operands from
+// (dimension-major) from the pool into LDS together (three groups of three
+// chunk buffers, one for float32 tiles; one barrier per group) and each
+// reads its operands from
 // there; an fp8 cache is widened to bf16 (exactly) as it is staged, so the
 // LDS tiles and the operand reads are the bf16 ones.  Workgroups are
 // issued largest first (the last column tiles see the most keys), and
@@ -53,11 +54,13 @@ constexpr float kRescaleSlack = 8.f;
 // (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
 constexpr int kVmcntZero = 0x0F70;
 
-// LDS bank rule for 16-byte reads (measured on MI355X with the LDS bank
-// conflict counter): the 16 lanes of each quarter-wave are served together,
-// and lanes reading rows r = 0..15 of a tile at a row stride S are
-// conflict-free when S is 32 bytes plus a multiple of 64 (S = 80, 144 or 272
-// bytes conflict two-way).  Both tiles use such strides.
+// LDS bank rules for 16-byte reads (measured on MI355X with the LDS bank
+// conflict counter): lanes r = 0..15 of a quarter-wave reading rows of a
+// tile at a row stride S are conflict-free when S is 32 bytes plus a
+// multiple of 64 (S = 80, 144 or 272 bytes conflict two-way); the K tiles
+// use such strides.  The bf16 V tile is unpadded (64-byte rows, two-way
+// conflicts as is) and XOR-swizzles its 16-byte pieces instead, which the
+// counter shows conflict-free for the V reads.
 //
 // LDS row of chunk token t in the K tile.  The 16 lanes of a lane group read
 // the rows of tokens 8 (r / 4) + 4 x + (r % 4), r < 16; without this row
@@ -84,15 +87,21 @@ struct PrefillCfg {
   static constexpr int kWaveCols = 16 * kT;
   static constexpr int kGroupCols = kWaves * kWaveCols;          // columns per workgroup
   static constexpr int kSK = D + 32 / kEs;                       // K tile row stride: +32 bytes
-  static constexpr int kSV = kChunkTokens + 32 / kEs;          // V row: 96 bytes (bf16 tiles), 160 (float32)
+  // V tile row: bf16 tiles 64 bytes, unpadded, the four 16-byte pieces of
+  // dimension d at piece q ^ ((d >> 1) & 3); float32 tiles 160 bytes.
+  static constexpr int kSV = kLds == kBF16 ? kChunkTokens : kChunkTokens + 32 / kEs;
   static constexpr int kKRowPieces = D / kPerPiece;
   static constexpr int kVRowPieces = kChunkTokens / kPerPiece;
   static constexpr int kKPieces = kChunkTokens * kKRowPieces;
   static constexpr int kVPieces = D * kVRowPieces;
   static constexpr int kThreads = 64 * kWaves;
-  // Chunks per barrier: two (64 keys) where three pairs of chunk tiles fit
-  // in LDS, one for the float32 tiles.
-  static constexpr int kPair = KV == kF32 ? 1 : 2;
+  // Chunks per barrier: three (96 keys) for the bf16 tiles (three groups of
+  // three chunks: 149 KiB of LDS at head_dim 128), one for the float32 tiles.
+  // Each barrier lines the waves of a SIMD up in the same phase; between
+  // barriers they drift apart and overlap one's MFMAs with the other's
+  // vector work, so fewer barriers pay (three chunks per barrier: +3% over
+  // two on MI355X).
+  static constexpr int kPair = KV == kF32 ? 1 : 3;
   static constexpr int kKPerThread = (kKPieces + kThreads - 1) / kThreads;
   static constexpr int kVPerThread = (kVPieces + kThreads - 1) / kThreads;
   static constexpr int kKTileElems = kChunkTokens * kSK;
@@ -140,7 +149,8 @@ template <int KV, int D>
 __device__ __forceinline__ void lds_v(typename PrefillCfg<KV, D>::Tile::V& v,
                                       const typename PrefillCfg<KV, D>::Elem* vs, int r, int j) {
   using C = PrefillCfg<KV, D>;
-  const typename C::Elem* base = vs + r * C::kSV + 8 * j;
+  // bf16 tiles: piece j of dimension 16 u + r sits at piece j ^ ((r >> 1) & 3)
+  const typename C::Elem* base = vs + r * C::kSV + 8 * (KV == kBF16 ? (j ^ ((r >> 1) & 3)) : j);
 #pragma unroll
   for (int u = 0; u < D / 16; ++u) {
     const typename C::Elem* p = base + 16 * u * C::kSV;
@@ -308,7 +318,9 @@ __device__ __forceinline__ void prefill_body(const DecodeArgs& a, const int32_t*
   constexpr int VH = C::kVRowPieces / 2;
   constexpr int kPs = C::kPs;   // pool element bytes
   uint32_t k_src[C::kKPerThread], v_src[C::kVPerThread];   // byte offsets inside a half
-  int k_dst[C::kKPerThread], v_dst[C::kVPerThread];        // LDS element offsets
+  // LDS element offsets; v_dst2: of an fp8 V piece's second bf16 piece
+  // from its first (the swizzle may put it before)
+  int k_dst[C::kKPerThread], v_dst[C::kVPerThread], v_dst2[C::kVPerThread];
   int k_half[C::kKPerThread], v_half[C::kVPerThread], v_tok[C::kVPerThread];
 #pragma unroll
   for (int i = 0; i < C::kKPerThread; ++i) {
@@ -325,7 +337,14 @@ __device__ __forceinline__ void prefill_body(const DecodeArgs& a, const int32_t*
     v_half[i] = uni(p / (D * VH));
     v_tok[i] = 16 * v_half[i] + q * C::kPerPiece;
     v_src[i] = (uint32_t)((d * bs + q * C::kPerPiece) * kPs);
-    v_dst[i] = d * C::kSV + v_tok[i];
+    if constexpr (C::kLds == kBF16) {
+      const int sw = (d >> 1) & 3, lp = v_tok[i] / 8;
+      v_dst[i] = d * C::kSV + 8 * (lp ^ sw);
+      v_dst2[i] = 8 * (((lp + 1) ^ sw) - (lp ^ sw));
+    } else {
+      v_dst[i] = d * C::kSV + v_tok[i];
+      v_dst2[i] = 8;
+    }
   }
   struct Stage {
     u32x4 k[C::kKPerThread];
@@ -366,10 +385,10 @@ __device__ __forceinline__ void prefill_body(const DecodeArgs& a, const int32_t*
   };
   // A piece of 16 fp8 codes is widened (exactly) to 16 bf16 values: two
   // 16-byte LDS stores.
-  auto put = [&](Elem* dst, const u32x4& w) {
+  auto put = [&](Elem* dst, const u32x4& w, int second) {
     if constexpr (KV == kFP8) {
       *reinterpret_cast<u32x4*>(dst) = fp8x8_to_bf16x8(w[0], w[1]);
-      *reinterpret_cast<u32x4*>(dst + 8) = fp8x8_to_bf16x8(w[2], w[3]);
+      *reinterpret_cast<u32x4*>(dst + second) = fp8x8_to_bf16x8(w[2], w[3]);
     } else {
       *reinterpret_cast<u32x4*>(dst) = w;
     }
@@ -377,10 +396,10 @@ __device__ __forceinline__ void prefill_body(const DecodeArgs& a, const int32_t*
   auto stage_store = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < C::kKPerThread; ++i)
-      if (C::kKPieces % C::kThreads == 0 || tid + C::kThreads * i < C::kKPieces) put(&lds_kt[buf][k_dst[i]], st.k[i]);
+      if (C::kKPieces % C::kThreads == 0 || tid + C::kThreads * i < C::kKPieces) put(&lds_kt[buf][k_dst[i]], st.k[i], 8);
 #pragma unroll
     for (int i = 0; i < C::kVPerThread; ++i)
-      if (C::kVPieces % C::kThreads == 0 || tid + C::kThreads * i < C::kVPieces) put(&lds_vt[buf][v_dst[i]], st.v[i]);
+      if (C::kVPieces % C::kThreads == 0 || tid + C::kThreads * i < C::kVPieces) put(&lds_vt[buf][v_dst[i]], st.v[i], v_dst2[i]);
   };
 
   // Per column tile: accumulator, the reference max m_ref of its
