@@ -9,12 +9,11 @@
 //
 // K tiles are token-major, so a token's K row is D contiguous elements; V
 // tiles are dim-major, so its V column is D elements B apart.  For an fp8
-// cache the bf16 input is divided by the kv head's float32 scale (IEEE
-// division) and rounded to E4M3 below.
+// cache the bf16 input is divided by the kv head's float32 scale and
+// rounded to E4M3, with the result of the IEEE division followed by E4M3
+// rounding (below).
 
 #include "pkv_internal.h"
-
-#include <type_traits>
 
 namespace pkv {
 namespace {
@@ -33,30 +32,54 @@ struct Vec16<uint32_t> {
   typedef uint32_t type __attribute__((ext_vector_type(4)));
 };
 
-// float32 -> OCP E4M3FN code: round to nearest, ties to even; |x| >= 448
-// (infinities included) saturates to +-448; NaN gives the NaN code with the
-// input's sign.  Works on the binary32 fields: the 24-bit significand is
-// shifted so that its integer part counts E4M3 grid steps.  In the binade
-// of 2^E (E >= -6) the grid step is 2^(E-3), i.e. the significand's top 4
-// bits; below 2^-6 the step stays 2^-9 (subnormal codes 0..8).
-__device__ __forceinline__ uint32_t e4m3_from_f32(float x) {
-  const uint32_t u = __builtin_bit_cast(uint32_t, x);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const uint32_t mag = u & 0x7FFFFFFFu;
-  if (mag > 0x7F800000u) return sign | 0x7Fu;        // NaN
-  if (mag >= 0x43E00000u) return sign | 0x7Eu;       // >= 448: saturate
-  const int e = (int)(mag >> 23);                    // biased binary32 exponent
-  const uint32_t sig = e ? ((mag & 0x7FFFFFu) | 0x800000u) : (mag & 0x7FFFFFu);
-  const int e_eff = e ? e : 1;
-  const int shift = e_eff >= 121 ? 20 : 141 - e_eff; // 121 = 127 - 6
-  if (shift > 24) return sign;                       // below half of 2^-9
-  const uint32_t steps = sig >> shift;
-  const uint32_t rem = sig & ((1u << shift) - 1u);
-  const uint32_t half = 1u << (shift - 1);
-  const uint32_t q = steps + ((rem > half || (rem == half && (steps & 1u))) ? 1u : 0u);
-  // normal binades: code = (E + 7) * 8 + (q - 8) with E = e_eff - 127
-  const uint32_t code = e_eff >= 121 ? (uint32_t)(e_eff - 120) * 8u + q - 8u : q;
-  return sign | code;
+// float32 -> OCP E4M3FN codes of two values (low byte: a): round to
+// nearest, ties to even; |x| >= 448 (infinities included) saturates to
+// +-448; NaN gives the NaN code with the input's sign.  gfx950's
+// v_cvt_pk_fp8_f32 rounds to nearest even but does not saturate, so it is
+// given the values clamped to [-448, 448] by v_med3_f32; the clamp turns a
+// NaN into a number, so NaN codes are put back afterwards.  (Over all 2^32
+// binary32 inputs this agrees with rounding the binary32 fields directly,
+// checked on MI355X.)
+__device__ __forceinline__ uint32_t e4m3_pair(float a, float b) {
+  uint32_t w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(a, -448.f, 448.f),
+                                                         __builtin_amdgcn_fmed3f(b, -448.f, 448.f), 0, false);
+  if (a != a) w = (w & 0xFF00u) | ((__builtin_bit_cast(uint32_t, a) >> 24) & 0x80u) | 0x7Fu;
+  if (b != b) w = (w & 0x00FFu) | ((((__builtin_bit_cast(uint32_t, b) >> 24) & 0x80u) | 0x7Fu) << 8);
+  return w & 0xFFFFu;
+}
+
+// x / s for the E4M3 rounding above, equal in code to the correctly rounded
+// binary32 quotient (IEEE division, then E4M3 rounding).  The quotient is
+// taken as q0 = x * r with r = 1/s correctly rounded: for a normal s and r,
+// q0 is within 1.51 * 2^-23 |x/s| of x/s, and the correctly rounded quotient
+// within 2^-24 |x/s|, so the two are at most 3 units in the last place of q0
+// apart.  Where the E4M3 rounding cannot tell them apart, q0 is used:
+//  - |q0| < 2^-11: both round to a signed zero (below half of 2^-9);
+//  - 2^-6 <= |q0| <= 2^16: every E4M3 rounding boundary in that range (the
+//    midpoints between neighbouring codes, which keep 4 significand bits)
+//    has its 20 low significand bits equal to 0x80000; q0 more than 4 units
+//    from that pattern lies strictly on the same side of every boundary as
+//    the correctly rounded quotient (values past 448 all saturate).
+// Otherwise (the E4M3 subnormal range, near a boundary, huge values, NaN,
+// or a scale whose reciprocal is not a normal number) the quotient is the
+// IEEE division itself.  The fast case replaces a division sequence by one
+// multiply in all but a few inputs in 10^4.
+struct Fp8Scale {
+  float s, r;
+  bool fast;
+};
+__device__ __forceinline__ Fp8Scale fp8_scale(float s) {
+  return Fp8Scale{s, __fdiv_rn(1.f, s), s >= 0x1p-125f && s <= 0x1p125f};
+}
+__device__ __forceinline__ float fp8_quotient(float x, const Fp8Scale& q) {
+  if (q.fast) {
+    const float q0 = x * q.r;
+    const float m = fabsf(q0);
+    const int dm = (int)(__builtin_bit_cast(uint32_t, m) & 0xFFFFFu) - 0x80000;
+    if (m < 0x1p-11f) return q0;
+    if (m >= 0x1p-6f && m <= 0x1p16f && (dm > 4 || dm < -4)) return q0;
+  }
+  return __fdiv_rn(x, q.s);
 }
 
 // Value stored for new element x of kv head h: a bit copy, or for an fp8
@@ -67,22 +90,33 @@ template <>
 struct Store<kF32> {
   using In = uint32_t;
   using Out = uint32_t;
-  __device__ static Out put(In x, float) { return x; }
+  using Scale = float;
+  __device__ static Out put(In x, const Scale&) { return x; }
 };
 template <>
 struct Store<kBF16> {
   using In = uint16_t;
   using Out = uint16_t;
-  __device__ static Out put(In x, float) { return x; }
+  using Scale = float;
+  __device__ static Out put(In x, const Scale&) { return x; }
 };
 template <>
 struct Store<kFP8> {
   using In = uint16_t;   // bf16
   using Out = uint8_t;
-  __device__ static Out put(In x, float s) {
-    return (Out)e4m3_from_f32(__fdiv_rn(__builtin_bit_cast(float, (uint32_t)x << 16), s));
+  using Scale = Fp8Scale;
+  __device__ static float widen(In x) { return __builtin_bit_cast(float, (uint32_t)x << 16); }
+  __device__ static Out put(In x, const Scale& s) { return (Out)e4m3_pair(fp8_quotient(widen(x), s), 0.f); }
+  // codes of two elements: low byte x0
+  __device__ static uint32_t put2(In x0, In x1, const Scale& s) {
+    return e4m3_pair(fp8_quotient(widen(x0), s), fp8_quotient(widen(x1), s));
   }
 };
+template <int KV>
+__device__ __forceinline__ typename Store<KV>::Scale store_scale(const float* scales, int h) {
+  if constexpr (KV == kFP8) return fp8_scale(scales[h]);
+  else return 1.f;
+}
 
 // Few new tokens (a decode step: one per sequence, each into its own
 // block): one wave per (token, kv head), so every token's quantisation and
@@ -101,20 +135,15 @@ __global__ __launch_bounds__(64) void append_scatter_kernel(AppendArgs a) {
   const size_t ktile = ((size_t)blk * a.num_kv_heads + h) * bs * D;
   const size_t kdst = ktile + (size_t)off * D;     // token-major: row `off`
   const size_t vdst = ktile + off;                 // dim-major: column `off`
+  using S = Store<KV>;
+  const typename S::In* kn = static_cast<const typename S::In*>(a.k_new);
+  const typename S::In* vn = static_cast<const typename S::In*>(a.v_new);
+  typename S::Out* kp = static_cast<typename S::Out*>(a.k_pool);
+  typename S::Out* vp = static_cast<typename S::Out*>(a.v_pool);
+  const typename S::Scale ks = store_scale<KV>(a.k_scale, h), vs = store_scale<KV>(a.v_scale, h);
   for (int d = threadIdx.x; d < D; d += 64) {
-    if constexpr (KV == kFP8) {
-      const uint16_t* kn = static_cast<const uint16_t*>(a.k_new);
-      const uint16_t* vn = static_cast<const uint16_t*>(a.v_new);
-      const float kx = __builtin_bit_cast(float, (uint32_t)kn[src + d] << 16);
-      const float vx = __builtin_bit_cast(float, (uint32_t)vn[src + d] << 16);
-      static_cast<uint8_t*>(a.k_pool)[kdst + d] = (uint8_t)e4m3_from_f32(__fdiv_rn(kx, a.k_scale[h]));
-      static_cast<uint8_t*>(a.v_pool)[vdst + (size_t)d * bs] =
-          (uint8_t)e4m3_from_f32(__fdiv_rn(vx, a.v_scale[h]));
-    } else {
-      using E = typename std::conditional<KV == kF32, uint32_t, uint16_t>::type;
-      static_cast<E*>(a.k_pool)[kdst + d] = static_cast<const E*>(a.k_new)[src + d];
-      static_cast<E*>(a.v_pool)[vdst + (size_t)d * bs] = static_cast<const E*>(a.v_new)[src + d];
-    }
+    kp[kdst + d] = S::put(kn[src + d], ks);
+    vp[vdst + (size_t)d * bs] = S::put(vn[src + d], vs);
   }
 }
 
@@ -144,11 +173,7 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
   const In* vn = static_cast<const In*>(a.v_new);
   Out* kp = static_cast<Out*>(a.k_pool);
   Out* vp = static_cast<Out*>(a.v_pool);
-  float ks = 1.f, vs = 1.f;
-  if constexpr (KV == kFP8) {
-    ks = a.k_scale[h];
-    vs = a.v_scale[h];
-  }
+  const typename S::Scale ks = store_scale<KV>(a.k_scale, h), vs = store_scale<KV>(a.v_scale, h);
   const int64_t limit = (int64_t)a.num_blocks * bs;
 
   __shared__ int64_t slot[kGroup];
@@ -174,11 +199,8 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
       const u32x4 w = *reinterpret_cast<const u32x4*>(kn + ((size_t)(g0 + k) * Hkv + h) * D + d0);
       if constexpr (KV == kFP8) {
         const auto x = __builtin_bit_cast(typename Vec16<In>::type, w);
-        uint32_t lo = 0, hi = 0;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) lo |= (uint32_t)S::put(x[e], ks) << (8 * e);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) hi |= (uint32_t)S::put(x[4 + e], ks) << (8 * e);
+        const uint32_t lo = S::put2(x[0], x[1], ks) | (S::put2(x[2], x[3], ks) << 16);
+        const uint32_t hi = S::put2(x[4], x[5], ks) | (S::put2(x[6], x[7], ks) << 16);
         *reinterpret_cast<u32x2*>(kdst + (size_t)k * D + d0) = u32x2{lo, hi};
       } else {
         *reinterpret_cast<u32x4*>(kdst + (size_t)k * D + d0) = w;
@@ -189,8 +211,17 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
       const int k = v / kRowVecs, d0 = (v - k * kRowVecs) * kVec;
       const u32x4 w = *reinterpret_cast<const u32x4*>(vn + ((size_t)(g0 + k) * Hkv + h) * D + d0);
       const auto x = __builtin_bit_cast(typename Vec16<In>::type, w);
+      if constexpr (KV == kFP8) {
 #pragma unroll
-      for (int e = 0; e < kVec; ++e) vt[d0 + e][k] = S::put(x[e], vs);
+        for (int e = 0; e < kVec; e += 2) {
+          const uint32_t c = S::put2(x[e], x[e + 1], vs);
+          vt[d0 + e][k] = (Out)c;
+          vt[d0 + e + 1][k] = (Out)(c >> 8);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) vt[d0 + e][k] = S::put(x[e], vs);
+      }
     }
     __syncthreads();
     // 16-byte pieces of the V rows: kOut tokens of one dim

@@ -54,12 +54,23 @@ def test_append_fp8_step_shape():
     _check_append(fp8_b256())
 
 
-@pytest.mark.parametrize("scale", [1.0, 0.37, 1.0 / 448.0, 3.5e-3])
-def test_fp8_quantiser_exhaustive(scale):
+# Scales: typical max/448 values, powers of two, the ends of the range where
+# the kernels' quotient shortcut applies (2^-125 .. 2^125) and just past
+# them, a negative scale, and values whose quotients fill the E4M3
+# subnormal and saturated ranges.
+QUANT_SCALES = [1.0, 0.37, 1.0 / 448.0, 3.5e-3, 2.0 ** -20, 1e-6, 7.3e-5, 0.0123, 5.5, 123.0, 3.0e4,
+                2.0 ** -125, 2.0 ** -126, 2.0 ** 124, 2.0 ** 126, -0.5]
+
+
+@pytest.mark.parametrize("tokens", [512, 1024])
+@pytest.mark.parametrize("scale", QUANT_SCALES)
+def test_fp8_quantiser_exhaustive(scale, tokens):
     """Every bf16 input pattern encodes to the same E4M3 code on the GPU and in
-    the oracle: one kv head, 512 tokens x 128 dims = all 65,536 patterns."""
-    D, Hkv, T = 128, 1, 512
-    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16).reshape(T, Hkv, D)
+    the oracle: one kv head, 128 dims, all 65,536 patterns (twice at 1,024
+    tokens); 512 tokens run the one-wave-per-token kernel, 1,024 consecutive
+    slots the tiled one."""
+    D, Hkv, T = 128, 1, tokens
+    bits = np.resize(np.arange(65536, dtype=np.uint32).astype(np.uint16), T * D).reshape(T, Hkv, D)
     k_new = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16)
     v_new = torch.from_numpy(bits[::-1].copy().view(np.int16)).view(torch.bfloat16)
     NB = T // 16
@@ -72,8 +83,9 @@ def test_fp8_quantiser_exhaustive(scale):
     kp, vp = k_pool.to(d), v_pool.to(d)
     ops.kv_append(k_new.to(d), v_new.to(d), slots.to(d), kp, vp, ks.to(d), vs.to(d))
     torch.cuda.synchronize()
-    ref_k, ref_v = oracle.oracle_append(k_pool.numpy(), v_pool.numpy(), storage_numpy(k_new),
-                                        storage_numpy(v_new), slots.numpy(), "fp8", ks.numpy(), vs.numpy())
+    with np.errstate(over="ignore", invalid="ignore", divide="ignore"):
+        ref_k, ref_v = oracle.oracle_append(k_pool.numpy(), v_pool.numpy(), storage_numpy(k_new),
+                                            storage_numpy(v_new), slots.numpy(), "fp8", ks.numpy(), vs.numpy())
     assert np.array_equal(kp.cpu().numpy(), ref_k)
     assert np.array_equal(vp.cpu().numpy(), ref_v)
 
