@@ -169,10 +169,11 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
   const int bs = a.block_size;
   const int n = min(kGroup, a.num_tokens - g0);
   const int tid = threadIdx.x;
-  const In* kn = static_cast<const In*>(a.k_new);
-  const In* vn = static_cast<const In*>(a.v_new);
-  Out* kp = static_cast<Out*>(a.k_pool);
-  Out* vp = static_cast<Out*>(a.v_pool);
+  // the new tokens' K/V and the pools do not overlap
+  const In* __restrict__ kn = static_cast<const In*>(a.k_new);
+  const In* __restrict__ vn = static_cast<const In*>(a.v_new);
+  Out* __restrict__ kp = static_cast<Out*>(a.k_pool);
+  Out* __restrict__ vp = static_cast<Out*>(a.v_pool);
   const typename S::Scale ks = store_scale<KV>(a.k_scale, h), vs = store_scale<KV>(a.v_scale, h);
   const int64_t limit = (int64_t)a.num_blocks * bs;
 
@@ -192,11 +193,29 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
     // 16-byte input vectors: kVec elements of one new token's row
     constexpr int kVec = 16 / sizeof(In);
     constexpr int kRowVecs = D / kVec;
+    // Every thread's K and V input vectors are loaded first, so both loads
+    // are in flight together (kGroup * kRowVecs <= 2 kAppendThreads).
+    constexpr int kPer = (kGroup * kRowVecs + kAppendThreads - 1) / kAppendThreads;
+    static_assert(kPer <= 2, "input vectors per thread");
+    u32x4 kin[kPer], vin[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int v = tid + i * kAppendThreads;
+      if (v < kGroup * kRowVecs) {
+        const int k = v / kRowVecs, d0 = (v - k * kRowVecs) * kVec;
+        const size_t src = ((size_t)(g0 + k) * Hkv + h) * D + d0;
+        kin[i] = *reinterpret_cast<const u32x4*>(kn + src);
+        vin[i] = *reinterpret_cast<const u32x4*>(vn + src);
+      }
+    }
     // K: rows off .. off+15 of the tile are kGroup * D contiguous elements
     Out* kdst = kp + tile + (size_t)off * D;
-    for (int v = tid; v < kGroup * kRowVecs; v += kAppendThreads) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int v = tid + i * kAppendThreads;
+      if (v >= kGroup * kRowVecs) break;
       const int k = v / kRowVecs, d0 = (v - k * kRowVecs) * kVec;
-      const u32x4 w = *reinterpret_cast<const u32x4*>(kn + ((size_t)(g0 + k) * Hkv + h) * D + d0);
+      const u32x4 w = kin[i];
       if constexpr (KV == kFP8) {
         const auto x = __builtin_bit_cast(typename Vec16<In>::type, w);
         const uint32_t lo = S::put2(x[0], x[1], ks) | (S::put2(x[2], x[3], ks) << 16);
@@ -207,9 +226,12 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
       }
     }
     // V: element (token k, dim d) goes to row d, column off + k, through LDS
-    for (int v = tid; v < kGroup * kRowVecs; v += kAppendThreads) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int v = tid + i * kAppendThreads;
+      if (v >= kGroup * kRowVecs) break;
       const int k = v / kRowVecs, d0 = (v - k * kRowVecs) * kVec;
-      const u32x4 w = *reinterpret_cast<const u32x4*>(vn + ((size_t)(g0 + k) * Hkv + h) * D + d0);
+      const u32x4 w = vin[i];
       const auto x = __builtin_bit_cast(typename Vec16<In>::type, w);
       if constexpr (KV == kFP8) {
 #pragma unroll
