@@ -101,7 +101,7 @@ struct PrefillCfg {
   // barriers they drift apart and overlap one's MFMAs with the other's
   // vector work, so fewer barriers pay (three chunks per barrier: +3% over
   // two on MI355X).
-  static constexpr int kPair = KV == kF32 ? 1 : 3;
+  static constexpr int kGroupChunks = KV == kF32 ? 1 : 3;
   static constexpr int kKPerThread = (kKPieces + kThreads - 1) / kThreads;
   static constexpr int kVPerThread = (kVPieces + kThreads - 1) / kThreads;
   static constexpr int kKTileElems = kChunkTokens * kSK;
@@ -207,8 +207,8 @@ __device__ __forceinline__ void prefill_body(const DecodeArgs& a, const int32_t*
 
   // Three chunk buffers: chunk c + 2 is staged while chunk c is computed and
   // chunk c + 1's operands are read.
-  __shared__ __attribute__((aligned(16))) Elem lds_kt[3 * C::kPair][C::kKTileElems];
-  __shared__ __attribute__((aligned(16))) Elem lds_vt[3 * C::kPair][C::kVTileElems];
+  __shared__ __attribute__((aligned(16))) Elem lds_kt[3 * C::kGroupChunks][C::kKTileElems];
+  __shared__ __attribute__((aligned(16))) Elem lds_vt[3 * C::kGroupChunks][C::kVTileElems];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -509,13 +509,13 @@ __device__ __forceinline__ void prefill_body(const DecodeArgs& a, const int32_t*
     if (more) lds_v<C::kLds, D>(vf, lds_vt[nbuf], r, j);
   };
 
-  // Pipeline over groups of kPair chunks (one barrier per group).  Chunk c
-  // lives in LDS buffer kPair * ((c / kPair) % 3) + c % kPair.  Before
-  // iteration p (chunks kPair p ...), groups p and p + 1 are in LDS;
-  // iteration p stages group p + 2 into group p - 1's buffers, one chunk
-  // after each chunk step; group p - 1's operands were read by the end of
-  // iteration p - 1 (before the barrier that ended it).
-  constexpr int kP = C::kPair;
+  // Pipeline over groups of P = kGroupChunks chunks (one barrier per
+  // group).  Chunk c lives in LDS buffer P ((c / P) % 3) + c % P.  Before
+  // iteration p (chunks P p ...), groups p and p + 1 are in LDS; iteration
+  // p stages group p + 2 into group p - 1's buffers, one chunk after each
+  // chunk step; group p - 1's operands were read by the end of iteration
+  // p - 1 (before the barrier that ended it).
+  constexpr int kP = C::kGroupChunks;
   auto bufof = [](int c) { return kP * ((c / kP) % 3) + c % kP; };
   for (int c = 0; c < 2 * kP && c < nck; ++c) {
     stage_load(c);
