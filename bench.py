@@ -50,6 +50,7 @@ def log(msg: str) -> None:
 
 
 COPY_SOURCES = ["paged_kv_cache_23_amd/csrc/copy.hip", "paged_kv_cache_23_amd/csrc/pkv_internal.h"]
+APPEND_SOURCES = ["paged_kv_cache_23_amd/csrc/append.hip", "paged_kv_cache_23_amd/csrc/pkv_internal.h"]
 PREFILL_SOURCES = ["paged_kv_cache_23_amd/csrc/prefill.hip", "paged_kv_cache_23_amd/csrc/tile_math.h",
                    "paged_kv_cache_23_amd/csrc/pkv_internal.h"]
 
@@ -681,7 +682,8 @@ def append_bench(args) -> dict:
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(gbs / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": (committed_traffic(f"append-65536-{kv}", "append_kernel", APPEND_SOURCES)
+                        if bs == 16 else None),
             "algorithmic_bytes_per_launch": nbytes,
             "mean_call_us": round(us, 2),
         },

@@ -29,3 +29,33 @@ def test_unique_bytes_count_the_prefix_once():
     per_token = 2 * 2 * 64 * 2   # K and V, 2 kv heads, head_dim 64, bf16
     assert bench.unique_kv_bytes(wl, False) == (P + sum(tails)) * per_token
     assert wl.kv_bytes() == (3 * P + sum(tails)) * per_token
+
+
+def test_committed_traffic_profiles_match_the_current_kernels():
+    """Every committed HBM-counter summary that a bench line reports as its
+    roofline `traffic` was taken on the current kernel source (else the bench
+    would report null) and lies within a few percent above the algorithmic
+    bytes of its launch unit, where that is a fixed figure."""
+    cases = [("llama3-8b-b64", "paged_decode", None, None),
+             ("copy-4096", "copy_blocks_kernel", bench.COPY_SOURCES, 2 * 2 * 4096 * 32768),
+             ("prefill-70b-10k", "prefill_kernel", bench.PREFILL_SOURCES, None),
+             ("shared-prefix-256", "paged_decode_shared", bench.KERNEL_SOURCES + bench.PREFILL_SOURCES[:1], 326_193_152),
+             ("append-65536-bf16", "append_kernel", bench.APPEND_SOURCES, 65536 * 8 * 128 * 2 * 4),
+             ("append-65536-fp8", "append_kernel", bench.APPEND_SOURCES, 65536 * 8 * 128 * 2 * 3)]
+    for wl, kind, src, algo in cases:
+        t = bench.committed_traffic(wl, kind, src) if src is not None else bench.committed_traffic(wl)
+        assert t is not None, (wl, kind)
+        if algo is not None:
+            assert algo <= t <= 1.35 * algo, (wl, t, algo)
+
+
+def test_committed_traffic_rejects_a_changed_source(tmp_path, monkeypatch):
+    """A summary whose recorded source hash differs from the current code is
+    not reported."""
+    text = "source_hash: 0123456789abcdef\nhbm_bytes_per_launch: 1000\n"
+    (tmp_path / "append_kernel_x_hbm_traffic.txt").write_text(text)
+    monkeypatch.setattr(bench, "PROFILE_DIR", str(tmp_path))
+    assert bench.committed_traffic("x", "append_kernel", bench.APPEND_SOURCES) is None
+    h = bench.kernel_source_hash(bench.APPEND_SOURCES)
+    (tmp_path / "append_kernel_x_hbm_traffic.txt").write_text(text.replace("0123456789abcdef", h))
+    assert bench.committed_traffic("x", "append_kernel", bench.APPEND_SOURCES) == 1000.0
