@@ -210,7 +210,8 @@ int pkv_paged_decode_ex(const pkv_cache_desc* desc, const void* q, const void* k
  * Three kernels on `stream`: (1) the many-query kernel runs every sequence's
  * query heads over the prefix (row 0's blocks) as the columns of one
  * (virtual) sequence per kv head, the prefix cut into key segments, and
- * leaves float32 partials (max, sum, unnormalised accumulator) per segment;
+ * leaves partials per segment (float32 max and sum; the unnormalised
+ * accumulator in the output's type: bf16 unless the cache is float32);
  * (2) the decode split kernel runs each sequence's tokens after the prefix,
  * leaving partials only; (3) the merge kernel combines both sets of partials
  * per (sequence, head) with section 3's rescale and writes out.

@@ -198,10 +198,13 @@ int32_t prefix_segments(const pkv_cache_desc* d, int32_t num_seqs, int32_t prefi
   return (int32_t)((chunks + per - 1) / per);
 }
 
-// Prefix partials after the decode workspace: accumulators [S][B*Hq][D],
-// then (max, sum) pairs [S][B*Hq][2].
+// Prefix partials after the decode workspace: accumulators [S][B*Hq][D] in
+// the output's type (the merge's other inputs are float32; the prefix
+// partials are the bulk of what it reads), then float32 (max, sum) pairs
+// [S][B*Hq][2].
 size_t prefix_acc_bytes(const pkv_cache_desc* d, int32_t num_seqs, int32_t segments) {
-  return align_up((size_t)segments * num_seqs * d->num_q_heads * d->head_dim * sizeof(float));
+  const size_t elt = d->kv_dtype == PKV_F32 ? 4 : 2;
+  return align_up((size_t)segments * num_seqs * d->num_q_heads * d->head_dim * elt);
 }
 size_t prefix_ml_bytes(const pkv_cache_desc* d, int32_t num_seqs, int32_t segments) {
   return align_up((size_t)segments * num_seqs * d->num_q_heads * 2 * sizeof(float));
@@ -388,7 +391,7 @@ int pkv_paged_decode_shared(const pkv_cache_desc* desc, const void* q, const voi
     return PKV_EWORKSPACE;
   if (!aligned16(workspace)) return PKV_EINVAL;
   char* ws = static_cast<char*>(workspace);
-  float* pre_acc = reinterpret_cast<float*>(ws + dec);
+  void* pre_acc = ws + dec;
   float* pre_ml = reinterpret_cast<float*>(ws + dec + prefix_acc_bytes(desc, num_seqs, segs));
   hipStream_t s = static_cast<hipStream_t>(stream);
 

@@ -425,7 +425,7 @@ __global__ __launch_bounds__(128) void decode_merge_kernel(const int2* __restric
                                                            const float* __restrict__ ws_acc,
                                                            const float* __restrict__ ws_ml, OutT* __restrict__ out,
                                                            int num_seqs, int num_kv_heads, int group, int q_len,
-                                                           const float* __restrict__ pre_acc,
+                                                           const OutT* __restrict__ pre_acc,
                                                            const float* __restrict__ pre_ml, int pre_segments) {
   const int pair = blockIdx.x;
   const int2 m = meta[pair];
@@ -475,7 +475,7 @@ __global__ __launch_bounds__(128) void decode_merge_kernel(const int2* __restric
       for (int s = 0; s < pre_segments; ++s) {
         const size_t slot = s * stride + col;
         const float2 ml = *reinterpret_cast<const float2*>(pre_ml + slot * 2);
-        const f32x4 acc_s = *reinterpret_cast<const f32x4*>(pre_acc + slot * D + 4 * q4);
+        const f32x4 acc_s = load4<OutT>(pre_acc + slot * D + 4 * q4);
         const float w = exp2_fast(ml.x - M2u);
         L += ml.y * w;
         o += acc_s * w;
@@ -521,7 +521,7 @@ hipError_t launch_merge_p(const DecodeArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((decode_merge_kernel<OutT, D, kPrefix>), dim3(grid), dim3(128), 0, stream,
                      static_cast<const int2*>(a.pair_meta), static_cast<const float*>(a.ws_acc),
                      static_cast<const float*>(a.ws_ml), static_cast<OutT*>(a.out), a.num_seqs, a.num_kv_heads,
-                     a.group, a.q_len, a.pre_acc, a.pre_ml, a.pre_segments);
+                     a.group, a.q_len, static_cast<const OutT*>(a.pre_acc), a.pre_ml, a.pre_segments);
   return hipGetLastError();
 }
 

@@ -46,7 +46,9 @@ struct DecodeArgs {
   // Shared-prefix decode (all zero otherwise).
   int32_t table_offset;   // tail pass: prefix blocks (block_tables points past them)
   int32_t tail_pass;      // split kernel: tail pass (lengths minus the prefix, every pair leaves partials)
-  float* pre_acc;         // merge input: prefix partials [pre_segments][num_seqs * num_q_heads][head_dim]
+  // merge input: prefix partial accumulators [pre_segments][num_seqs * num_q_heads][head_dim],
+  // in the output's type (float32 for a float32 cache, else bf16)
+  void* pre_acc;
   float* pre_ml;          // [pre_segments][num_seqs * num_q_heads][2]  (max in log2 units, sum)
   int32_t pre_segments;   // merge: prefix pieces per column; prefill kernel: key segments
   int32_t prefix_tokens;  // prefill kernel in prefix mode: keys every column sees

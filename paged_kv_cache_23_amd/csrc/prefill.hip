@@ -224,7 +224,8 @@ __device__ __forceinline__ void prefill_body(const DecodeArgs& a, const int32_t*
   // prefix, whose "query tokens" are the batch's sequences (q_len = batch,
   // q rows [batch][Hq][D]); every column sees all prefix_tokens keys (no
   // causal mask), the keys are cut into pre_segments ranges, one per
-  // workgroup, and each workgroup leaves float32 partials.
+  // workgroup, and each workgroup leaves partials: float32 (max, sum) and
+  // the unnormalised accumulator in the output's type.
   // (a run-time value inside the prefix instantiation: folding it there
   // lets the compiler hoist more state than the registers hold)
   const bool pm = kPrefix && a.prefix_mode != 0;
@@ -555,9 +556,9 @@ __device__ __forceinline__ void prefill_body(const DecodeArgs& a, const int32_t*
       else l_tot = row_sum4(l_run[t]);
       if (col0 + 16 * t + r < NC) {
         const size_t slot = ((size_t)seg * L + qi[t]) * Hq + (size_t)g * G + qh[t];
-        float* dst = a.pre_acc + slot * D + 4 * j;
+        OutT* dst = static_cast<OutT*>(a.pre_acc) + slot * D + 4 * j;   // the output's type
 #pragma unroll
-        for (int u = 0; u < kTiles; ++u) *reinterpret_cast<f32x4*>(dst + 16 * u) = acc[t][u] * mul;
+        for (int u = 0; u < kTiles; ++u) store4<OutT>(dst + 16 * u, acc[t][u] * mul);
         if (j == 0) *reinterpret_cast<float2*>(a.pre_ml + slot * 2) = float2{m_ref[t], l_tot};
       }
     }

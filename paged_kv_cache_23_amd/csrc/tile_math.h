@@ -338,5 +338,20 @@ __device__ __forceinline__ void store4<__bf16>(__bf16* dst, f32x4 v) {
   *reinterpret_cast<bf16x4*>(dst) = o;
 }
 
+// Four consecutive elements widened to float32 (exact).
+template <typename T>
+__device__ __forceinline__ f32x4 load4(const T* src);
+template <>
+__device__ __forceinline__ f32x4 load4<float>(const float* src) {
+  return *reinterpret_cast<const f32x4*>(src);
+}
+template <>
+__device__ __forceinline__ f32x4 load4<__bf16>(const __bf16* src) {
+  typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+  const u32x2v w = *reinterpret_cast<const u32x2v*>(src);
+  return f32x4{__builtin_bit_cast(float, w[0] << 16), __builtin_bit_cast(float, w[0] & 0xFFFF0000u),
+               __builtin_bit_cast(float, w[1] << 16), __builtin_bit_cast(float, w[1] & 0xFFFF0000u)};
+}
+
 }  // namespace
 }  // namespace pkv
