@@ -50,10 +50,11 @@ __device__ __forceinline__ uint32_t e4m3_pair(float a, float b) {
 
 // x / s for the E4M3 rounding above, equal in code to the correctly rounded
 // binary32 quotient (IEEE division, then E4M3 rounding).  The quotient is
-// taken as q0 = x * r with r = 1/s correctly rounded: for a normal s and r,
-// q0 is within 1.51 * 2^-23 |x/s| of x/s, and the correctly rounded quotient
-// within 2^-24 |x/s|, so the two are at most 3 units in the last place of q0
-// apart.  Where the E4M3 rounding cannot tell them apart, q0 is used:
+// taken as q0 = x * r with r = 1/s correctly rounded: for a normal s and r
+// (and no underflow), q0 is within (2^-23 + 2^-48) |x/s| of x/s and the
+// correctly rounded quotient within 2^-24 |x/s|, so the two are within
+// 1.5 * 2^-23 |x/s|, i.e. 3 units in the last place of q0, of each other.
+// Where the E4M3 rounding cannot tell them apart, q0 is used:
 //  - |q0| < 2^-11: both round to a signed zero (below half of 2^-9);
 //  - 2^-6 <= |q0| <= 2^16: every E4M3 rounding boundary in that range (the
 //    midpoints between neighbouring codes, which keep 4 significand bits)
