@@ -38,6 +38,9 @@ def _tails(rng, B, hi):
     ("bf16", 128, 4, 37, 640, 16), ("bf16", 64, 16, 33, 1024, 16), ("bf16", 128, 1, 300, 4096, 256),
     ("bf16", 128, 8, 1, 320, 16), ("fp8", 128, 8, 20, 2000, 16), ("fp8", 64, 2, 9, 512, 32),
     ("f32", 64, 2, 9, 256, 16), ("f32", 128, 4, 70, 1024, 64),
+    # long prefixes: 128 key segments whose partial accumulators (bf16 for
+    # bf16 and fp8 caches) the merge combines
+    ("bf16", 128, 4, 8, 16384, 16), ("fp8", 128, 4, 6, 16384, 16), ("f32", 64, 2, 4, 8192, 16),
 ])
 def test_shared_parity(kv_dtype, D, G, B, P, bs):
     rng = np.random.default_rng(B * 7 + P)
