@@ -62,13 +62,13 @@ QUANT_SCALES = [1.0, 0.37, 1.0 / 448.0, 3.5e-3, 2.0 ** -20, 1e-6, 7.3e-5, 0.0123
                 2.0 ** -125, 2.0 ** -126, 2.0 ** 124, 2.0 ** 126, -0.5]
 
 
-@pytest.mark.parametrize("tokens", [512, 1024])
+@pytest.mark.parametrize("tokens,shuffled", [(512, False), (1024, False), (1024, True)])
 @pytest.mark.parametrize("scale", QUANT_SCALES)
-def test_fp8_quantiser_exhaustive(scale, tokens):
+def test_fp8_quantiser_exhaustive(scale, tokens, shuffled):
     """Every bf16 input pattern encodes to the same E4M3 code on the GPU and in
     the oracle: one kv head, 128 dims, all 65,536 patterns (twice at 1,024
-    tokens); 512 tokens run the one-wave-per-token kernel, 1,024 consecutive
-    slots the tiled one."""
+    tokens); 512 tokens run the one-wave-per-token kernel, 1,024 the tiled
+    one (consecutive slots: its run path; shuffled: its element-wise one)."""
     D, Hkv, T = 128, 1, tokens
     bits = np.resize(np.arange(65536, dtype=np.uint32).astype(np.uint16), T * D).reshape(T, Hkv, D)
     k_new = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16)
@@ -77,6 +77,8 @@ def test_fp8_quantiser_exhaustive(scale, tokens):
     k_pool = torch.zeros((NB, Hkv, 16, D), dtype=torch.uint8)
     v_pool = torch.zeros((NB, Hkv, D, 16), dtype=torch.uint8)
     slots = torch.arange(T, dtype=torch.int64)
+    if shuffled:
+        slots = slots[torch.randperm(T, generator=torch.Generator().manual_seed(5))]
     ks = torch.tensor([scale], dtype=torch.float32)
     vs = torch.tensor([scale * 2.0], dtype=torch.float32)
     d = torch.device("cuda:0")
