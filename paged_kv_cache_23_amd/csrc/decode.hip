@@ -421,7 +421,7 @@ void decode_split_kernel_wide(DecodeArgs a, const int32_t* __restrict__ tables, 
 // rescale.  Two dependent round trips: the record, then the partials.
 // ---------------------------------------------------------------------------
 template <typename OutT, int D, bool kPrefix>
-__global__ __launch_bounds__(128) void decode_merge_kernel(const int2* __restrict__ meta,
+__global__ __launch_bounds__(256) void decode_merge_kernel(const int2* __restrict__ meta,
                                                            const float* __restrict__ ws_acc,
                                                            const float* __restrict__ ws_ml, OutT* __restrict__ out,
                                                            int num_seqs, int num_kv_heads, int group, int q_len,
@@ -437,7 +437,7 @@ __global__ __launch_bounds__(128) void decode_merge_kernel(const int2* __restric
   const int g = pair - b * num_kv_heads;
   const size_t place = (size_t)g * num_seqs + b;   // the pair's place in the head-major chunk order
   const size_t Hq = (size_t)num_kv_heads * G;
-  for (int e = threadIdx.x; e < NC * (D / 4); e += 128) {
+  for (int e = threadIdx.x; e < NC * (D / 4); e += blockDim.x) {
     const int c = e / (D / 4);
     const int q4 = e % (D / 4);
     const int qi = c / G;
@@ -518,7 +518,9 @@ hipError_t launch_split_t(const DecodeArgs& a, hipStream_t stream) {
 template <typename OutT, int D, bool kPrefix>
 hipError_t launch_merge_p(const DecodeArgs& a, hipStream_t stream) {
   const unsigned grid = (unsigned)a.num_seqs * (unsigned)a.num_kv_heads;
-  hipLaunchKernelGGL((decode_merge_kernel<OutT, D, kPrefix>), dim3(grid), dim3(128), 0, stream,
+  // one thread per four output elements of the pair, up to 256
+  const unsigned threads = a.q_len * a.group * (D / 4) > 128 ? 256 : 128;
+  hipLaunchKernelGGL((decode_merge_kernel<OutT, D, kPrefix>), dim3(grid), dim3(threads), 0, stream,
                      static_cast<const int2*>(a.pair_meta), static_cast<const float*>(a.ws_acc),
                      static_cast<const float*>(a.ws_ml), static_cast<OutT*>(a.out), a.num_seqs, a.num_kv_heads,
                      a.group, a.q_len, static_cast<const OutT*>(a.pre_acc), a.pre_ml, a.pre_segments);
