@@ -94,17 +94,39 @@ def half_ulp_bf16(ref: np.ndarray) -> np.ndarray:
     return np.exp2(np.floor(np.log2(a)) - 8)
 
 
+def bounds(ref: np.ndarray, kv_dtype: str):
+    """Per-element error bound and the mask of elements given rounding slack.
+
+    The bound is the flat tolerance of the cache dtype (2e-3 f32, 1e-2 bf16,
+    3e-2 fp8).  Only where the bf16 output's own final rounding can by itself
+    reach that tolerance -- half a bf16 ulp of |ref| >= tol, i.e. |ref| >= 4
+    for 1e-2 and |ref| >= 8 for 3e-2 -- is that half ulp added: there no
+    kernel, however exact, could meet the flat bound."""
+    tol = TOL[kv_dtype]
+    if kv_dtype == "f32":
+        return np.full(ref.shape, tol), np.zeros(ref.shape, dtype=bool)
+    h = half_ulp_bf16(ref)
+    slack = h >= tol
+    return np.where(slack, tol + h, tol), slack
+
+
 def assert_close(out: torch.Tensor, ref: np.ndarray, kv_dtype: str) -> float:
-    """|got - ref| <= tolerance of the cache dtype, plus, for bf16 outputs, the
-    half ulp that the final rounding to bf16 adds at that magnitude."""
+    """|got - ref| <= the flat tolerance of the cache dtype (see ``bounds``);
+    prints how many elements needed the rounding slack.  Returns max|err|."""
     got = out_f64(out) if isinstance(out, torch.Tensor) else out
     assert np.all(np.isfinite(got)), "non-finite output"
     if ref.size == 0:
         return 0.0
     err = np.abs(got - ref)
-    bound = TOL[kv_dtype] + (0.0 if kv_dtype == "f32" else half_ulp_bf16(ref))
+    bound, slack = bounds(ref, kv_dtype)
     worst = np.unravel_index(np.argmax(err - bound), err.shape)
-    assert np.all(err <= bound), f"max|err| {err.max():.4g}; worst at {worst}: {err[worst]:.4g} > {np.broadcast_to(bound, err.shape)[worst]:.4g}"
+    n_slack = int(slack.sum())
+    over_flat = int((err > TOL[kv_dtype]).sum())
+    if n_slack:
+        print(f"assert_close[{kv_dtype}]: {n_slack} of {err.size} elements have |ref| where the output's "
+              f"rounding alone reaches the tolerance; {over_flat} of them exceed the flat bound", flush=True)
+    assert np.all(err <= bound), (f"max|err| {err.max():.4g}; worst at {worst}: {err[worst]:.4g} > "
+                                  f"{bound[worst]:.4g} (|ref| {abs(ref[worst]):.4g})")
     return float(err.max())
 
 
