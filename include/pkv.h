@@ -3,7 +3,8 @@
  *
  * Plain C ABI: device pointers, sizes and a HIP stream handle, nothing else.
  * The library allocates no memory and keeps no pointer after a call returns;
- * its only global state is a per-device cache of the compute-unit count.
+ * its only global state is a per-device cache of the compute-unit count and
+ * the static scratch buffer of pkv_paged_decode_static.
  * Every call is asynchronous on `stream` (a hipStream_t passed as void*,
  * NULL for the default stream).
  *
@@ -56,6 +57,7 @@ extern "C" {
 #define PKV_EWORKSPACE (-3)   /* workspace missing or too small */
 #define PKV_ELAUNCH (-4)      /* the HIP runtime reported an error (host: out of memory) */
 #define PKV_ENOSPACE (-5)     /* the block pool has too few free blocks */
+#define PKV_ESCRATCH (-6)     /* pkv_paged_decode_static: batch too large for the static scratch */
 
 #define PKV_BLOCK_SIZE 16   /* the default; 32, 64, 128 and 256 are supported too */
 
@@ -189,6 +191,27 @@ int pkv_paged_decode_ex(const pkv_cache_desc* desc, const void* q, const void* k
                         int32_t num_seqs, int32_t max_context_len, float scale,
                         int32_t num_workers, void* out, void* workspace,
                         size_t workspace_bytes, void* stream);
+
+/* pkv_paged_decode for callers that cannot allocate device memory at all:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  The same kernels and the default worker count, so the result
+ * is pkv_paged_decode's, bit for bit; the workspace is the library's own
+ * static device buffer of PKV_STATIC_SCRATCH_BYTES, of which every device
+ * the library runs on holds one copy until the process ends.  This call
+ * allocates and frees nothing (its first call on a device looks up that
+ * device's copy).  A batch whose workspace,
+ * pkv_decode_workspace_bytes(desc, num_seqs, max_context_len, 0), exceeds
+ * the buffer is refused with PKV_ESCRATCH before any launch.  The buffer
+ * needs no initialisation; every call on a device shares it, so calls that
+ * overlap on one device (any streams, any threads) race and must be
+ * ordered by the caller.  Other arguments, errors and clamping as for
+ * pkv_paged_decode. */
+#define PKV_STATIC_SCRATCH_BYTES (32u << 20)
+int pkv_paged_decode_static(const pkv_cache_desc* desc, const void* q, const void* k_pool,
+                            const void* v_pool, const int32_t* block_tables,
+                            int32_t max_blocks_per_seq, const int32_t* context_lens,
+                            int32_t num_seqs, int32_t max_context_len, float scale, void* out,
+                            void* stream);
 
 /* Decode over a batch whose sequences all begin with the same shared blocks
  * (parallel sampling or best-of-n over one prompt: Habr article, section 4,

@@ -13,6 +13,7 @@ namespace {
 using pkv::DecodeArgs;
 
 constexpr size_t kWsAlign = 256;
+static_assert(pkv::kStaticScratchBytes == PKV_STATIC_SCRATCH_BYTES, "static scratch size in pkv.h");
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -346,6 +347,23 @@ int pkv_paged_decode(const pkv_cache_desc* desc, const void* q, const void* k_po
                              max_context_len, scale, 0, out, workspace, ws_bytes, stream);
 }
 
+int pkv_paged_decode_static(const pkv_cache_desc* desc, const void* q, const void* k_pool, const void* v_pool,
+                            const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                            int32_t num_seqs, int32_t max_context_len, float scale, void* out, void* stream) {
+  int st = check_decode_args(desc, q, k_pool, v_pool, block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                             max_context_len, out);
+  if (st != PKV_OK) return st;
+  const int32_t w = resolve_workers(desc, num_seqs, max_context_len, 0);
+  if (w <= 0) return w == 0 ? PKV_EINVAL : w;
+  if (num_seqs == 0) return PKV_OK;
+  if (workspace_bytes(desc, num_seqs, 1, w) > pkv::kStaticScratchBytes) return PKV_ESCRATCH;
+  void* scratch = pkv::static_scratch();
+  if (!scratch) return PKV_ELAUNCH;
+  DecodeArgs a = make_args(desc, q, k_pool, v_pool, block_tables, max_blocks_per_seq, context_lens, num_seqs, 1,
+                           max_context_len, scale, w, out, scratch);
+  return launch_status(pkv::launch_decode(a, static_cast<hipStream_t>(stream)));
+}
+
 int32_t pkv_shared_prefix_pays(const pkv_cache_desc* desc, int32_t num_seqs, int32_t prefix_tokens) {
   int st = check_desc(desc);
   if (st != PKV_OK) return st;
@@ -432,6 +450,7 @@ const char* pkv_strerror(int status) {
     case PKV_EWORKSPACE: return "workspace missing or too small";
     case PKV_ELAUNCH: return "HIP launch failed";
     case PKV_ENOSPACE: return "not enough free blocks";
+    case PKV_ESCRATCH: return "the decode needs more than the library's static 32 MiB scratch buffer";
     default: return "unknown status";
   }
 }

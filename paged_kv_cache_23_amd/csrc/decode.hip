@@ -40,6 +40,8 @@
 // the context length and the partition size, never on physical block ids, so
 // permuting the pool or sharing blocks leaves the output bit-identical.
 
+#include <atomic>
+
 #include "pkv_internal.h"
 #include "tile_math.h"
 
@@ -556,6 +558,25 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   const hipError_t e = launch_split(a, stream);
   if (e != hipSuccess) return e;
   return launch_merge(a, stream);
+}
+
+// Decode workspace for callers that cannot allocate (see
+// pkv_paged_decode_static).  Each device holds its own copy for the life of
+// the process.  In host code `scratch` names a host-side stand-in, never the
+// device memory: kernels and copies get the address static_scratch() looks
+// up per device.
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
+
+void* static_scratch() {
+  static std::atomic<void*> addr[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  void* p = addr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  // first call on this device, with it current: resolve this device's copy
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+  addr[dev].store(p, std::memory_order_release);
+  return p;
 }
 
 }  // namespace pkv

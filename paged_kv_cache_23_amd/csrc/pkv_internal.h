@@ -96,6 +96,11 @@ int prefill_group_cols(int kv_dtype);
 hipError_t launch_split(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_merge(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
+// The library's static decode workspace: kStaticScratchBytes of device memory
+// per device, at the address static_scratch() returns for the current device
+// (nullptr if the runtime cannot resolve it).
+constexpr size_t kStaticScratchBytes = size_t(32) << 20;
+void* static_scratch();
 hipError_t launch_copy(const CopyArgs& a, hipStream_t stream);
 size_t copy_slice_bytes();
 

@@ -65,6 +65,7 @@ def library() -> ctypes.CDLL:
             "pkv_decode_workspace_bytes": (SZ, [D, I32, I32, I32]),
             "pkv_paged_decode": (ctypes.c_int, [D, P, P, P, P, I32, P, I32, I32, F, P, P, SZ, P]),
             "pkv_paged_decode_ex": (ctypes.c_int, [D, P, P, P, P, I32, P, I32, I32, F, I32, P, P, SZ, P]),
+            "pkv_paged_decode_static": (ctypes.c_int, [D, P, P, P, P, I32, P, I32, I32, F, P, P]),
             "pkv_paged_attention": (ctypes.c_int, [D, P, P, P, P, I32, P, I32, I32, I32, F, I32, P, P, SZ, P]),
             "pkv_attention_workspace_bytes": (SZ, [D, I32, I32, I32, I32]),
             "pkv_shared_decode_workspace_bytes": (SZ, [D, I32, I32, I32, I32]),
@@ -293,6 +294,26 @@ def paged_decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
                                    block_tables.shape[1], _ptr(context_lens), q.shape[0], mctx, float(scale),
                                    int(num_workers), _ptr(out), _ptr(workspace), wbytes, _stream(stream)),
            "pkv_paged_decode_ex")
+    return out
+
+
+STATIC_SCRATCH_BYTES = 32 << 20   # the library's static decode workspace per device
+
+
+def paged_decode_static(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                        block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
+                        out: torch.Tensor, k_scale: Optional[torch.Tensor] = None,
+                        v_scale: Optional[torch.Tensor] = None, max_context_len: Optional[int] = None,
+                        stream=None, reread: bool = False) -> torch.Tensor:
+    """``paged_decode`` that allocates nothing: the caller passes ``out`` and the
+    library uses its own static device workspace (``STATIC_SCRATCH_BYTES`` per
+    device; larger batches raise).  Calls that overlap on one device race."""
+    desc, out = _decode_checks(q, k_pool, v_pool, block_tables, context_lens, k_scale, v_scale, out, reread)
+    mctx = _max_ctx(block_tables, max_context_len, k_pool.shape[2])
+    _check(library().pkv_paged_decode_static(ctypes.byref(desc), _ptr(q), _ptr(k_pool), _ptr(v_pool),
+                                             _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),
+                                             q.shape[0], mctx, float(scale), _ptr(out), _stream(stream)),
+           "pkv_paged_decode_static")
     return out
 
 

@@ -195,3 +195,16 @@ def test_strerror_and_version():
     assert b"workspace" in lib.pkv_strerror(EWORKSPACE)
     assert lib.pkv_strerror(12345) == b"unknown status"
     assert b"gfx950" in lib.pkv_version()
+
+
+def test_static_decode_checks_arguments_before_any_hip_call():
+    """pkv_paged_decode_static: the decode's argument checks, on the host."""
+    lib = ops.library()
+    d = _desc()
+    assert lib.pkv_paged_decode_static(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 64, 0.1,
+                                       None, None) == EINVAL      # no output
+    assert lib.pkv_paged_decode_static(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 0, FAKE, 2, 64, 0.1,
+                                       FAKE, None) == EINVAL      # no table columns
+    assert lib.pkv_paged_decode_static(ctypes.byref(_desc(head_dim=96)), FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 64,
+                                       0.1, FAKE, None) == EUNSUPPORTED
+    assert lib.pkv_strerror(-6).decode().startswith("the decode needs more")
