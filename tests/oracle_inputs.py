@@ -79,3 +79,29 @@ def relayout(wl: Workload, block_size: int, seed: int, poison: bool = True):
         k2[dst_blk, :, dst_off, :] = k_rows
         v2[dst_blk, :, :, dst_off] = v_rows
     return k2, v2, torch.from_numpy(t2)
+
+
+def onehot_v_pool(v_pool, block_tables, context_lens, one):
+    """A V pool whose value row at token position t of every sequence is the
+    unit vector e_d with d = (t // 32) mod head_dim, for every kv head (test-
+    side data; the G-5 read-out).  Attention then returns, in dimension d,
+    the total softmax weight of the 32-token chunks of class d, so a chunk
+    dropped or counted twice shows up in its class.  ``one`` is the stored
+    value 1 (1.0, or the E4M3 code 0x38 for an fp8 pool with unit scales).
+    Works on the tensors' own device; other slots hold 0."""
+    import torch
+
+    D, bs = v_pool.shape[2], v_pool.shape[3]
+    dev = v_pool.device
+    lens = context_lens.to(torch.int64).cpu()
+    tables = block_tables.to(dev).to(torch.int64)
+    v = torch.zeros_like(v_pool)
+    B = lens.shape[0]
+    for b in range(B):
+        n = int(lens[b])
+        if n == 0:
+            continue
+        t = torch.arange(n, device=dev)
+        phys = tables[b][t // bs]
+        v[phys, :, (t // 32) % D, t % bs] = one
+    return v
