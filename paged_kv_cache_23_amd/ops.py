@@ -218,6 +218,19 @@ def new_workspace(nbytes: int, device) -> torch.Tensor:
     return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
 
 
+def _temp_workspace(nbytes: int, device, stream) -> torch.Tensor:
+    """Scratch for one call.  It is freed when the call returns, while the
+    kernels may still be queued, so it is allocated on the stream they run
+    on: torch's caching allocator then reuses it only for later work on that
+    same stream, which runs after them."""
+    if stream is None:
+        return new_workspace(nbytes, device)
+    if not isinstance(stream, torch.cuda.Stream):
+        stream = torch.cuda.ExternalStream(int(getattr(stream, "cuda_stream", stream)), device=device)
+    with torch.cuda.stream(stream):
+        return new_workspace(nbytes, device)
+
+
 def attention_workspace_bytes(k_pool, v_pool, num_q_heads: int, num_seqs: int, q_len: int,
                               max_context_len: int, num_workers: int = 0, k_scale=None, v_scale=None) -> int:
     desc = cache_desc(k_pool, v_pool, num_q_heads, k_scale, v_scale)
@@ -253,7 +266,7 @@ def paged_attention(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
     if need == 0 and B > 0:
         _check(-2 if L * (Hq // desc.num_kv_heads) > 1 << 24 else -1, "pkv_attention_workspace_bytes")
     if workspace is None:
-        workspace = new_workspace(need, q.device)
+        workspace = _temp_workspace(need, q.device, stream)
     wbytes = workspace.numel() * workspace.element_size()
     if workspace.device.type != "cuda" or wbytes < need:
         raise ValueError(f"workspace must be a device buffer of at least {need} bytes")
@@ -286,7 +299,7 @@ def paged_decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
     if need == 0 and q.shape[0] > 0:
         _check(-1, "pkv_decode_workspace_bytes")
     if workspace is None:
-        workspace = new_workspace(need, q.device)
+        workspace = _temp_workspace(need, q.device, stream)
     wbytes = workspace.numel() * workspace.element_size()
     if workspace.device.type != "cuda" or wbytes < need:
         raise ValueError(f"workspace must be a device buffer of at least {need} bytes")
@@ -354,7 +367,7 @@ def paged_decode_shared(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Ten
     if need == 0:
         _check(-1, "pkv_shared_decode_workspace_bytes")
     if workspace is None:
-        workspace = new_workspace(need, q.device)
+        workspace = _temp_workspace(need, q.device, stream)
     wbytes = workspace.numel() * workspace.element_size()
     if workspace.device.type != "cuda" or wbytes < need:
         raise ValueError(f"workspace must be a device buffer of at least {need} bytes")
