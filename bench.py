@@ -269,36 +269,117 @@ def check_against_oracle(runner, got, sample_seqs: int = 4) -> float:
     return float(np.max(np.abs(rows - ref)))
 
 
-def cpu_baseline(wl, min_seconds: float = 10.0, max_reps: int = 20):
-    """The oracle, as it stands, on this host: the whole decode step of the
-    workload (every sequence and kv head), repeated until min_seconds."""
+def host_cores() -> int:
+    """Host cores the oracle leg runs on: this process's CPU affinity, at most
+    16 (one GPU's share of the machine's cores)."""
+    return max(1, min(len(os.sched_getaffinity(0)), 16))
+
+
+_POOL_INPUTS = None
+
+
+def _oracle_pool_init(folder: str, meta: dict) -> None:
+    """Oracle worker start: one BLAS thread, the inputs memory-mapped read-only."""
+    global _POOL_INPUTS
     import numpy as np
     from threadpoolctl import threadpool_limits
 
+    threadpool_limits(1)
+    arrays = {name: np.load(os.path.join(folder, name + ".npy"), mmap_mode="r") for name in meta["arrays"]}
+    _POOL_INPUTS = (arrays, meta)
+
+
+def _oracle_ready(_) -> int:
+    return os.getpid()
+
+
+def _oracle_pairs_task(pairs):
+    """oracle_decode_pairs, as it stands, over some (sequence, kv head) pairs."""
     import oracle
+
+    a, m = _POOL_INPUTS
+    return oracle.oracle_decode_pairs(a["q"], m["q_dtype"], a["k_pool"], a["v_pool"], m["kv_dtype"], a["tables"],
+                                      a["lens"], m["scale"], pairs, a.get("k_scale"), a.get("v_scale"))
+
+
+def _oracle_rows_task(rows):
+    """oracle_attention_multi, as it stands, over query rows [lo, hi) of one
+    chunk (they see the first n - L + hi tokens)."""
+    import oracle
+
+    a, m = _POOL_INPUTS
+    lo, hi = rows
+    return oracle.oracle_attention_multi(a["q"][:, lo:hi], m["q_dtype"], a["k_pool"], a["v_pool"], m["kv_dtype"],
+                                         a["tables"], [m["n"] - m["L"] + hi], m["scale"], a.get("k_scale"),
+                                         a.get("v_scale"))
+
+
+class OraclePool:
+    """The oracle on the host's cores: spawned worker processes (they never
+    touch the GPU), each with one BLAS thread, sharing the inputs through
+    memory-mapped files; tasks are handed out one at a time, longest first."""
+
+    def __init__(self, arrays: dict, meta: dict, workers: int):
+        import multiprocessing
+        import tempfile
+
+        import numpy as np
+
+        self._dir = tempfile.TemporaryDirectory(prefix="pkv_oracle_")
+        names = []
+        for name, arr in arrays.items():
+            if arr is not None:
+                np.save(os.path.join(self._dir.name, name + ".npy"), np.ascontiguousarray(arr))
+                names.append(name)
+        self.workers = workers
+        ctx = multiprocessing.get_context("spawn")
+        self._pool = ctx.Pool(workers, initializer=_oracle_pool_init,
+                              initargs=(self._dir.name, dict(meta, arrays=names)))
+        self._pool.map(_oracle_ready, range(workers), chunksize=1)
+
+    def map(self, fn, tasks):
+        return self._pool.map(fn, tasks, chunksize=1)
+
+    def close(self) -> None:
+        self._pool.close()
+        self._pool.join()
+        self._dir.cleanup()
+
+
+def cpu_baseline(wl, min_seconds: float = 10.0, max_reps: int = 400):
+    """The oracle, as it stands, on this host's cores: whole decode steps of
+    the workload (every sequence and kv head; the (sequence, kv head) pairs
+    shared out over a process pool), repeated until min_seconds."""
     from paged_kv_cache_23_amd.workloads import storage_numpy
 
-    q, kp, vp = storage_numpy(wl.q), storage_numpy(wl.k_pool), storage_numpy(wl.v_pool)
-    ks = None if wl.k_scale is None else wl.k_scale.numpy()
-    vs = None if wl.v_scale is None else wl.v_scale.numpy()
-    tables, lens = wl.block_tables.numpy(), wl.context_lens.numpy()
-    reps, t0 = 0, time.perf_counter()
-    with threadpool_limits(1):
+    lens = wl.context_lens.numpy()
+    pool = OraclePool(dict(q=storage_numpy(wl.q), k_pool=storage_numpy(wl.k_pool), v_pool=storage_numpy(wl.v_pool),
+                           tables=wl.block_tables.numpy(), lens=lens,
+                           k_scale=None if wl.k_scale is None else wl.k_scale.numpy(),
+                           v_scale=None if wl.v_scale is None else wl.v_scale.numpy()),
+                      dict(q_dtype=wl.q_dtype, kv_dtype=wl.kv_dtype, scale=wl.scale), host_cores())
+    try:
+        pairs = sorted(((b, g) for b in range(wl.batch) for g in range(wl.num_kv_heads)), key=lambda p: -lens[p[0]])
+        tasks = [[p] for p in pairs]
+        pool.map(_oracle_pairs_task, tasks)          # first pass: page the inputs in
+        reps, t0 = 0, time.perf_counter()
         while reps < max_reps:
-            oracle.oracle_decode(q, wl.q_dtype, kp, vp, wl.kv_dtype, tables, lens, wl.scale, ks, vs)
+            pool.map(_oracle_pairs_task, tasks)
             reps += 1
             if time.perf_counter() - t0 >= min_seconds:
                 break
-    sec = (time.perf_counter() - t0) / reps
+        sec = (time.perf_counter() - t0) / reps
+    finally:
+        pool.close()
     return {
         "value": round(wl.kv_bytes() / sec / 1e9, 4),
         "unit": "GB/s",
-        "cores": 1,
+        "cores": pool.workers,
         "kind": "oracle",
-        "sample": f"whole {wl.name} decode step (all {wl.batch} sequences x {wl.num_kv_heads} kv heads, "
-                  f"{wl.kv_bytes() / 1e6:.0f} MB of KV) in fp64 NumPy on one host thread, "
-                  f"{reps} repetitions, {sec:.2f} s each",
-        "seconds_per_step": round(sec, 3),
+        "sample": f"whole {wl.name} decode steps (all {wl.batch} sequences x {wl.num_kv_heads} kv heads, "
+                  f"{wl.kv_bytes() / 1e6:.0f} MB of KV) in fp64 NumPy, the pairs shared out over "
+                  f"{pool.workers} host processes of one thread each, {reps} repetitions, {sec:.3f} s each",
+        "seconds_per_step": round(sec, 4),
         "decode_tokens_per_s": round(wl.batch / sec, 2),
     }
 
@@ -800,35 +881,39 @@ def _scales(wl):
 
 
 def prefill_cpu_baseline(runner, min_seconds: float):
-    """The oracle on this host over a bounded sample: the first query rows of
-    the last chunk (each sees about 8,200 tokens), rows added until
-    min_seconds; reported as TFLOP/s of the same causal flop count."""
-    from threadpoolctl import threadpool_limits
-
-    import oracle
+    """The oracle on this host's cores over a bounded sample: the query rows of
+    the last chunk (each sees about 8,200 tokens), four rows per task over a
+    process pool, rows added until min_seconds; reported as TFLOP/s of the
+    same causal flop count."""
     from paged_kv_cache_23_amd.workloads import storage_numpy
 
     wl, s = runner.wl, runner.steps[-1]
-    kp, vp = storage_numpy(wl.k_pool), storage_numpy(wl.v_pool)
-    q = storage_numpy(s.q)
     L, n = s.q.shape[1], runner.n[-1]
-    done, flops, t0 = 0, 0, time.perf_counter()
-    with threadpool_limits(1):
+    ks, vs = _scales(wl)
+    pool = OraclePool(dict(q=storage_numpy(s.q), k_pool=storage_numpy(wl.k_pool), v_pool=storage_numpy(wl.v_pool),
+                           tables=wl.block_tables.numpy(), k_scale=ks, v_scale=vs),
+                      dict(q_dtype=wl.q_dtype, kv_dtype=wl.kv_dtype, scale=wl.scale, n=n, L=L), host_cores())
+    try:
+        rows = 4
+        pool.map(_oracle_rows_task, [(i * rows, (i + 1) * rows) for i in range(pool.workers)])   # page in
+        done, flops, t0 = 0, 0, time.perf_counter()
         while done < L and time.perf_counter() - t0 < min_seconds:
-            rows = min(8, L - done)
-            lens = [n - L + done + rows]
-            oracle.oracle_attention_multi(q[:, done:done + rows], wl.q_dtype, kp, vp, wl.kv_dtype,
-                                          wl.block_tables.numpy(), lens, wl.scale, *_scales(wl))
-            flops += sum(4 * wl.num_q_heads * wl.head_dim * (n - L + 1 + i) for i in range(done, done + rows))
-            done += rows
-    sec = time.perf_counter() - t0
+            batch = [(lo, min(L, lo + rows)) for lo in range(done, min(L, done + rows * pool.workers), rows)]
+            pool.map(_oracle_rows_task, batch)
+            hi = batch[-1][1]
+            flops += sum(4 * wl.num_q_heads * wl.head_dim * (n - L + 1 + i) for i in range(done, hi))
+            done = hi
+        sec = time.perf_counter() - t0
+    finally:
+        pool.close()
     return {
         "value": round(flops / sec / 1e12, 6),
         "unit": "TFLOP/s",
-        "cores": 1,
+        "cores": pool.workers,
         "kind": "oracle",
         "sample": f"first {done} query rows of the last chunk (n = {n}, {wl.num_q_heads} q heads) through "
-                  f"oracle_attention_multi in fp64 NumPy on one host thread, {sec:.1f} s",
+                  f"oracle_attention_multi in fp64 NumPy, {rows} rows per task over {pool.workers} host "
+                  f"processes of one thread each, {sec:.1f} s",
     }
 
 

@@ -64,3 +64,37 @@ def test_committed_traffic_rejects_a_changed_source(tmp_path, monkeypatch):
     h = bench.kernel_source_hash(bench.APPEND_SOURCES)
     (tmp_path / "append_kernel_x_hbm_traffic.txt").write_text(text.replace("0123456789abcdef", h))
     assert bench.committed_traffic("x", "append_kernel", bench.APPEND_SOURCES) == 1000.0
+
+
+def test_oracle_pool_gives_the_oracles_results():
+    """The bench's oracle leg runs the oracle unchanged on several host
+    processes: what they return equals the oracle called directly."""
+    import numpy as np
+
+    import bench
+    import oracle
+    from paged_kv_cache_23_amd.workloads import build_workload, storage_numpy
+
+    wl = build_workload("pool", [5, 40, 100], 8, 2, 64, "fp8", seed=3)
+    args = dict(q=storage_numpy(wl.q), k_pool=storage_numpy(wl.k_pool), v_pool=storage_numpy(wl.v_pool),
+                tables=wl.block_tables.numpy(), lens=wl.context_lens.numpy(), k_scale=wl.k_scale.numpy(),
+                v_scale=wl.v_scale.numpy())
+    pool = bench.OraclePool(args, dict(q_dtype="bf16", kv_dtype="fp8", scale=wl.scale), 2)
+    try:
+        pairs = [(b, g) for b in range(3) for g in range(2)]
+        got = np.concatenate(pool.map(bench._oracle_pairs_task, [[p] for p in pairs]))
+    finally:
+        pool.close()
+    ref = oracle.oracle_decode_pairs(args["q"], "bf16", args["k_pool"], args["v_pool"], "fp8", args["tables"],
+                                     args["lens"], wl.scale, pairs, args["k_scale"], args["v_scale"])
+    assert np.array_equal(got, ref)
+
+
+def test_cpu_baseline_reports_the_cores_it_used():
+    import bench
+    from paged_kv_cache_23_amd.workloads import build_workload
+
+    wl = build_workload("cores", [64, 300], 8, 2, 64, "bf16", seed=4)
+    res = bench.cpu_baseline(wl, min_seconds=0.2, max_reps=3)
+    assert res["cores"] == bench.host_cores() >= 1
+    assert res["value"] > 0 and res["kind"] == "oracle"
