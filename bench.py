@@ -17,6 +17,8 @@ Extra modes:
   --profile-one   warm up, then launch the decode a few times (for rocprofv3)
   --copy-probe    run a plain device-to-device copy of known size (calibrates
                   the FETCH_SIZE / WRITE_SIZE counters)
+  --tile-probe    the read-stream ceiling: whole tiles read at random positions
+                  of a 4 GiB buffer with no arithmetic (libpkv_probe.so)
   --cow           time the copy-on-write block copy and a parallel-sampling step
   --prefill       time chunked prefill: a 10,000-token prompt in chunks of at
                   most 2048 tokens on one Llama-3-70B-shaped layer (TFLOP/s
@@ -555,6 +557,68 @@ def copy_probe(args) -> None:
     log(f"copied {n} bytes {args.steps} times")
 
 
+def tile_probe(args) -> dict:
+    """The read-stream ceiling: libpkv_probe.so reads whole tiles at random
+    positions of a 4 GiB buffer (the decode's access pattern with no
+    arithmetic; the decode reads one 4 KiB (bf16) or 2 KiB (fp8) tile per
+    (block, kv head) for K and one for V), over tile sizes, KiB in flight per
+    wave, ordinary and non-temporal loads and one or two waves per SIMD; also
+    the same tiles read in order.  Each line: GB/s over 10 launches timed with
+    HIP events on the launch stream."""
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_23_amd.build import PROBE_PATH
+
+    lib = ctypes.CDLL(PROBE_PATH)
+    P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    lib.pkv_probe_read_tiles.restype = ctypes.c_int
+    lib.pkv_probe_read_tiles.argtypes = [P, SZ, P, I64, I32, I32, I32, I32, P, P]
+    nbytes = 4 << 30
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda:0")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.empty(4 * cus * 2 * 64, dtype=torch.int32, device="cuda:0")
+    s = torch.cuda.current_stream()
+    rng = np.random.default_rng(0)
+    rows = []
+    for tile_kib in args.probe_tiles:
+        n = nbytes // (tile_kib << 10)
+        ids = {"random": torch.from_numpy(rng.permutation(n).astype(np.int32)).cuda(),
+               "in order": torch.arange(n, dtype=torch.int32, device="cuda:0")}
+        for order, t in ids.items():
+            for waves_per_simd in (1, 2):
+                for kib in (4, 8, 16, 32):
+                    for nt in (1, 0):
+                        if order == "in order" and (kib != 16 or waves_per_simd != 1):
+                            continue
+                        waves = 4 * cus * waves_per_simd
+
+                        def launch():
+                            st = lib.pkv_probe_read_tiles(buf.data_ptr(), nbytes, t.data_ptr(), n, tile_kib, kib,
+                                                          waves, nt, sink.data_ptr(), ctypes.c_void_p(s.cuda_stream))
+                            if st != 0:
+                                raise RuntimeError(f"pkv_probe_read_tiles: status {st}")
+                        for _ in range(2):
+                            launch()
+                        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                        e0.record(s)
+                        for _ in range(10):
+                            launch()
+                        e1.record(s)
+                        torch.cuda.synchronize()
+                        us = e0.elapsed_time(e1) / 10 * 1e3
+                        rows.append({"tile_kib": tile_kib, "order": order, "waves_per_simd": waves_per_simd,
+                                     "kib_in_flight_per_wave": kib, "loads": "non-temporal" if nt else "cached",
+                                     "us": round(us, 1), "GB/s": round(nbytes / us / 1e3, 1)})
+                        log(f"tiles {tile_kib} KiB {order:8s} {waves_per_simd} wave/SIMD {kib:2d} KiB in flight "
+                            f"{'nt ' if nt else 'ord'}: {nbytes / us / 1e3:8.1f} GB/s")
+    best = max((r for r in rows if r["order"] == "random"), key=lambda r: r["GB/s"])
+    return {"metric": "random-tile read stream (probe, no arithmetic)", "value": best["GB/s"], "unit": "GB/s",
+            "n_gpus": 1, "higher_is_better": True, "data": "synthetic",
+            "config": {"workload": "4 GiB buffer read once per launch as whole tiles in a random permutation",
+                       "best": best}, "rows": rows}
+
+
 def cow_bench(args) -> dict:
     """Copy-on-write: pkv_copy_blocks at the parallel-sampling shape (8 samples
     of a 2005-token prompt: one shared 5-token block copied per sample, 32 KiB
@@ -1038,6 +1102,10 @@ def main() -> int:
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--profile-one", action="store_true")
     p.add_argument("--copy-probe", action="store_true")
+    p.add_argument("--tile-probe", action="store_true",
+                   help="measure the random-tile read ceiling with the probe library instead")
+    p.add_argument("--probe-tiles", type=int, nargs="+", default=[1, 2, 4, 8],
+                   help="tile sizes (KiB) for --tile-probe")
     p.add_argument("--cow", action="store_true", help="time the copy-on-write block copy instead")
     p.add_argument("--block-size", type=int, default=16, help="tokens per cache block (16, 32, 64, 128, 256)")
     p.add_argument("--reread", choices=["auto", "on", "off"], default="auto",
@@ -1058,6 +1126,9 @@ def main() -> int:
         return 2
     if args.copy_probe:
         copy_probe(args)
+        return 0
+    if args.tile_probe:
+        print(json.dumps(tile_probe(args)), flush=True)
         return 0
     if args.prefill and args.profile_one:
         prefill_profile(args)

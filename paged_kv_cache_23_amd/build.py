@@ -17,6 +17,9 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB_PATH = os.path.join(HERE, "libpkv.so")
 SOURCES = ["api.hip", "append.hip", "copy.hip", "decode.hip", "prefill.hip", "prefix_cache.cpp"]
+# the read-stream ceiling probe that bench.py --tile-probe times (not part of the attention library)
+PROBE_PATH = os.path.join(HERE, "libpkv_probe.so")
+PROBE_SOURCES = ["probe.hip"]
 
 HIP_FLAGS = [
     "--offload-arch=gfx950",
@@ -38,12 +41,11 @@ def hipcc() -> str:
     return exe
 
 
-def build(verbose: bool = False, extra_flags=None) -> str:
-    """Compile every source and return the library path."""
-    tmp = LIB_PATH + ".tmp"
+def _compile(sources, out: str, verbose: bool, extra_flags) -> str:
+    tmp = out + ".tmp"
     cmd = [hipcc(), *HIP_FLAGS, *(extra_flags or []),
            "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-           *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
+           *[os.path.join(CSRC, s) for s in sources], "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -54,8 +56,14 @@ def build(verbose: bool = False, extra_flags=None) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{msgs}")
     if verbose and msgs.strip():
         print(msgs, flush=True)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, out)
+    return out
+
+
+def build(verbose: bool = False, extra_flags=None) -> str:
+    """Compile every source (the library and the read-stream probe); return the library path."""
+    _compile(PROBE_SOURCES, PROBE_PATH, verbose, extra_flags)
+    return _compile(SOURCES, LIB_PATH, verbose, extra_flags)
 
 
 if __name__ == "__main__":

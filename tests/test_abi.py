@@ -208,3 +208,24 @@ def test_static_decode_checks_arguments_before_any_hip_call():
     assert lib.pkv_paged_decode_static(ctypes.byref(_desc(head_dim=96)), FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 64,
                                        0.1, FAKE, None) == EUNSUPPORTED
     assert lib.pkv_strerror(-6).decode().startswith("the decode needs more")
+
+
+def test_probe_library_exports_its_entry_point_and_checks_arguments():
+    """libpkv_probe.so (the read-stream ceiling probe bench.py --tile-probe
+    times) exports what include/pkv_probe.h declares and rejects bad
+    arguments before any launch."""
+    from paged_kv_cache_23_amd.build import PROBE_PATH
+
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "pkv_probe.h")).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(pkv_[a-z_0-9]+)\s*\(", text)))
+    assert names == ["pkv_probe_read_tiles"]
+    lib = ctypes.CDLL(PROBE_PATH)
+    fn = lib.pkv_probe_read_tiles
+    P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    fn.restype, fn.argtypes = ctypes.c_int, [P, SZ, P, I64, I32, I32, I32, I32, P, P]
+    ok = dict(buf=FAKE, nbytes=1 << 20, ids=FAKE, n=4, kib=4, inflight=16, waves=8, nt=1, sink=FAKE)
+    for bad in (dict(buf=None), dict(kib=3), dict(kib=128), dict(inflight=12), dict(waves=6), dict(n=0),
+                dict(nbytes=1024), dict(sink=None)):
+        a = dict(ok, **bad)
+        assert fn(a["buf"], a["nbytes"], a["ids"], a["n"], a["kib"], a["inflight"], a["waves"], a["nt"],
+                  a["sink"], None) == -1, bad
