@@ -307,6 +307,13 @@ int32_t pkv_pool_allocate(pkv_block_pool* pool, int32_t count, int32_t* blocks_o
 int32_t pkv_pool_cache_blocks(pkv_block_pool* pool, const int32_t* tokens, int32_t num_tokens,
                               uint64_t extra_key, const int32_t* blocks, int32_t num_blocks);
 
+/* Add one reference to each listed block: another sequence now shares it
+ * (a fork for parallel sampling or beam search: Habr article, section 4,
+ * "Copy-on-Write for parallel sampling", where the variants point at the
+ * prompt's blocks and each block counts its references).  Every listed
+ * block must already be referenced (else PKV_EINVAL and nothing changes). */
+int pkv_pool_ref(pkv_block_pool* pool, const int32_t* blocks, int32_t num_blocks);
+
 /* Drop one reference from each listed block (a request finished).  Blocks
  * reaching zero join the tail of the LRU queue, the request's last block
  * first, so that a chain's tail is evicted before its head; they stay in the

@@ -333,6 +333,14 @@ int32_t pkv_pool_cache_blocks(pkv_block_pool* pool, const int32_t* tokens, int32
   return added;
 }
 
+int pkv_pool_ref(pkv_block_pool* pool, const int32_t* blocks, int32_t num_blocks) {
+  if (!pool || num_blocks < 0 || (num_blocks > 0 && !blocks)) return PKV_EINVAL;
+  for (int32_t j = 0; j < num_blocks; ++j)
+    if (!valid_block(pool, blocks[j]) || pool->ref[blocks[j]] == 0) return PKV_EINVAL;
+  for (int32_t j = 0; j < num_blocks; ++j) ++pool->ref[blocks[j]];
+  return PKV_OK;
+}
+
 int pkv_pool_free(pkv_block_pool* pool, const int32_t* blocks, int32_t num_blocks) {
   if (!pool || num_blocks < 0 || (num_blocks > 0 && !blocks)) return PKV_EINVAL;
   try {   // every id valid and referenced at least as often as it is listed
