@@ -189,6 +189,7 @@ int32_t prefix_segments(const pkv_cache_desc* d, int32_t num_seqs, int32_t prefi
   const int64_t cols = (int64_t)num_seqs * (d->num_q_heads / d->num_kv_heads);
   const int64_t gc = pkv::prefill_group_cols(d->kv_dtype);
   const int64_t groups = (cols + gc - 1) / gc * d->num_kv_heads;
+  if (groups == 0) return 1;   // no sequences: one (empty) segment
   const int64_t chunks = ((int64_t)prefix_tokens + pkv::kChunkTokens - 1) / pkv::kChunkTokens;
   int64_t s = (kSegGroupsPerCu * cus + groups - 1) / groups;
   const int64_t cap = chunks / kMinSegChunks;
