@@ -397,10 +397,12 @@ __device__ __forceinline__ void split_body(const DecodeArgs& a, const int32_t* _
 
 // Tables, lengths and scales are passed again as restrict parameters: nothing
 // the kernel writes aliases them, so their wave-uniform reads go through the
-// scalar cache and never wait behind the vector loads in flight.  Two waves
-// per SIMD (at most 256 VGPRs each) are resident together; the float32 path at
-// head_dim 128 needs more registers for its double buffer and runs one wave
-// per SIMD instead of spilling.
+// scalar cache and never wait behind the vector loads in flight.  Registers
+// are capped at 256 per wave (two waves per SIMD would fit), although the
+// default launch runs one worker wave per SIMD (1024 waves on 256 compute
+// units): a second wave per SIMD measured slower.  The float32 path at
+// head_dim 128 needs more registers for its double buffer and is built for
+// one wave per SIMD instead of spilling.
 template <int KV, int D, bool KNT, bool VNT, bool kTail>
 __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void decode_split_kernel(DecodeArgs a, const int32_t* __restrict__ tables, const int32_t* __restrict__ lens,
