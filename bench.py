@@ -52,7 +52,8 @@ def log(msg: str) -> None:
 
 
 COPY_SOURCES = ["paged_kv_cache_23_amd/csrc/copy.hip", "paged_kv_cache_23_amd/csrc/pkv_internal.h"]
-APPEND_SOURCES = ["paged_kv_cache_23_amd/csrc/append.hip", "paged_kv_cache_23_amd/csrc/pkv_internal.h"]
+APPEND_SOURCES = ["paged_kv_cache_23_amd/csrc/append.hip", "paged_kv_cache_23_amd/csrc/pkv_internal.h",
+                  "paged_kv_cache_23_amd/csrc/e4m3.h"]
 PREFILL_SOURCES = ["paged_kv_cache_23_amd/csrc/prefill.hip", "paged_kv_cache_23_amd/csrc/tile_math.h",
                    "paged_kv_cache_23_amd/csrc/pkv_internal.h"]
 

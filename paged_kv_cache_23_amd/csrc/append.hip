@@ -13,6 +13,7 @@
 // rounded to E4M3, with the result of the IEEE division followed by E4M3
 // rounding (below).
 
+#include "e4m3.h"
 #include "pkv_internal.h"
 
 namespace pkv {
@@ -31,22 +32,6 @@ template <>
 struct Vec16<uint32_t> {
   typedef uint32_t type __attribute__((ext_vector_type(4)));
 };
-
-// float32 -> OCP E4M3FN codes of two values (low byte: a): round to
-// nearest, ties to even; |x| >= 448 (infinities included) saturates to
-// +-448; NaN gives the NaN code with the input's sign.  gfx950's
-// v_cvt_pk_fp8_f32 rounds to nearest even but does not saturate, so it is
-// given the values clamped to [-448, 448] by v_med3_f32; the clamp turns a
-// NaN into a number, so NaN codes are put back afterwards.  (Over all 2^32
-// binary32 inputs this agrees with rounding the binary32 fields directly,
-// checked on MI355X.)
-__device__ __forceinline__ uint32_t e4m3_pair(float a, float b) {
-  uint32_t w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(a, -448.f, 448.f),
-                                                         __builtin_amdgcn_fmed3f(b, -448.f, 448.f), 0, false);
-  if (a != a) w = (w & 0xFF00u) | ((__builtin_bit_cast(uint32_t, a) >> 24) & 0x80u) | 0x7Fu;
-  if (b != b) w = (w & 0x00FFu) | ((((__builtin_bit_cast(uint32_t, b) >> 24) & 0x80u) | 0x7Fu) << 8);
-  return w & 0xFFFFu;
-}
 
 // x / s for the E4M3 rounding above, equal in code to the correctly rounded
 // binary32 quotient (IEEE division, then E4M3 rounding).  The quotient is

@@ -1,13 +1,17 @@
-// Read-stream ceiling probe (not part of the attention path; bench.py
-// --tile-probe times it).  It measures how fast HBM serves the paged
+// Measurement and check kernels beside the attention library (not part of
+// its path).  (1) The read-stream ceiling probe (bench.py --tile-probe times
+// it).  It measures how fast HBM serves the paged
 // decode's access pattern with no arithmetic: whole tiles of a few KiB read
 // at random positions of a large buffer, 16 bytes per lane, a set number of
 // KiB in flight per wave.  The decode reads one such tile per (block, kv
-// head) for K and one for V.
+// head) for K and one for V.  (2) A check of the float32 -> E4M3 conversion
+// the append kernels use (e4m3.h) on every binary32 input, and that
+// conversion on a caller's array, for comparison with the CPU oracle.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "e4m3.h"
 #include "pkv_probe.h"
 
 namespace {
@@ -86,6 +90,57 @@ hipError_t launch_nt(const uint8_t* buf, const uint32_t* ids, int64_t pieces, in
   return hipGetLastError();
 }
 
+// OCP E4M3FN rounding of a binary32 value written out from the format in
+// integer arithmetic: sign kept; NaN -> 0x7F; magnitudes >= 448 (infinities
+// included) -> 448 (0x7E); otherwise the nearest multiple, ties to even, of
+// the spacing 2^(E - 3) of the value's binade E (E = -6 for everything
+// below 2^-6: the subnormal grid), code (E + 7) * 8 + steps - 8, so a
+// round-up across a binade edge lands on the next exponent's first code.
+__device__ __forceinline__ uint32_t e4m3_fields(uint32_t x) {
+  const uint32_t s = (x >> 24) & 0x80u;
+  const uint32_t a = x & 0x7FFFFFFFu;
+  if (a > 0x7F800000u) return s | 0x7Fu;     // NaN
+  if (a >= 0x43E00000u) return s | 0x7Eu;    // 448 = 1.75 * 2^8 and above
+  const int ef = (int)(a >> 23);
+  const uint64_t m = (a & 0x7FFFFFu) | (ef ? 0x800000u : 0u);   // value = m * 2^(e - 23)
+  const int e = ef ? ef - 127 : -126;
+  const int bin = e < -6 ? -6 : e;
+  const int sh = 20 + bin - e;               // steps = m / 2^sh (>= 20)
+  uint64_t q = 0;
+  if (sh <= 40) {                            // else the value is below 2^-17 spacings: 0
+    q = m >> sh;
+    const uint64_t rem = m & ((uint64_t(1) << sh) - 1), half = uint64_t(1) << (sh - 1);
+    if (rem > half || (rem == half && (q & 1))) ++q;
+  }
+  return s | (uint32_t)((bin + 7) * 8 + (int)q - 8);
+}
+
+// Every input x in [first, first + count) (as binary32 bit patterns) through
+// e4m3_pair in both halves of the pair against e4m3_fields; mismatches are
+// counted, and the smallest mismatching x kept.
+__global__ __launch_bounds__(256) void e4m3_check_kernel(uint64_t first, uint64_t count,
+                                                         unsigned long long* __restrict__ bad,
+                                                         uint32_t* __restrict__ first_bad) {
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += stride) {
+    const uint32_t x = (uint32_t)(first + i);
+    const float f = __builtin_bit_cast(float, x);
+    const uint32_t want = e4m3_fields(x);
+    const uint32_t lo = pkv::e4m3_pair(f, 0.f) & 0xFFu;
+    const uint32_t hi = (pkv::e4m3_pair(0.f, f) >> 8) & 0xFFu;
+    if (lo != want || hi != want) {
+      atomicAdd(bad, 1ull);
+      atomicMin(first_bad, x);
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void e4m3_encode_kernel(const float* __restrict__ in, uint8_t* __restrict__ out,
+                                                          int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) out[i] = (uint8_t)(pkv::e4m3_pair(in[i], 0.f) & 0xFFu);
+}
+
 }  // namespace
 
 extern "C" {
@@ -107,6 +162,25 @@ int pkv_probe_read_tiles(const void* buf, size_t buf_bytes, const uint32_t* tile
   const hipError_t e = nontemporal ? launch_nt<true>(b, tile_ids, pieces, tile_shift, buf_tiles, per, kib_in_flight, grid, sink, s)
                                    : launch_nt<false>(b, tile_ids, pieces, tile_shift, buf_tiles, per, kib_in_flight, grid, sink, s);
   return e == hipSuccess ? 0 : -4;
+}
+
+int pkv_probe_e4m3_check(uint64_t first, uint64_t count, unsigned long long* mismatches, uint32_t* first_mismatch,
+                         void* stream) {
+  if (!mismatches || !first_mismatch || count == 0 || count > (uint64_t(1) << 32) ||
+      first + count > (uint64_t(1) << 32))
+    return -1;
+  hipLaunchKernelGGL(e4m3_check_kernel, dim3(8192), dim3(256), 0, static_cast<hipStream_t>(stream), first, count,
+                     mismatches, first_mismatch);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+int pkv_probe_e4m3_encode(const float* in, uint8_t* out, int64_t n, void* stream) {
+  if (!in || !out || n <= 0 || n > (int64_t(1) << 40)) return -1;
+  const int64_t grid = (n + 255) / 256;
+  if (grid > 0x7FFFFFFF) return -1;
+  hipLaunchKernelGGL(e4m3_encode_kernel, dim3((unsigned)grid), dim3(256), 0, static_cast<hipStream_t>(stream), in,
+                     out, n);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
 }  // extern "C"

@@ -210,6 +210,21 @@ def test_static_decode_checks_arguments_before_any_hip_call():
     assert lib.pkv_strerror(-6).decode().startswith("the decode needs more")
 
 
+def test_probe_e4m3_calls_check_arguments():
+    from paged_kv_cache_23_amd.build import PROBE_PATH
+
+    lib = ctypes.CDLL(PROBE_PATH)
+    P = ctypes.c_void_p
+    chk, enc = lib.pkv_probe_e4m3_check, lib.pkv_probe_e4m3_encode
+    chk.restype, chk.argtypes = ctypes.c_int, [ctypes.c_uint64, ctypes.c_uint64, P, P, P]
+    enc.restype, enc.argtypes = ctypes.c_int, [P, P, ctypes.c_int64, P]
+    assert chk(0, 16, None, FAKE, None) == -1
+    assert chk(0, 0, FAKE, FAKE, None) == -1
+    assert chk(1, 1 << 32, FAKE, FAKE, None) == -1          # past 2^32
+    assert chk((1 << 32) - 4, 8, FAKE, FAKE, None) == -1
+    assert enc(None, FAKE, 4, None) == -1 and enc(FAKE, FAKE, 0, None) == -1
+
+
 def test_probe_library_exports_its_entry_point_and_checks_arguments():
     """libpkv_probe.so (the read-stream ceiling probe bench.py --tile-probe
     times) exports what include/pkv_probe.h declares and rejects bad
@@ -218,7 +233,7 @@ def test_probe_library_exports_its_entry_point_and_checks_arguments():
 
     text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "pkv_probe.h")).read(), flags=re.S)
     names = sorted(set(re.findall(r"\b(pkv_[a-z_0-9]+)\s*\(", text)))
-    assert names == ["pkv_probe_read_tiles"]
+    assert names == ["pkv_probe_e4m3_check", "pkv_probe_e4m3_encode", "pkv_probe_read_tiles"]
     lib = ctypes.CDLL(PROBE_PATH)
     fn = lib.pkv_probe_read_tiles
     P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
