@@ -204,6 +204,36 @@ int32_t prefix_segments(const pkv_cache_desc* d, int32_t num_seqs, int32_t prefi
 // the output's type (the merge's other inputs are float32; the prefix
 // partials are the bulk of what it reads), then float32 (max, sum) pairs
 // [S][B*Hq][2].
+// One-launch shared-prefix decode (the tail walk and the prefix part share
+// every SIMD): taken when the tails alone give every SIMD a tail wave and the
+// cache is bf16; otherwise the prefix pass runs on the prefill kernel before
+// the tail walk.
+bool shared_one_launch(const pkv_cache_desc* d, int32_t workers) {
+  if (d->kv_dtype != PKV_BF16) return false;
+  const int cus = device_cus();
+  return cus > 0 && workers == (int64_t)cus * 4 * pkv::kWavesPerSimd;
+}
+
+// Key segments of the shared-prefix decode for `workers` tail waves.  In one
+// launch: about one (kv head, workgroup's column groups, segment) item per
+// workgroup (workers / 4 of them), at least kMinSegChunks chunks per
+// segment, none empty.
+int32_t shared_segments(const pkv_cache_desc* d, int32_t num_seqs, int32_t prefix_tokens, int32_t workers) {
+  if (!shared_one_launch(d, workers)) return prefix_segments(d, num_seqs, prefix_tokens);
+  const int64_t cols = (int64_t)num_seqs * (d->num_q_heads / d->num_kv_heads);
+  const int64_t gc = pkv::shared_workgroup_cols(d->head_dim);
+  const int64_t groups = (cols + gc - 1) / gc * d->num_kv_heads;
+  if (groups == 0) return 1;   // no sequences: one (empty) segment
+  const int64_t chunks = ((int64_t)prefix_tokens + pkv::kChunkTokens - 1) / pkv::kChunkTokens;
+  int64_t s = workers / pkv::kDecodeWaves / groups;
+  const int64_t cap = chunks / kMinSegChunks;
+  if (s > cap) s = cap;
+  if (s > 1024) s = 1024;
+  if (s < 1) s = 1;
+  const int64_t per = (chunks + s - 1) / s;   // the kernel's chunks per segment
+  return (int32_t)((chunks + per - 1) / per);
+}
+
 size_t prefix_acc_bytes(const pkv_cache_desc* d, int32_t num_seqs, int32_t segments) {
   const size_t elt = d->kv_dtype == PKV_F32 ? 4 : 2;
   return align_up((size_t)segments * num_seqs * d->num_q_heads * d->head_dim * elt);
@@ -381,7 +411,7 @@ size_t pkv_shared_decode_workspace_bytes(const pkv_cache_desc* desc, int32_t num
   if (prefix_tokens % desc->block_size != 0 || prefix_tokens > max_context_len) return 0;
   const int32_t w = resolve_workers(desc, num_seqs, tail_ctx(max_context_len, prefix_tokens), num_workers);
   if (w <= 0) return 0;
-  const int32_t s = prefix_tokens > 0 ? prefix_segments(desc, num_seqs, prefix_tokens) : 0;
+  const int32_t s = prefix_tokens > 0 ? shared_segments(desc, num_seqs, prefix_tokens, w) : 0;
   if (s < 0) return 0;
   return workspace_bytes(desc, num_seqs, 1, w) + prefix_acc_bytes(desc, num_seqs, s) +
          prefix_ml_bytes(desc, num_seqs, s);
@@ -403,7 +433,7 @@ int pkv_paged_decode_shared(const pkv_cache_desc* desc, const void* q, const voi
   const int32_t w = resolve_workers(desc, num_seqs, tctx, num_workers);
   if (w <= 0) return w == 0 ? PKV_EINVAL : w;
   if (num_seqs == 0) return PKV_OK;
-  const int32_t segs = prefix_segments(desc, num_seqs, prefix_tokens);
+  const int32_t segs = shared_segments(desc, num_seqs, prefix_tokens, w);
   if (segs < 0) return segs;
   const size_t dec = workspace_bytes(desc, num_seqs, 1, w);
   if (!workspace || ws_bytes < dec + prefix_acc_bytes(desc, num_seqs, segs) + prefix_ml_bytes(desc, num_seqs, segs))
@@ -413,6 +443,22 @@ int pkv_paged_decode_shared(const pkv_cache_desc* desc, const void* q, const voi
   void* pre_acc = ws + dec;
   float* pre_ml = reinterpret_cast<float*>(ws + dec + prefix_acc_bytes(desc, num_seqs, segs));
   hipStream_t s = static_cast<hipStream_t>(stream);
+  const int32_t pblocks = prefix_tokens / desc->block_size;
+
+  if (shared_one_launch(desc, w)) {
+    // the tail walk (every sequence's tokens after the prefix, all as
+    // partials) and the prefix part in one launch, then the merge
+    DecodeArgs ta = make_args(desc, q, k_pool, v_pool, block_tables + pblocks, max_blocks_per_seq, context_lens,
+                              num_seqs, 1, max_context_len, scale, w, out, workspace);
+    ta.table_offset = pblocks;
+    ta.tail_pass = 1;
+    ta.prefix_tokens = prefix_tokens;
+    ta.pre_segments = segs;
+    ta.pre_acc = pre_acc;
+    ta.pre_ml = pre_ml;
+    if (pkv::launch_shared(ta, s) != hipSuccess) return PKV_ELAUNCH;
+    return launch_status(pkv::launch_merge(ta, s));
+  }
 
   // 1. the prefix for every sequence at once: one virtual sequence whose
   //    query tokens are the batch's sequences, over row 0's prefix blocks
@@ -429,7 +475,6 @@ int pkv_paged_decode_shared(const pkv_cache_desc* desc, const void* q, const voi
   // 2. every sequence's own tokens after the prefix, all as partials
   //    (each row read from its first block after the prefix; the row stride
   //    stays max_blocks_per_seq)
-  const int32_t pblocks = prefix_tokens / desc->block_size;
   DecodeArgs ta = make_args(desc, q, k_pool, v_pool, block_tables + pblocks, max_blocks_per_seq, context_lens,
                             num_seqs, 1, max_context_len, scale, w, out, workspace);
   ta.table_offset = pblocks;

@@ -12,6 +12,10 @@ constexpr int kChunkTokens = 32;    // tokens one wave consumes per step: two bl
 constexpr int kDecodeWaves = 4;     // worker waves per decode workgroup
 constexpr int kMaxGroup = 16;       // query heads per kv head that one MFMA column tile holds
 constexpr int kWavesPerSimd = 1;    // worker waves per SIMD: a second one mostly waits on the first
+// Prefix columns one wave of the one-launch shared-prefix decode owns (two
+// 16-column MFMA tiles), and one workgroup's four prefix waves together.
+constexpr int shared_group_cols(int) { return 32; }
+constexpr int shared_workgroup_cols(int head_dim) { return 4 * shared_group_cols(head_dim); }
 
 enum KvType : int32_t { kF32 = 0, kBF16 = 1, kFP8 = 2 };
 
@@ -95,6 +99,11 @@ int prefill_group_cols(int kv_dtype);
 // prefix pass between them).
 hipError_t launch_split(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_merge(const DecodeArgs& a, hipStream_t stream);
+// Shared-prefix decode, tail walk and prefix part in one launch (bf16
+// caches): num_workers / 4 eight-wave workgroups; the prefix partials go to
+// pre_acc / pre_ml in pre_segments key segments per column.  The merge
+// kernel then finishes every pair.
+hipError_t launch_shared(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
 // The library's static decode workspace: kStaticScratchBytes of device memory
 // per device, at the address static_scratch() returns for the current device

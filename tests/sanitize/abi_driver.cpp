@@ -38,6 +38,7 @@ hipError_t hipDeviceGetAttribute(int* value, hipDeviceAttribute_t, int) {
 namespace {
 const char* g_ws = nullptr;   // the workspace the current call was given
 size_t g_ws_bytes = 0;
+int g_shared_one_launch = 0;   // shared-prefix calls that took the one-launch path
 int g_launches = 0;
 
 struct Region {
@@ -91,6 +92,14 @@ hipError_t launch_split(const DecodeArgs& a, hipStream_t) {
   CHECK(a.tail_pass == 1);
   check_decode_workspace(a);
   ++g_launches;
+  return hipSuccess;
+}
+hipError_t launch_shared(const DecodeArgs& a, hipStream_t) {
+  CHECK(a.tail_pass == 1 && a.prefix_tokens > 0 && a.pre_segments >= 1);
+  CHECK(a.kv_dtype != kF32);
+  check_decode_workspace(a);   // the prefix partials included
+  ++g_launches;
+  ++g_shared_one_launch;
   return hipSuccess;
 }
 hipError_t launch_merge(const DecodeArgs& a, hipStream_t) {
@@ -212,6 +221,7 @@ int main() {
     }
   }
   CHECK(g_launches > 3000);
+  CHECK(g_shared_one_launch > 0);
   // block pool handles: created and destroyed
   pkv_block_pool* p = pkv_pool_create(8, 16);
   CHECK(p != nullptr);

@@ -26,6 +26,12 @@ def _shared(dev: Dev, prefix_tokens: int, max_context_len=None, workers=0, works
                                    num_workers=workers, workspace=workspace)
 
 
+def _one_launch_workers() -> int:
+    """One tail wave per SIMD: with a bf16 or fp8 cache the call then runs the
+    tail walk and the prefix part in one launch."""
+    return 4 * torch.cuda.get_device_properties(0).multi_processor_count
+
+
 def _tails(rng, B, hi):
     """Tail lengths after the prefix: empty, 1, one chunk's edges, the rest random."""
     fixed = [0, 1, 31, 32, 33, 100]
@@ -41,14 +47,18 @@ def _tails(rng, B, hi):
     # long prefixes: 128 key segments whose partial accumulators (bf16 for
     # bf16 and fp8 caches) the merge combines
     ("bf16", 128, 4, 8, 16384, 16), ("fp8", 128, 4, 6, 16384, 16), ("f32", 64, 2, 4, 8192, 16),
+    # prefixes that end half way into a 32-token chunk (1040 = 32.5 chunks)
+    ("bf16", 128, 4, 24, 1040, 16), ("bf16", 64, 8, 40, 528, 16),
 ])
-def test_shared_parity(kv_dtype, D, G, B, P, bs):
+@pytest.mark.parametrize("one_launch", [False, True])
+def test_shared_parity(kv_dtype, D, G, B, P, bs, one_launch):
     rng = np.random.default_rng(B * 7 + P)
     lens = [P + t for t in _tails(rng, B, 300)]
     wl = build_workload("shared", lens, 2 * G, 2, D, kv_dtype, seed=B + P, shared_prefix=P, rng=rng,
                         block_size=bs)
-    print(f"shared {kv_dtype} D={D} G={G} B={B} P={P} bs={bs}", flush=True)
-    out = _shared(Dev(wl), P)
+    workers = _one_launch_workers() if one_launch else 0
+    print(f"shared {kv_dtype} D={D} G={G} B={B} P={P} bs={bs} workers={workers}", flush=True)
+    out = _shared(Dev(wl), P, workers=workers)
     assert out.shape == wl.q.shape
     assert_close(out, oracle_full(wl), kv_dtype)
 
@@ -64,6 +74,7 @@ def test_any_block_aligned_part_of_the_shared_prefix():
     ref = oracle_full(wl)
     for p in (0, 16, 400, 784, 800):
         assert_close(_shared(dev, p), ref, "bf16")
+        assert_close(_shared(dev, p, workers=_one_launch_workers()), ref, "bf16")
 
 
 def test_every_tail_empty():
@@ -71,7 +82,26 @@ def test_every_tail_empty():
     pass alone."""
     P = 1024
     wl = build_workload("shared", [P] * 12, 32, 8, 128, "bf16", seed=6, shared_prefix=P)
-    assert_close(_shared(Dev(wl), P), oracle_full(wl), "bf16")
+    dev = Dev(wl)
+    ref = oracle_full(wl)
+    assert_close(_shared(dev, P), ref, "bf16")
+    assert_close(_shared(dev, P, workers=_one_launch_workers()), ref, "bf16")
+
+
+@pytest.mark.parametrize("scale", [-0.07, 0.0])
+def test_scale_signs(scale):
+    """A negative score scale (the prefix part flips the queries' signs
+    instead) and a zero one (every visible token weighs the same), on both
+    paths."""
+    rng = np.random.default_rng(12)
+    P = 528
+    wl = build_workload("shared", [P + t for t in _tails(rng, 30, 200)], 32, 8, 128, "bf16", seed=12,
+                        shared_prefix=P, rng=rng)
+    wl = dataclasses.replace(wl, scale=scale)
+    dev = Dev(wl)
+    ref = oracle_full(wl)
+    for workers in (0, _one_launch_workers()):
+        assert_close(_shared(dev, P, workers=workers), ref, "bf16")
 
 
 def test_worker_counts_and_a_reused_workspace():
@@ -82,9 +112,11 @@ def test_worker_counts_and_a_reused_workspace():
     dev = Dev(wl)
     ref = oracle_full(wl)
     mctx = int(wl.context_lens.max())
-    need = max(ops.shared_decode_workspace_bytes(dev.k_pool, dev.v_pool, 32, 40, mctx, P, w) for w in (4, 64, 1024))
+    full = _one_launch_workers()
+    counts = (4, 64, 1024, full, 4)
+    need = max(ops.shared_decode_workspace_bytes(dev.k_pool, dev.v_pool, 32, 40, mctx, P, w) for w in counts)
     ws = ops.new_workspace(need, dev.q.device)
-    for w in (4, 64, 1024, 4):   # partials of the earlier calls stay behind
+    for w in counts:             # partials of the earlier calls stay behind
         for p in (P, 0):         # the plain decode (no prefix) shares the workspace too
             assert_close(_shared(dev, p, workers=w, workspace=ws), ref, "bf16")
 
@@ -120,16 +152,25 @@ def test_shared_prefix_256_all_outputs():
     output of the shared-prefix call against the oracle."""
     wl = W.shared_prefix_256()
     print("shared-prefix-256 through the shared-prefix call", flush=True)
-    out = _shared(Dev(wl), 4096)
-    err = assert_close(out, oracle_full(wl), "bf16")
-    print(f"shared-prefix-256 (shared call) max|err| = {err:.3g}")
+    dev = Dev(wl)
+    ref = oracle_full(wl)
+    full = _one_launch_workers()
+    # the default (one launch: the tails give every SIMD a wave), then the
+    # three-launch path (one tail wave fewer per workgroup's worth)
+    for workers in (0, full - 4):
+        err = assert_close(_shared(dev, 4096, workers=workers), ref, "bf16")
+        print(f"shared-prefix-256 (shared call, workers={workers}) max|err| = {err:.3g}")
 
 
 def test_best_of_8_all_outputs():
-    """Best-of-8 over a 2,000-token prompt (125 shared blocks)."""
+    """Best-of-8 over a 2,000-token prompt (125 shared blocks), with the
+    library's worker count and in one launch."""
     wl = W.best_of_8()
-    err = assert_close(_shared(Dev(wl), 2000), oracle_full(wl), "bf16")
-    print(f"best-of-8 (shared call) max|err| = {err:.3g}")
+    dev = Dev(wl)
+    ref = oracle_full(wl)
+    for workers in (0, _one_launch_workers()):
+        err = assert_close(_shared(dev, 2000, workers=workers), ref, "bf16")
+        print(f"best-of-8 (shared call, workers={workers}) max|err| = {err:.3g}")
 
 
 def test_policy_picks_either_path_with_the_same_result():
