@@ -43,8 +43,12 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0
 METRIC = "paged decode KV GB/s read (% of HBM peak) + decode tokens/s, 8B-shape b64"
 PROFILE_DIR = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = ["paged_kv_cache_23_amd/csrc/decode.hip", "paged_kv_cache_23_amd/csrc/tile_math.h",
-                  "paged_kv_cache_23_amd/csrc/pkv_internal.h"]
+KERNEL_SOURCES = ["paged_kv_cache_23_amd/csrc/decode.hip", "paged_kv_cache_23_amd/csrc/split_body.h",
+                  "paged_kv_cache_23_amd/csrc/tile_math.h", "paged_kv_cache_23_amd/csrc/pkv_internal.h"]
+# the shared-prefix call: bf16 caches run the one-launch kernel, other dtypes
+# the prefill kernel's prefix pass; both end with the decode's merge kernel
+SHARED_SOURCES = {"bf16": KERNEL_SOURCES + ["paged_kv_cache_23_amd/csrc/shared.hip"],
+                  "other": KERNEL_SOURCES + ["paged_kv_cache_23_amd/csrc/prefill.hip"]}
 
 
 def log(msg: str) -> None:
@@ -471,8 +475,9 @@ def run_bench(args) -> dict:
     # prefix once plus every tail
     algo = unique if prefix else runner.kv_bytes
     kern_gbs = algo / (part_ms.mean() * 1e-3) / 1e9
-    traffic = (committed_traffic(wl.name, "paged_decode_shared", KERNEL_SOURCES + PREFILL_SOURCES[:1]) if prefix
-               else committed_traffic(wl.name))
+    one_launch = wl.kv_dtype == "bf16"
+    traffic = (committed_traffic(wl.name, "paged_decode_shared", SHARED_SOURCES["bf16" if one_launch else "other"])
+               if prefix else committed_traffic(wl.name))
     result = {
         "metric": METRIC,
         "value": round(gbs, 2),
@@ -504,8 +509,10 @@ def run_bench(args) -> dict:
         "query_tokens_per_seq": args.q_len,
         "max_abs_err_sampled": None,
         "roofline": {
-            "kernel": ("pkv_paged_decode_shared (prefill_kernel over the prefix + decode_split_kernel + "
-                       "decode_merge_kernel)" if prefix else
+            "kernel": (("pkv_paged_decode_shared (decode_shared_kernel: tail walk and prefix waves in one "
+                        "launch; decode_merge_kernel)" if one_launch else
+                        "pkv_paged_decode_shared (prefill_kernel over the prefix + decode_split_kernel + "
+                        "decode_merge_kernel)") if prefix else
                        "pkv_paged_decode (decode_split_kernel + decode_merge_kernel)"),
             "bound": "hbm",
             "achieved": round(kern_gbs, 2),

@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB_PATH = os.path.join(HERE, "libpkv.so")
-SOURCES = ["api.hip", "append.hip", "copy.hip", "decode.hip", "prefill.hip", "prefix_cache.cpp"]
+SOURCES = ["api.hip", "append.hip", "copy.hip", "decode.hip", "prefill.hip", "shared.hip", "prefix_cache.cpp"]
 # the read-stream ceiling probe that bench.py --tile-probe times (not part of the attention library)
 PROBE_PATH = os.path.join(HERE, "libpkv_probe.so")
 PROBE_SOURCES = ["probe.hip"]
