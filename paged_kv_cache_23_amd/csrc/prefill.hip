@@ -408,16 +408,22 @@ __device__ __forceinline__ void prefill_body(const DecodeArgs& a, const int32_t*
   // from below) and the running sum: a register for float32, an MFMA
   // accumulator (four equal copies) for bf16 weights.
   constexpr bool kMfmaSum = KV != kF32;
+  // thr: the largest raw score (q . k, before the scale) that keeps a
+  // weight within kRescaleSlack of the reference, (m_ref + slack) / sl; a
+  // lane whose scores all stay at or below it needs no cross-lane maximum.
+  // neg_m: minus the reference the exponentials use (0 for a column that
+  // has seen no token, so its weights are 0, never NaN).
   f32x4 acc[kT][kTiles];
   f32x4 lsum[kT];
-  float m_ref[kT], m_ref_next[kT], l_run[kT];
+  float m_ref[kT], thr[kT], neg_m[kT], l_run[kT];
 #pragma unroll
   for (int t = 0; t < kT; ++t) {
 #pragma unroll
     for (int u = 0; u < kTiles; ++u) acc[t][u] = f32x4{0.f, 0.f, 0.f, 0.f};
     lsum[t] = f32x4{0.f, 0.f, 0.f, 0.f};
     m_ref[t] = -INFINITY;
-    m_ref_next[t] = -INFINITY;
+    thr[t] = -INFINITY;
+    neg_m[t] = 0.f;
     l_run[t] = 0.f;
   }
 
@@ -444,8 +450,7 @@ __device__ __forceinline__ void prefill_body(const DecodeArgs& a, const int32_t*
     if (more) lds_k<C::kLds, D>(kf, lds_kt[nbuf], r, j);
     float s[kT][8];   // raw scores q . k; scaled inside the exponent
     int nvalid[kT];
-    bool raise[kT];
-    bool any = false;
+    bool over = false;
 #pragma unroll
     for (int t = 0; t < kT; ++t) {
 #pragma unroll
@@ -461,38 +466,40 @@ __device__ __forceinline__ void prefill_body(const DecodeArgs& a, const int32_t*
       }
       // Scores here are finite or -inf: rows past a sequence's end (which
       // may hold NaN) only occur in masked chunks, where they are -inf.
-      float mraw = fmax_nq(fmax_nq(fmax_nq(s[t][0], s[t][1]), fmax_nq(s[t][2], s[t][3])),
-                           fmax_nq(fmax_nq(s[t][4], s[t][5]), fmax_nq(s[t][6], s[t][7])));
-      mraw = row_max4_nq(mraw);
-      const float mloc = mraw == -INFINITY ? -INFINITY : mraw * sl;   // sl >= 0
-      // Raise the reference only when this chunk's max passes it by more
-      // than the slack (the first chunk with a visible token always does).
-      raise[t] = mloc > m_ref[t] + kRescaleSlack;
-      any |= raise[t];
-      if (raise[t]) m_ref_next[t] = mloc;
+      const float lmax = fmax_nq(fmax_nq(fmax_nq(s[t][0], s[t][1]), fmax_nq(s[t][2], s[t][3])),
+                                 fmax_nq(fmax_nq(s[t][4], s[t][5]), fmax_nq(s[t][6], s[t][7])));
+      over |= lmax > thr[t];
     }
-    if (__builtin_amdgcn_ballot_w64(any)) {
+    // Rare: some lane's scores passed its column's threshold.  Only then are
+    // the column maxima formed across the four lanes of each column, and the
+    // reference raised where a column's max passes it by more than the slack
+    // (the first chunk with a visible token always does).
+    if (__builtin_amdgcn_ballot_w64(over)) {
 #pragma unroll
       for (int t = 0; t < kT; ++t) {
-        // Lanes that keep their reference use factor 1 (never exp2(-inf - -inf)
-        // for a column that has seen nothing); a first raise gives exp2(-inf) = 0.
-        const float corr = raise[t] ? exp2_fast(m_ref[t] - m_ref_next[t]) : 1.f;
+        float mraw = fmax_nq(fmax_nq(fmax_nq(s[t][0], s[t][1]), fmax_nq(s[t][2], s[t][3])),
+                             fmax_nq(fmax_nq(s[t][4], s[t][5]), fmax_nq(s[t][6], s[t][7])));
+        mraw = row_max4_nq(mraw);
+        const float mloc = mraw == -INFINITY ? -INFINITY : mraw * sl;   // sl >= 0
+        if (mloc > m_ref[t] + kRescaleSlack) {
+          // a column's first raise gives factor exp2(-inf) = 0 (nothing to keep)
+          const float corr = exp2_fast(m_ref[t] - mloc);
 #pragma unroll
-        for (int u = 0; u < kTiles; ++u) acc[t][u] *= corr;
-        if constexpr (kMfmaSum) lsum[t] *= corr;
-        else l_run[t] *= corr;
-        m_ref[t] = m_ref_next[t];
+          for (int u = 0; u < kTiles; ++u) acc[t][u] *= corr;
+          if constexpr (kMfmaSum) lsum[t] *= corr;
+          else l_run[t] *= corr;
+          m_ref[t] = mloc;
+          thr[t] = (mloc + kRescaleSlack) / sl;   // +inf when sl == 0: never raised again
+          neg_m[t] = -mloc;
+        }
       }
     }
 #pragma unroll
     for (int t = 0; t < kT; ++t) {
-      // A column that has seen no token keeps -inf and is exponentiated
-      // against 0, so its weights are 0, never NaN.
-      const float m_use = m_ref[t] == -INFINITY ? 0.f : m_ref[t];
       float pk[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        pk[k] = exp2_fast(fmaf(s[t][k], sl, -m_use));
+        pk[k] = exp2_fast(fmaf(s[t][k], sl, neg_m[t]));
         if constexpr (kMask) pk[k] = k < nvalid[t] ? pk[k] : 0.f;   // also when sl == 0
       }
       if constexpr (kMfmaSum) {

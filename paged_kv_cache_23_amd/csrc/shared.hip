@@ -244,17 +244,22 @@ __device__ __forceinline__ void prefix_waves_body(const DecodeArgs& a, const int
     // equal copies) and the reference max m_ref of the exponentials (log2
     // units), raised only when a column's max passes it by more than
     // kSharedSlack, so weights stay below 2^kSharedSlack and most chunks
-    // skip the rescale.
+    // skip the rescale.  thr is the largest raw score (before the scale)
+    // that stays within the slack, (m_ref + slack) / sl: a lane whose scores
+    // all stay at or below it needs no cross-lane maximum.  neg_m is minus
+    // the reference the exponentials use (0 before a column's first token).
     constexpr float kSharedSlack = 8.f;
     f32x4 acc[kT][kTiles];
     f32x4 lsum[kT];
-    float m_ref[kT];
+    float m_ref[kT], thr[kT], neg_m[kT];
 #pragma unroll
     for (int t = 0; t < kT; ++t) {
 #pragma unroll
       for (int u = 0; u < kTiles; ++u) acc[t][u] = f32x4{0.f, 0.f, 0.f, 0.f};
       lsum[t] = f32x4{0.f, 0.f, 0.f, 0.f};
       m_ref[t] = -INFINITY;
+      thr[t] = -INFINITY;
+      neg_m[t] = 0.f;
     }
     const bf16x8 ones = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f,
                          (__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f};
@@ -285,33 +290,52 @@ __device__ __forceinline__ void prefix_waves_body(const DecodeArgs& a, const int
       f32x4 sx[kT], sy[kT];
 #pragma unroll
       for (int t = 0; t < kT; ++t) T::scores(kb, qop[t], sx[t], sy[t]);
+      float sc[kT][8];
+      bool over = false;
 #pragma unroll
       for (int t = 0; t < kT; ++t) {
-        float sc[8] = {sx[t][0], sx[t][1], sx[t][2], sx[t][3], sy[t][0], sy[t][1], sy[t][2], sy[t][3]};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          sc[t][k] = sx[t][k];
+          sc[t][k + 4] = sy[t][k];
+        }
         if (cut) {
 #pragma unroll
           for (int k = 0; k < 8; ++k)
-            if (k >= nvalid) sc[k] = -INFINITY;
+            if (k >= nvalid) sc[t][k] = -INFINITY;
         }
         // raw scores are finite or -inf; the scale (>= 0) applies after the max
-        float mraw = fmax_nq(fmax_nq(fmax_nq(sc[0], sc[1]), fmax_nq(sc[2], sc[3])),
-                             fmax_nq(fmax_nq(sc[4], sc[5]), fmax_nq(sc[6], sc[7])));
-        mraw = row_max4_nq(mraw);
-        const float mloc = mraw == -INFINITY ? -INFINITY : mraw * sl;
-        const bool raise = mloc > m_ref[t] + kSharedSlack;
-        if (__builtin_amdgcn_ballot_w64(raise)) {
-          // a column's first raise gives factor exp2(-inf) = 0 (nothing to keep)
-          const float corr = raise ? exp2_fast(m_ref[t] - mloc) : 1.f;
+        const float lmax = fmax_nq(fmax_nq(fmax_nq(sc[t][0], sc[t][1]), fmax_nq(sc[t][2], sc[t][3])),
+                                   fmax_nq(fmax_nq(sc[t][4], sc[t][5]), fmax_nq(sc[t][6], sc[t][7])));
+        over |= lmax > thr[t];
+      }
+      // rare: some lane passed its column's threshold; only then the column
+      // maxima across lanes, and a raise where one passes the slack
+      if (__builtin_amdgcn_ballot_w64(over)) {
 #pragma unroll
-          for (int u = 0; u < kTiles; ++u) acc[t][u] *= corr;
-          lsum[t] *= corr;
-          if (raise) m_ref[t] = mloc;
+        for (int t = 0; t < kT; ++t) {
+          float mraw = fmax_nq(fmax_nq(fmax_nq(sc[t][0], sc[t][1]), fmax_nq(sc[t][2], sc[t][3])),
+                               fmax_nq(fmax_nq(sc[t][4], sc[t][5]), fmax_nq(sc[t][6], sc[t][7])));
+          mraw = row_max4_nq(mraw);
+          const float mloc = mraw == -INFINITY ? -INFINITY : mraw * sl;
+          if (mloc > m_ref[t] + kSharedSlack) {
+            // a column's first raise gives factor exp2(-inf) = 0 (nothing to keep)
+            const float corr = exp2_fast(m_ref[t] - mloc);
+#pragma unroll
+            for (int u = 0; u < kTiles; ++u) acc[t][u] *= corr;
+            lsum[t] *= corr;
+            m_ref[t] = mloc;
+            thr[t] = (mloc + kSharedSlack) / sl;   // +inf when sl == 0: never raised again
+            neg_m[t] = -mloc;
+          }
         }
-        const float m_use = m_ref[t] == -INFINITY ? 0.f : m_ref[t];
+      }
+#pragma unroll
+      for (int t = 0; t < kT; ++t) {
         bf16x8 pb;
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-          float pk = exp2_fast(fmaf(sc[k], sl, -m_use));
+          float pk = exp2_fast(fmaf(sc[t][k], sl, neg_m[t]));
           if (cut) pk = k < nvalid ? pk : 0.f;   // also when sl == 0
           pb[k] = (__bf16)pk;
         }
