@@ -313,8 +313,11 @@ __device__ __forceinline__ void prefill_body(const DecodeArgs& a, const int32_t*
   const int bshift = a.block_shift;
   const int32_t* table = tables + (size_t)b * a.max_blocks;
   const int last_blk = ((n + bs - 1) >> bshift) - 1;
-  const char* kpool = static_cast<const char*>(a.k_pool);
-  const char* vpool = static_cast<const char*>(a.v_pool);
+  // A block of either pool holds Hkv tiles of bs x D elements (the pools
+  // share the layout); kbase / vbase: this pair's kv head in block 0.
+  const uint32_t blk_bytes = (uint32_t)Hkv * (uint32_t)bs * (uint32_t)(D * C::kPs);
+  const char* kbase = static_cast<const char*>(a.k_pool) + (size_t)g * bs * D * C::kPs;
+  const char* vbase = static_cast<const char*>(a.v_pool) + (size_t)g * bs * D * C::kPs;
   constexpr int KR = C::kKRowPieces;
   constexpr int VH = C::kVRowPieces / 2;
   constexpr int kPs = C::kPs;   // pool element bytes
@@ -356,15 +359,19 @@ __device__ __forceinline__ void prefill_body(const DecodeArgs& a, const int32_t*
     const int t0 = (c_begin + c) * kChunkTokens;
     // Blocks holding the chunk's two 16-token halves, and where each half
     // starts in its block's K tile and V tile (wave-uniform).
-    const int i0 = min(max(table[min(t0 >> bshift, last_blk)], 0), a.num_blocks - 1);
-    const int i1 = min(max(table[min((t0 + 16) >> bshift, last_blk)], 0), a.num_blocks - 1);
-    const int off0 = t0 & (bs - 1);
-    const int off1 = (t0 + 16) & (bs - 1);
-    const size_t tile0 = ((size_t)i0 * Hkv + g) * bs * D, tile1 = ((size_t)i1 * Hkv + g) * bs * D;
-    const char* kb0 = kpool + (tile0 + (size_t)off0 * D) * kPs;
-    const char* kb1 = kpool + (tile1 + (size_t)off1 * D) * kPs;
-    const char* vb0 = vpool + (tile0 + off0) * kPs;
-    const char* vb1 = vpool + (tile1 + off1) * kPs;
+    // Both table reads are issued before either is used; one 32 x 32-bit
+    // product per block gives its offset in both pools.
+    const int raw0 = table[min(t0 >> bshift, last_blk)];
+    const int raw1 = table[min((t0 + 16) >> bshift, last_blk)];
+    const uint32_t i0 = (uint32_t)min(max(raw0, 0), a.num_blocks - 1);
+    const uint32_t i1 = (uint32_t)min(max(raw1, 0), a.num_blocks - 1);
+    const size_t o0 = (size_t)i0 * blk_bytes, o1 = (size_t)i1 * blk_bytes;
+    const uint32_t off0 = (uint32_t)(t0 & (bs - 1));
+    const uint32_t off1 = (uint32_t)((t0 + 16) & (bs - 1));
+    const char* kb0 = kbase + o0 + off0 * (uint32_t)(D * kPs);
+    const char* kb1 = kbase + o1 + off1 * (uint32_t)(D * kPs);
+    const char* vb0 = vbase + o0 + off0 * (uint32_t)kPs;
+    const char* vb1 = vbase + o1 + off1 * (uint32_t)kPs;
 #pragma unroll
     for (int i = 0; i < C::kKPerThread; ++i)
       if (C::kKPieces % C::kThreads == 0 || tid + C::kThreads * i < C::kKPieces)
