@@ -312,6 +312,11 @@ __device__ __forceinline__ void prefill_body(const DecodeArgs& a, const int32_t*
   const int bs = a.block_size;
   const int bshift = a.block_shift;
   const int32_t* table = tables + (size_t)b * a.max_blocks;
+  // entry i of the row, addressed by a 32-bit byte offset (one scalar load
+  // with a register offset)
+  auto tbl_at = [&](uint32_t i) -> int {
+    return *reinterpret_cast<const int32_t*>(reinterpret_cast<const char*>(table) + (i << 2));
+  };
   const int last_blk = ((n + bs - 1) >> bshift) - 1;
   // A block of either pool holds Hkv tiles of bs x D elements (the pools
   // share the layout); kbase / vbase: this pair's kv head in block 0.
@@ -359,19 +364,29 @@ __device__ __forceinline__ void prefill_body(const DecodeArgs& a, const int32_t*
     const int t0 = (c_begin + c) * kChunkTokens;
     // Blocks holding the chunk's two 16-token halves, and where each half
     // starts in its block's K tile and V tile (wave-uniform).
-    // Both table reads are issued before either is used; one 32 x 32-bit
-    // product per block gives its offset in both pools.
-    const int raw0 = table[min(t0 >> bshift, last_blk)];
-    const int raw1 = table[min((t0 + 16) >> bshift, last_blk)];
-    const uint32_t i0 = (uint32_t)min(max(raw0, 0), a.num_blocks - 1);
-    const uint32_t i1 = (uint32_t)min(max(raw1, 0), a.num_blocks - 1);
-    const size_t o0 = (size_t)i0 * blk_bytes, o1 = (size_t)i1 * blk_bytes;
-    const uint32_t off0 = (uint32_t)(t0 & (bs - 1));
-    const uint32_t off1 = (uint32_t)((t0 + 16) & (bs - 1));
-    const char* kb0 = kbase + o0 + off0 * (uint32_t)(D * kPs);
-    const char* kb1 = kbase + o1 + off1 * (uint32_t)(D * kPs);
-    const char* vb0 = vbase + o0 + off0 * (uint32_t)kPs;
-    const char* vb1 = vbase + o1 + off1 * (uint32_t)kPs;
+    // One 32 x 32-bit product per block gives its offset in both pools.
+    // 16-token blocks: the halves are two blocks, each from its first
+    // token; larger blocks (multiples of 32): one block holds both halves.
+    const char *kb0, *kb1, *vb0, *vb1;
+    if (bs == 16) {
+      const uint32_t j = (uint32_t)t0 >> 4;   // both reads in flight before either is used
+      const int raw0 = tbl_at(min(j, (uint32_t)last_blk));
+      const int raw1 = tbl_at(min(j + 1, (uint32_t)last_blk));
+      const size_t o0 = (size_t)(uint32_t)min(max(raw0, 0), a.num_blocks - 1) * blk_bytes;
+      const size_t o1 = (size_t)(uint32_t)min(max(raw1, 0), a.num_blocks - 1) * blk_bytes;
+      kb0 = kbase + o0;
+      kb1 = kbase + o1;
+      vb0 = vbase + o0;
+      vb1 = vbase + o1;
+    } else {
+      const int raw = tbl_at(min((uint32_t)t0 >> bshift, (uint32_t)last_blk));
+      const size_t o = (size_t)(uint32_t)min(max(raw, 0), a.num_blocks - 1) * blk_bytes;
+      const uint32_t off = (uint32_t)(t0 & (bs - 1));
+      kb0 = kbase + o + off * (uint32_t)(D * kPs);
+      kb1 = kb0 + 16 * D * kPs;
+      vb0 = vbase + o + off * (uint32_t)kPs;
+      vb1 = vb0 + 16 * kPs;
+    }
 #pragma unroll
     for (int i = 0; i < C::kKPerThread; ++i)
       if (C::kKPieces % C::kThreads == 0 || tid + C::kThreads * i < C::kKPieces)
