@@ -560,21 +560,24 @@ __device__ __forceinline__ void prefill_body(const DecodeArgs& a, const int32_t*
     lds_k<C::kLds, D>(kf, lds_kt[0], r, j);
     lds_v<C::kLds, D>(vf, lds_vt[0], r, j);
   }
-  for (int c = 0; c < nck; c += kP) {
+  // The loop body covers all three groups (3P chunks), so every chunk's
+  // LDS buffer is a compile-time constant (immediate LDS offsets).
+  constexpr int kRing = 3 * kP;
+  for (int c = 0; c < nck; c += kRing) {
 #pragma unroll
-    for (int h = 0; h < kP; ++h) {
-      const int cc = c + h;
+    for (int h = 0; h < kRing; ++h) {
+      const int cc = c + h;   // bufof(cc) == h
       if (cc + 2 * kP < nck) stage_load(cc + 2 * kP);   // its loads fly while chunk cc is computed
       const int t0 = (c_begin + cc) * kChunkTokens;
       if (cc < nck && t0 < kend_w) {
         const bool more = t0 + kChunkTokens < kend_w;   // this wave computes chunk cc + 1 too
-        const int nbuf = bufof(cc + 1);
+        const int nbuf = (h + 1) % kRing;
         if (t0 + kChunkTokens > lim_lo) compute(t0, nbuf, more, std::true_type{});
         else compute(t0, nbuf, more, std::false_type{});
       }
-      if (cc + 2 * kP < nck) stage_store(bufof(cc + 2 * kP));
+      if (cc + 2 * kP < nck) stage_store((h + 2 * kP) % kRing);
+      if (h % kP == kP - 1) __syncthreads();
     }
-    __syncthreads();
   }
 
   if (pm) {   // partials of this key segment: (reference max, sum), unnormalised accumulator
