@@ -101,55 +101,6 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const int2* __restric
     const int qi = c / G;
     float M = -INFINITY, L = 0.f;
     f32x4 o = {0.f, 0.f, 0.f, 0.f};
-    // Shared-prefix pieces: the same column's partials over the prefix's
-    // key segments (one query token per sequence here).  They do not depend
-    // on the pair's record, so up to kPreRegs of them are loaded at once,
-    // while the record's round trip is still in flight, and combined first
-    // (maximum, then the weighted sums); the tail pieces follow.
-    if constexpr (kPrefix) {
-      constexpr int kPreRegs = 8;
-      const size_t col = (size_t)b * Hq + (size_t)g * G + (c - qi * G);
-      const size_t stride = (size_t)num_seqs * Hq;
-      float Mp = -INFINITY;
-      if (pre_segments <= kPreRegs) {
-        float2 ml[kPreRegs];
-        f32x4 acc_s[kPreRegs];
-#pragma unroll
-        for (int s = 0; s < kPreRegs; ++s) {
-          if (s < pre_segments) {
-            const size_t slot = s * stride + col;
-            ml[s] = *reinterpret_cast<const float2*>(pre_ml + slot * 2);
-            acc_s[s] = load4<OutT>(pre_acc + slot * D + 4 * q4);
-          }
-        }
-#pragma unroll
-        for (int s = 0; s < kPreRegs; ++s)
-          if (s < pre_segments) Mp = fmaxf(Mp, ml[s].x);
-        const float Mu = Mp == -INFINITY ? 0.f : Mp;
-#pragma unroll
-        for (int s = 0; s < kPreRegs; ++s) {
-          if (s < pre_segments) {
-            const float w = exp2_fast(ml[s].x - Mu);
-            L += ml[s].y * w;
-            o += acc_s[s] * w;
-          }
-        }
-      } else {
-#pragma unroll 8
-        for (int s = 0; s < pre_segments; ++s) Mp = fmaxf(Mp, pre_ml[(s * stride + col) * 2]);
-        const float Mu = Mp == -INFINITY ? 0.f : Mp;
-#pragma unroll 8
-        for (int s = 0; s < pre_segments; ++s) {
-          const size_t slot = s * stride + col;
-          const float2 ml = *reinterpret_cast<const float2*>(pre_ml + slot * 2);
-          const f32x4 acc_s = load4<OutT>(pre_acc + slot * D + 4 * q4);
-          const float w = exp2_fast(ml.x - Mu);
-          L += ml.y * w;
-          o += acc_s * w;
-        }
-      }
-      M = Mp;
-    }
 #pragma unroll 4
     for (int w = m.x; w < m.x + m.y; ++w) {
       const size_t slot = ((size_t)w + place) * NC + c;
@@ -162,6 +113,31 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const int2* __restric
       L = L * f_old + ml.y * f_new;
       o = o * f_old + acc_w * f_new;
       M = M2;
+    }
+    // Shared-prefix pieces: the same column's partials over the prefix's
+    // key segments (one query token per sequence here).  Their maximum
+    // first, then the weighted sums, so that the pieces' loads do not wait
+    // on one another.
+    if constexpr (kPrefix) {
+      const size_t col = (size_t)b * Hq + (size_t)g * G + (c - qi * G);
+      const size_t stride = (size_t)num_seqs * Hq;
+      float Mp = -INFINITY;
+#pragma unroll 8
+      for (int s = 0; s < pre_segments; ++s) Mp = fmaxf(Mp, pre_ml[(s * stride + col) * 2]);
+      const float M2 = fmaxf(M, Mp);
+      const float M2u = M2 == -INFINITY ? 0.f : M2;
+      const float f_old = exp2_fast(M - M2u);
+      L *= f_old;
+      o *= f_old;
+#pragma unroll 8
+      for (int s = 0; s < pre_segments; ++s) {
+        const size_t slot = s * stride + col;
+        const float2 ml = *reinterpret_cast<const float2*>(pre_ml + slot * 2);
+        const f32x4 acc_s = load4<OutT>(pre_acc + slot * D + 4 * q4);
+        const float w = exp2_fast(ml.x - M2u);
+        L += ml.y * w;
+        o += acc_s * w;
+      }
     }
     OutT* dst = out + (((size_t)b * q_len + qi) * Hq + (size_t)g * G + (c - qi * G)) * D + 4 * q4;
     store4<OutT>(dst, o * (L > 0.f ? 1.f / L : 0.f));
