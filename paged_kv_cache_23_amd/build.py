@@ -30,6 +30,9 @@ HIP_FLAGS = [
     # keep hipcc from forming packed-fp32 instructions (v_pk_fma_f32 & co.)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall",
+    # a local that shadows another is an error: one such name once sent a
+    # ring read to the wrong LDS offset
+    "-Werror=shadow",
     "-Wno-unused-command-line-argument",
 ]
 
