@@ -110,12 +110,14 @@ typedef struct pkv_cache_desc {
  * k_new, v_new and the pools must be 16-byte aligned (else PKV_EINVAL).
  * FP8: code = E4M3 round-to-nearest-even, saturating to +-448, of the IEEE
  * float32 quotient x / scale[h].  Slots must be distinct and must not lie in
- * blocks shared with other sequences; two tokens with the same slot leave
- * one of them.  num_tokens == 0 is a no-op.
- * One kernel: a workgroup per 16 consecutive new tokens and kv head.  When
- * their slots are 16 consecutive rows of one block (a prefill chunk's
- * appends) it writes the block's K rows as one run and its V tile row by row
- * through LDS; otherwise it scatters element by element. */
+ * blocks shared with other sequences; what two tokens with the same slot
+ * leave there is unspecified.  num_tokens == 0 is a no-op.
+ * One kernel.  Below 1,024 tokens (a decode step's appends): one wave per
+ * (token, kv head).  From 1,024 tokens: workgroups of one kv head take
+ * groups of 16 consecutive new tokens in turn; each token's K row is written
+ * as 16-byte pieces, and when the 16 slots are 16 consecutive rows of one
+ * block (a prefill chunk's appends) the V tile's 16 columns go through LDS
+ * and out row by row, otherwise each V column element by element. */
 int pkv_kv_append(const pkv_cache_desc* desc, const void* k_new, const void* v_new,
                   const int64_t* slot_mapping, int32_t num_tokens, void* k_pool,
                   void* v_pool, void* stream);

@@ -116,8 +116,10 @@ __device__ __forceinline__ uint32_t e4m3_fields(uint32_t x) {
 }
 
 // Every input x in [first, first + count) (as binary32 bit patterns) through
-// e4m3_pair in both halves of the pair against e4m3_fields; mismatches are
-// counted, and the smallest mismatching x kept.
+// e4m3_pair in both halves of the pair and through e4m3_quad in each of its
+// four places, against e4m3_fields; e4m3_quad's other three values are 1.0
+// (code 0x38) and then NaN with the sign bit set (code 0xFF), which must keep
+// their codes.  Mismatches are counted, and the smallest mismatching x kept.
 __global__ __launch_bounds__(256) void e4m3_check_kernel(uint64_t first, uint64_t count,
                                                          unsigned long long* __restrict__ bad,
                                                          uint32_t* __restrict__ first_bad) {
@@ -128,7 +130,20 @@ __global__ __launch_bounds__(256) void e4m3_check_kernel(uint64_t first, uint64_
     const uint32_t want = e4m3_fields(x);
     const uint32_t lo = pkv::e4m3_pair(f, 0.f) & 0xFFu;
     const uint32_t hi = (pkv::e4m3_pair(0.f, f) >> 8) & 0xFFu;
-    if (lo != want || hi != want) {
+    bool quad_ok = true;
+    const float nan = __builtin_bit_cast(float, 0xFFC00000u);
+#pragma unroll
+    for (int other = 0; other < 2; ++other) {
+      const float o = other ? nan : 1.f;
+      const uint32_t oc = other ? 0xFFu : 0x38u;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const uint32_t got = pkv::e4m3_quad(p == 0 ? f : o, p == 1 ? f : o, p == 2 ? f : o, p == 3 ? f : o);
+        const uint32_t expect = (oc * 0x01010101u & ~(0xFFu << (8 * p))) | (want << (8 * p));
+        quad_ok &= got == expect;
+      }
+    }
+    if (lo != want || hi != want || !quad_ok) {
       atomicAdd(bad, 1ull);
       atomicMin(first_bad, x);
     }

@@ -146,3 +146,23 @@ def test_bulk_appends_into_consecutive_slots(kv_dtype, D, bs, first_run):
 def test_bulk_append_large_run():
     """4,096 tokens into consecutive slots across 8 kv heads: 256 full tiles per head."""
     _bulk("bf16", 128, 8, 16, list(range(16, 16 + 4096)), seed=3)
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8", "f32"])
+def test_bulk_append_workgroups_walk_several_groups(kv_dtype):
+    """40,000 tokens over 2 kv heads: more 16-token groups (2,500 per head)
+    than workgroups per head (1,024), so each workgroup takes two or three
+    groups in turn, loading the next while it stores the current one.  The
+    slots make workgroup b's groups alternate between a run (consecutive
+    slots: V through LDS) and scattered slots: b, b + 1,024, b + 2,048 fall
+    in the first 16,384 consecutive tokens, the 16,384 shuffled ones and the
+    last 7,232 consecutive ones."""
+    rng = np.random.default_rng(31)
+    a = list(range(64, 64 + 16384))
+    lo = 64 + 16384 + 32
+    b = (lo + rng.permutation(2 * 16384)[:16384]).tolist()
+    c0 = lo + 2 * 16384 + 48
+    c = list(range(c0, c0 + 40000 - 2 * 16384))
+    slots = a + b + c
+    assert len(slots) == 40000 and len(set(slots)) == 40000
+    _bulk(kv_dtype, 128, 2, 16, slots, seed=32)
