@@ -151,32 +151,45 @@ __device__ __forceinline__ typename Store<KV>::Scale store_scale(const float* sc
 // scattered V column run in parallel across the machine.
 template <int KV, int D>
 __global__ __launch_bounds__(64) void append_scatter_kernel(AppendArgs a) {
+  using S = Store<KV>;
   const int item = blockIdx.x;
   const int i = item / a.num_kv_heads;
   const int h = item % a.num_kv_heads;
+  const typename S::In* kn = static_cast<const typename S::In*>(a.k_new);
+  const typename S::In* vn = static_cast<const typename S::In*>(a.v_new);
+  typename S::Out* kp = static_cast<typename S::Out*>(a.k_pool);
+  typename S::Out* vp = static_cast<typename S::Out*>(a.v_pool);
+  // The token's K and V rows do not depend on its slot: they are loaded
+  // first, so that their loads and the slot's are in flight together.
+  const size_t src = ((size_t)i * a.num_kv_heads + h) * D;
+  constexpr int kPer = D / 64;
+  typename S::In kx[kPer], vx[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    kx[j] = kn[src + threadIdx.x + 64 * j];
+    vx[j] = vn[src + threadIdx.x + 64 * j];
+  }
+  const typename S::Scale ks = store_scale<KV>(a.k_scale, h), vs = store_scale<KV>(a.v_scale, h);
+  // keeps the compiler from moving those loads below the padding test
+  asm volatile("" ::: "memory");
   const int64_t slot = a.slot_mapping[i];
   const int bs = a.block_size;
   if (slot < 0 || slot >= (int64_t)a.num_blocks * bs) return;  // padding
   const int64_t blk = slot >> __builtin_ctz(bs);   // block sizes are powers of two
   const int off = (int)(slot & (bs - 1));
-  const size_t src = ((size_t)i * a.num_kv_heads + h) * D;
   const size_t ktile = ((size_t)blk * a.num_kv_heads + h) * bs * D;
   const size_t kdst = ktile + (size_t)off * D;     // token-major: row `off`
   const size_t vdst = ktile + off;                 // dim-major: column `off`
-  using S = Store<KV>;
-  const typename S::In* kn = static_cast<const typename S::In*>(a.k_new);
-  const typename S::In* vn = static_cast<const typename S::In*>(a.v_new);
-  typename S::Out* kp = static_cast<typename S::Out*>(a.k_pool);
-  typename S::Out* vp = static_cast<typename S::Out*>(a.v_pool);
-  const typename S::Scale ks = store_scale<KV>(a.k_scale, h), vs = store_scale<KV>(a.v_scale, h);
   // Non-temporal stores: the bytes go out to HBM at once.  A V column
   // touches D / (lines per block row) cache lines for D elements; left
   // cached, those partly written lines were written back later in the middle
   // of the decode's read stream and slowed it (measured on MI355X: 256
   // sequences, fp8 cache, append + decode 183.7 -> 174.5 us).
-  for (int d = threadIdx.x; d < D; d += 64) {
-    __builtin_nontemporal_store(S::put(kn[src + d], ks), &kp[kdst + d]);
-    __builtin_nontemporal_store(S::put(vn[src + d], vs), &vp[vdst + (size_t)d * bs]);
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int d = threadIdx.x + 64 * j;
+    __builtin_nontemporal_store(S::put(kx[j], ks), &kp[kdst + d]);
+    __builtin_nontemporal_store(S::put(vx[j], vs), &vp[vdst + (size_t)d * bs]);
   }
 }
 
