@@ -510,7 +510,7 @@ def run_bench(args) -> dict:
         "max_abs_err_sampled": None,
         "roofline": {
             "kernel": (("pkv_paged_decode_shared (decode_shared_kernel: tail walk and prefix waves in one "
-                        "launch; decode_merge_kernel)" if one_launch else
+                        "launch; shared_merge_kernel)" if one_launch else
                         "pkv_paged_decode_shared (prefill_kernel over the prefix + decode_split_kernel + "
                         "decode_merge_kernel)") if prefix else
                        "pkv_paged_decode (decode_split_kernel + decode_merge_kernel)"),

@@ -456,8 +456,7 @@ int pkv_paged_decode_shared(const pkv_cache_desc* desc, const void* q, const voi
     ta.pre_segments = segs;
     ta.pre_acc = pre_acc;
     ta.pre_ml = pre_ml;
-    if (pkv::launch_shared(ta, s) != hipSuccess) return PKV_ELAUNCH;
-    return launch_status(pkv::launch_merge(ta, s));
+    return launch_status(pkv::launch_shared(ta, s));
   }
 
   // 1. the prefix for every sequence at once: one virtual sequence whose

@@ -101,8 +101,8 @@ hipError_t launch_split(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_merge(const DecodeArgs& a, hipStream_t stream);
 // Shared-prefix decode, tail walk and prefix part in one launch (bf16
 // caches): num_workers / 4 eight-wave workgroups; the prefix partials go to
-// pre_acc / pre_ml in pre_segments key segments per column.  The merge
-// kernel then finishes every pair.
+// pre_acc / pre_ml in pre_segments key segments per column.  A merge kernel
+// launched after it finishes every pair.
 hipError_t launch_shared(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
 // The library's static decode workspace: kStaticScratchBytes of device memory

@@ -388,6 +388,86 @@ void decode_shared_kernel(DecodeArgs a, const int32_t* __restrict__ tables, cons
   }
 }
 
+// The merge after the one launch (one query token per sequence, bf16, at
+// most kSegs prefix segments).  The same combination, in the same
+// order, as the decode's merge kernel in its shared-prefix form: the pair's
+// tail pieces with the online-softmax rescale, then the column's prefix
+// segments, their maximum first.  Here a column's prefix partials are
+// loaded first, before the pair's record is read, so that their round trip
+// and the record's overlap and only the tail partials wait for the record.
+// Every one of the kSegs loads is made (past the last segment they repeat
+// it and are not used), so that they are issued back to back.
+template <int D, int kSegs>
+__global__ __launch_bounds__(256) void shared_merge_kernel(const int2* __restrict__ meta,
+                                                           const float* __restrict__ ws_acc,
+                                                           const float* __restrict__ ws_ml, __bf16* __restrict__ out,
+                                                           int num_seqs, int num_kv_heads, int group,
+                                                           const __bf16* __restrict__ pre_acc,
+                                                           const float* __restrict__ pre_ml, int pre_segments) {
+  typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+  const int pair = blockIdx.x;
+  const int G = group;   // the pair's columns: its G query heads
+  const int b = pair / num_kv_heads;
+  const int g = pair - b * num_kv_heads;
+  const size_t place = (size_t)g * num_seqs + b;   // the pair's place in the head-major chunk order
+  const size_t Hq = (size_t)num_kv_heads * G;
+  const size_t stride = (size_t)num_seqs * Hq;     // partial rows per prefix segment
+  for (int e = threadIdx.x; e < G * (D / 4); e += blockDim.x) {
+    const int c = e / (D / 4);
+    const int q4 = e % (D / 4);
+    const size_t col = (size_t)b * Hq + (size_t)g * G + c;
+    float2 pml[kSegs];
+    u32x2v pacc[kSegs];   // four bf16 values, widened where they are used
+#pragma unroll
+    for (int s = 0; s < kSegs; ++s) {
+      const size_t slot = (size_t)min(s, pre_segments - 1) * stride + col;
+      pml[s] = *reinterpret_cast<const float2*>(pre_ml + slot * 2);
+      pacc[s] = *reinterpret_cast<const u32x2v*>(pre_acc + slot * D + 4 * q4);
+    }
+    // keeps the compiler from reading the record before those loads
+    asm volatile("" ::: "memory");
+    const int2 m = meta[pair];
+    float M = -INFINITY, L = 0.f;
+    f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int w = m.x; w < m.x + m.y; ++w) {
+      const size_t slot = ((size_t)w + place) * G + c;
+      const float2 ml = *reinterpret_cast<const float2*>(ws_ml + slot * 2);
+      const f32x4 acc_w = *reinterpret_cast<const f32x4*>(ws_acc + slot * D + 4 * q4);
+      const float M2 = fmaxf(M, ml.x);
+      const float M2u = M2 == -INFINITY ? 0.f : M2;   // pieces that saw no token weigh 0
+      const float f_old = exp2_fast(M - M2u);
+      const float f_new = exp2_fast(ml.x - M2u);
+      L = L * f_old + ml.y * f_new;
+      o = o * f_old + acc_w * f_new;
+      M = M2;
+    }
+    float Mp = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < kSegs; ++s)
+      if (s < pre_segments) Mp = fmaxf(Mp, pml[s].x);
+    const float M2 = fmaxf(M, Mp);
+    const float M2u = M2 == -INFINITY ? 0.f : M2;
+    const float f_old = exp2_fast(M - M2u);
+    L *= f_old;
+    o *= f_old;
+#pragma unroll
+    for (int s = 0; s < kSegs; ++s) {
+      if (s < pre_segments) {
+        const f32x4 acc_s = {__builtin_bit_cast(float, pacc[s][0] << 16),
+                             __builtin_bit_cast(float, pacc[s][0] & 0xFFFF0000u),
+                             __builtin_bit_cast(float, pacc[s][1] << 16),
+                             __builtin_bit_cast(float, pacc[s][1] & 0xFFFF0000u)};
+        const float w = exp2_fast(pml[s].x - M2u);
+        L += pml[s].y * w;
+        o += acc_s * w;
+      }
+    }
+    __bf16* dst = out + ((size_t)b * Hq + (size_t)g * G + c) * D + 4 * q4;
+    store4<__bf16>(dst, o * (L > 0.f ? 1.f / L : 0.f));
+  }
+}
+
 template <int D>
 hipError_t launch_shared_t(const DecodeArgs& a, hipStream_t stream) {
   const unsigned grid = (unsigned)(a.num_workers / kDecodeWaves);
@@ -397,7 +477,21 @@ hipError_t launch_shared_t(const DecodeArgs& a, hipStream_t stream) {
   else
     hipLaunchKernelGGL((decode_shared_kernel<D, true, true>), dim3(grid), dim3(kSharedThreads), 0, stream, a,
                        a.block_tables, a.context_lens);
-  return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (a.q_len != 1 || a.pre_segments < 1 || a.pre_segments > 16) return launch_merge(a, stream);
+  const dim3 pairs((unsigned)a.num_seqs * (unsigned)a.num_kv_heads);
+  const dim3 threads(a.group * (D / 4) > 128 ? 256 : 128);
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, pairs, threads, 0, stream, static_cast<const int2*>(a.pair_meta),
+                       static_cast<const float*>(a.ws_acc), static_cast<const float*>(a.ws_ml),
+                       static_cast<__bf16*>(a.out), a.num_seqs, a.num_kv_heads, a.group,
+                       static_cast<const __bf16*>(a.pre_acc), a.pre_ml, a.pre_segments);
+    return hipGetLastError();
+  };
+  if (a.pre_segments <= 4) return go(shared_merge_kernel<D, 4>);
+  if (a.pre_segments <= 8) return go(shared_merge_kernel<D, 8>);
+  return go(shared_merge_kernel<D, 16>);
 }
 
 }  // namespace
