@@ -121,7 +121,8 @@ def _bulk(kv_dtype, D, Hkv, bs, slots, seed):
     assert np.array_equal(storage_numpy(vp.cpu()), ref_v)
 
 
-@pytest.mark.parametrize("kv_dtype,D", [("bf16", 128), ("fp8", 128), ("f32", 64), ("bf16", 64)])
+@pytest.mark.parametrize("kv_dtype,D", [("bf16", 128), ("fp8", 128), ("f32", 64), ("bf16", 64), ("fp8", 64),
+                                        ("f32", 128)])
 @pytest.mark.parametrize("bs", [16, 32, 256])
 @pytest.mark.parametrize("first_run", [200, 1200])
 def test_bulk_appends_into_consecutive_slots(kv_dtype, D, bs, first_run):
@@ -149,7 +150,8 @@ def test_bulk_append_large_run():
 
 
 @pytest.mark.parametrize("kv_dtype", ["bf16", "fp8", "f32"])
-def test_bulk_append_workgroups_walk_several_groups(kv_dtype):
+@pytest.mark.parametrize("D", [128, 64])
+def test_bulk_append_workgroups_walk_several_groups(kv_dtype, D):
     """40,000 tokens over 2 kv heads: more 16-token groups (2,500 per head)
     than workgroups per head (1,024), so each workgroup takes two or three
     groups in turn, loading the next while it stores the current one.  The
@@ -165,4 +167,4 @@ def test_bulk_append_workgroups_walk_several_groups(kv_dtype):
     c = list(range(c0, c0 + 40000 - 2 * 16384))
     slots = a + b + c
     assert len(slots) == 40000 and len(set(slots)) == 40000
-    _bulk(kv_dtype, 128, 2, 16, slots, seed=32)
+    _bulk(kv_dtype, D, 2, 16, slots, seed=32)
