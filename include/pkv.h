@@ -232,14 +232,17 @@ int pkv_paged_decode_static(const pkv_cache_desc* desc, const void* q, const voi
  *                  sequence's (clamped) length must be at least prefix_tokens;
  *                  for one that is not, or a row that differs in the prefix,
  *                  the output is unspecified (no access leaves the pools).
- * Three kernels on `stream`: (1) the many-query kernel runs every sequence's
- * query heads over the prefix (row 0's blocks) as the columns of one
- * (virtual) sequence per kv head, the prefix cut into key segments, and
- * leaves partials per segment (float32 max and sum; the unnormalised
- * accumulator in the output's type: bf16 unless the cache is float32);
- * (2) the decode split kernel runs each sequence's tokens after the prefix,
- * leaving partials only; (3) the merge kernel combines both sets of partials
- * per (sequence, head) with section 3's rescale and writes out.
+ * The work: every sequence's query heads over the prefix (row 0's blocks)
+ * as the columns of one (virtual) sequence per kv head, the prefix cut into
+ * key segments, leaving partials per segment (float32 max and sum; the
+ * unnormalised accumulator in the output's type: bf16 unless the cache is
+ * float32); each sequence's tokens after the prefix, leaving partials only;
+ * then a merge of both sets of partials per (sequence, head) with section
+ * 3's rescale, which writes out.  Kernels on `stream`: for a bf16 cache
+ * whose worker count gives every SIMD one tail wave (the default count),
+ * two: one kernel whose workgroups run the tail walk and the prefix part
+ * side by side, then the merge; otherwise three: the many-query kernel
+ * over the prefix, the decode split kernel over the tails, the merge.
  *   workspace  pkv_shared_decode_workspace_bytes(...) bytes (same num_workers),
  *              16-byte aligned scratch; calls sharing it must be ordered. */
 /* Whether pkv_paged_decode_shared is expected to beat pkv_paged_decode_ex
