@@ -239,8 +239,8 @@ int pkv_paged_decode_static(const pkv_cache_desc* desc, const void* q, const voi
  * float32); each sequence's tokens after the prefix, leaving partials only;
  * then a merge of both sets of partials per (sequence, head) with section
  * 3's rescale, which writes out.  Kernels on `stream`: for a bf16 cache
- * whose worker count gives every SIMD one tail wave (the default count),
- * two: one kernel whose workgroups run the tail walk and the prefix part
+ * whose worker count gives every SIMD one tail wave (4 per compute unit,
+ * the default once the tails have enough 32-token chunks), two: one kernel whose workgroups run the tail walk and the prefix part
  * side by side, then the merge; otherwise three: the many-query kernel
  * over the prefix, the decode split kernel over the tails, the merge.
  *   workspace  pkv_shared_decode_workspace_bytes(...) bytes (same num_workers),
